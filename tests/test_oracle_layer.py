@@ -1,0 +1,52 @@
+"""Pins of the layer oracle (CPU only)."""
+import numpy as np
+
+import oracle
+from oracle.layer import split_uvqk
+
+
+def test_layernorm_moments():
+    rng = np.random.default_rng(0)
+    a = 5.0 + 3.0 * rng.standard_normal((7, 512))
+    y = oracle.layernorm(a)
+    var = a.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+
+
+def test_layer_bruteforce_tiny():
+    """GEMMs, SiLU, split order and LN of the layer against scalar loops."""
+    import math
+    rng = np.random.default_rng(1)
+    H, D, dm = 2, 3, 4
+    offs = np.array([0, 4, 7])
+    nt = np.array([1, 2])
+    T = 7
+    x = rng.standard_normal((T, dm))
+    w1 = 0.5 * rng.standard_normal((dm, 4 * H * D))
+    b1 = 0.1 * rng.standard_normal(4 * H * D)
+    w2 = 0.5 * rng.standard_normal((H * D, dm))
+    b2 = 0.1 * rng.standard_normal(dm)
+    r = oracle.layer_fwd(x, w1, b1, w2, b2, offs, nt, H, D)
+    # projection, by loops
+    uvqk = np.zeros((T, 4 * H * D))
+    for t in range(T):
+        for c in range(4 * H * D):
+            z = b1[c] + sum(x[t, m] * w1[m, c] for m in range(dm))
+            uvqk[t, c] = z / (1.0 + math.exp(-z))
+    assert np.max(np.abs(uvqk - r["uvqk"])) < 1e-12
+    u, v, q, k = split_uvqk(uvqk, H, D)
+    assert np.array_equal(u[:, 1, :], uvqk[:, D:2 * D])
+    assert np.array_equal(k[:, 0, :], uvqk[:, 3 * H * D:3 * H * D + D])
+    So, Sa = oracle.scalar_attention_fwd(q, k, v, None, offs, 4, nt)
+    a = np.array(Sa).reshape(T, H * D)
+    assert np.max(np.abs(a - r["a"])) < 1e-12
+    y = np.zeros((T, dm))
+    for t in range(T):
+        mu = sum(a[t]) / (H * D)
+        var = sum((e - mu) ** 2 for e in a[t]) / (H * D)
+        ln = [(e - mu) / math.sqrt(var + 1e-5) for e in a[t]]
+        g = [ln[c] * u.reshape(T, H * D)[t, c] for c in range(H * D)]
+        for n in range(dm):
+            y[t, n] = b2[n] + sum(g[c] * w2[c, n] for c in range(H * D))
+    assert np.max(np.abs(y - r["y"])) < 1e-12
