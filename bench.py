@@ -1,0 +1,191 @@
+"""Benchmark: jagged HSTU attention forward + backward on one MI355X.
+
+One step = the whole hot path over one batch of the efficiency workload
+(8 jagged sequences, lengths uniform in [4096, 8192], 4 heads, head dim 128,
+position + time rab with 16383 + 128 buckets, bf16): per-sequence prep,
+scheduling, fused forward, backward preprocessing, fused backward and dQ
+conversion, all through the C ABI on torch's current stream, inputs already
+in HBM. Throughput is algorithmic TFLOP/s over unmasked pairs only
+(forward 2*Dqk + 2*Dv, backward 6*Dqk + 4*Dv per pair and head).
+
+Prints one JSON line. Also measures the M-FALCON inference layer (forward)
+and times the CPU oracle on a bounded sample as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HSTU jagged attn fwd+bwd TFLOP/s @ max_len 8192; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--workload", default="efficiency_8192_bf16")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from hstu_pointwise_attention_amd import _lib, ops
+    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd
+    from hstu_pointwise_attention_amd.flops import attention_flops
+
+    _lib.load()
+    wl = {w.name: w for w in W.ATTN_WORKLOADS}[args.workload]
+    inp = W.make_attention_inputs(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = "cuda"
+    T = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev, dt) for k in ("q", "k", "v", "u", "d_o")}
+    offs = torch.from_numpy(inp["seq_offsets"]).to(dev)
+    ts = torch.from_numpy(inp["timestamps"]).to(dev)
+    rp = torch.from_numpy(inp["rab_pos"]).to(dev)
+    rt = torch.from_numpy(inp["rab_time"]).to(dev)
+    fl = attention_flops(inp["lengths"], wl.heads, wl.d_qk, wl.d_v)
+
+    def step():
+        o, a = ops.attn_fwd(T["q"], T["k"], T["v"], T["u"], offs, wl.max_len, timestamps=ts,
+                            rab_pos=rp, rab_time=rt, save_a=True)
+        g = ops.attn_bwd(T["q"], T["k"], T["v"], T["u"], offs, wl.max_len, a, T["d_o"],
+                         timestamps=ts, rab_pos=rp, rab_time=rt)
+        return o, g
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, per-kernel HIP events recorded by the library on the
+    # same stream the kernels run on.
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with _lib.KernelTimer() as kt:
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tflops = fl["total"] / (ms_step * 1e-3) / 1e12
+
+    kern = {name: round(kt.avg_ms(name), 5) for name in kt.results}
+    bwd_ms = kt.avg_ms("bwd")
+    fwd_ms = kt.avg_ms("fwd")
+    bwd_tf = fl["bwd"] / (bwd_ms * 1e-3) / 1e12
+    fwd_tf = fl["fwd"] / (fwd_ms * 1e-3) / 1e12
+    # the dominant kernel by time
+    dom, dom_ms, dom_flops = ("bwd", bwd_ms, fl["bwd"]) if bwd_ms >= fwd_ms else ("fwd", fwd_ms, fl["fwd"])
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 5)}
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+                   "head_dim": wl.d_qk, "max_len": wl.max_len,
+                   "lengths": f"uniform [{wl.length_args[0]}, {wl.length_args[1]}], seed {wl.seed}",
+                   "tokens": int(inp["seq_offsets"][-1]), "pair_heads": fl["pair_heads"],
+                   "flops_per_step": fl["total"], "rab": "position 16383 + time 128 buckets"},
+        "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+        "kernels_avg_ms": kern,
+        "roofline": roofline,
+    }
+
+    if not args.no_layer:
+        out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl)
+
+    print(json.dumps(out), flush=True)
+
+
+def bench_layer(torch, W, hstu_layer_fwd, iters=10):
+    """M-FALCON-style inference layer forward: 4 users x (8192 history + 1024 candidates)."""
+    from hstu_pointwise_attention_amd.flops import unmasked_pairs_host
+    w = W.MFALCON_LAYER
+    li = W.make_layer_inputs(w)
+    dev = "cuda"
+    x = torch.from_numpy(li["x"]).to(dev, torch.bfloat16)
+    w1 = torch.from_numpy(li["w1"]).to(dev, torch.bfloat16)
+    w2 = torch.from_numpy(li["w2"]).to(dev, torch.bfloat16)
+    b1 = torch.from_numpy(li["b1"]).to(dev)
+    b2 = torch.from_numpy(li["b2"]).to(dev)
+    offs = torch.from_numpy(li["seq_offsets"]).to(dev)
+    nt = torch.from_numpy(li["num_targets"]).to(dev)
+    for _ in range(3):
+        hstu_layer_fwd(x, w1, b1, w2, b2, offs, nt, w.heads, w.head_dim)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        hstu_layer_fwd(x, w1, b1, w2, b2, offs, nt, w.heads, w.head_dim)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    T = x.shape[0]
+    pairs = unmasked_pairs_host(li["lengths"], li["num_targets"]) * w.heads
+    attn = pairs * 4 * w.head_dim
+    gemm = 2 * T * w.model_dim * (4 * w.heads * w.head_dim) + 2 * T * (w.heads * w.head_dim) * w.model_dim
+    return {"ms": round(ms, 4), "tflops": round((attn + gemm) / (ms * 1e-3) / 1e12, 2),
+            "attn_flops": attn, "gemm_flops": gemm, "tokens": T}
+
+
+def cpu_baseline(inp, wl):
+    """The oracle (numpy fp64) on a bounded sample: the first sequence of the batch, head 0."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    from hstu_pointwise_attention_amd.flops import attention_flops
+    s, e = int(inp["seq_offsets"][0]), int(inp["seq_offsets"][1])
+    sl = slice(s, e)
+    sub = {k: inp[k][sl, :1] for k in ("q", "k", "v", "u", "d_o")}      # head 0 only
+    sub["timestamps"] = inp["timestamps"][sl]
+    offs = np.array([0, e - s])
+    t0 = time.perf_counter()
+    oracle.attention_bwd(sub["q"], sub["k"], sub["v"], sub["u"], offs, wl.max_len, sub["d_o"],
+                         None, sub["timestamps"], inp["rab_pos"], inp["rab_time"])
+    sec = time.perf_counter() - t0
+    # attention_bwd evaluates the forward once inside; count fwd + bwd work
+    f = attention_flops([e - s], 1, wl.d_qk, wl.d_v)
+    return {"value": round(f["total"] / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"sequence 0 of the batch (L={e - s}), head 0, fwd+bwd, fp64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

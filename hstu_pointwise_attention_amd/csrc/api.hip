@@ -1,0 +1,324 @@
+// C ABI of the jagged HSTU attention library: argument validation, workspace
+// carve-up and the launch sequence of each call. Every check runs before the
+// first launch, so an error never leaves an output half written.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/hstu_attn.h"
+#include "internal.h"
+
+using namespace hstu;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hstu_status fail(hstu_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hstu_status ok() {
+  g_last_error.clear();
+  return HSTU_OK;
+}
+
+hstu_status hip_fail(hipError_t e, const char* what) {
+  return fail(HSTU_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == HSTU_DTYPE_BF16 ? 2 : 4; }
+
+// Shape checks shared by every attention entry point.
+hstu_status check_desc(const hstu_attn_desc* d) {
+  if (!d) return fail(HSTU_EINVAL, "desc is NULL");
+  if (d->batch < 0) return fail(HSTU_EINVAL, "batch %d < 0", d->batch);
+  if (d->heads < 1) return fail(HSTU_EINVAL, "heads %d < 1", d->heads);
+  if (d->dtype != HSTU_DTYPE_BF16 && d->dtype != HSTU_DTYPE_FP32)
+    return fail(HSTU_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->d_qk != d->d_v)
+    return fail(HSTU_EUNSUPPORTED, "d_qk (%d) != d_v (%d) is not supported", d->d_qk, d->d_v);
+  const bool dim_ok = d->dtype == HSTU_DTYPE_BF16
+                          ? (d->d_qk == 32 || d->d_qk == 64 || d->d_qk == 128)
+                          : (d->d_qk == 32 || d->d_qk == 64);
+  if (!dim_ok)
+    return fail(HSTU_EUNSUPPORTED, "head dim %d is not supported for dtype %d", d->d_qk, d->dtype);
+  if (d->max_len < 1 || d->max_len > (1 << 30)) return fail(HSTU_EINVAL, "max_len %d out of range", d->max_len);
+  if (d->n_time_buckets < 0 || d->n_time_buckets > 1024)
+    return fail(HSTU_EINVAL, "n_time_buckets %d outside [0, 1024]", d->n_time_buckets);
+  if (d->rab_heads != 1 && d->rab_heads != d->heads)
+    return fail(HSTU_EINVAL, "rab_heads %d must be 1 or heads (%d)", d->rab_heads, d->heads);
+  if (d->total_tokens < 0 || d->total_tokens >= ((int64_t)1 << 31))
+    return fail(HSTU_EINVAL, "total_tokens %lld outside [0, 2^31)", (long long)d->total_tokens);
+  if ((int64_t)d->heads * d->d_qk * d->total_tokens / (d->total_tokens ? d->total_tokens : 1) !=
+      (int64_t)d->heads * d->d_qk)
+    return fail(HSTU_EINVAL, "size overflow");
+  const int64_t hd = (int64_t)d->heads * d->d_qk;
+  const int vec = 16 / elem_bytes(d->dtype);
+  const int64_t strides[4] = {d->stride_q, d->stride_k, d->stride_v, d->stride_u};
+  const char* names[4] = {"stride_q", "stride_k", "stride_v", "stride_u"};
+  for (int i = 0; i < 4; ++i) {
+    if (i == 3 && strides[i] == 0) continue;  // u may be absent
+    if (strides[i] < hd) return fail(HSTU_EINVAL, "%s %lld < heads*d (%lld)", names[i], (long long)strides[i], (long long)hd);
+    if (strides[i] % vec) return fail(HSTU_EINVAL, "%s %lld must be a multiple of %d", names[i], (long long)strides[i], vec);
+  }
+  return HSTU_OK;
+}
+
+AttnParams base_params(const hstu_attn_desc* d, const int64_t* seq_offsets, const int64_t* num_targets,
+                       const int64_t* timestamps, const float* rab_pos, const float* rab_time,
+                       const void* q, const void* k, const void* v, const void* u) {
+  AttnParams p = {};
+  p.B = d->batch;
+  p.H = d->heads;
+  p.D = d->d_qk;
+  p.max_len = d->max_len;
+  p.n_time_buckets = rab_time ? d->n_time_buckets : 0;
+  p.rab_heads = d->rab_heads;
+  p.T = d->total_tokens;
+  p.sq = d->stride_q;
+  p.sk = d->stride_k;
+  p.sv = d->stride_v;
+  p.su = d->stride_u;
+  p.seq_offsets = seq_offsets;
+  p.num_targets = num_targets;
+  p.timestamps = rab_time ? timestamps : nullptr;
+  p.rab_pos = rab_pos;
+  p.rab_time = rab_time;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.u = u;
+  return p;
+}
+
+hstu_status check_inputs(const hstu_attn_desc* d, const int64_t* seq_offsets, const int64_t* timestamps,
+                         const float* rab_time, const void* q, const void* k, const void* v,
+                         const void* u) {
+  if (d->batch > 0 && !seq_offsets) return fail(HSTU_EINVAL, "seq_offsets is NULL");
+  if (rab_time && d->n_time_buckets < 1)
+    return fail(HSTU_EINVAL, "rab_time given but n_time_buckets is %d", d->n_time_buckets);
+  if (rab_time && !timestamps) return fail(HSTU_EINVAL, "rab_time given without timestamps");
+  if (d->total_tokens > 0) {
+    if (!q || !k || !v) return fail(HSTU_EINVAL, "q, k and v are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || (u && !aligned(u, 16)))
+      return fail(HSTU_EINVAL, "q, k, v, u must be 16-byte aligned");
+    if (u && d->stride_u == 0) return fail(HSTU_EINVAL, "u given with stride_u 0");
+  }
+  return HSTU_OK;
+}
+
+template <typename T>
+hipError_t dispatch_fwd(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd<T, 32>(p, s);
+    case 64: return launch_fwd<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <>
+hipError_t dispatch_fwd<bf16>(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd<bf16, 32>(p, s);
+    case 64: return launch_fwd<bf16, 64>(p, s);
+    case 128: return launch_fwd<bf16, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t dispatch_bwd(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_bwd<T, 32>(p, s);
+    case 64: return launch_bwd<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <>
+hipError_t dispatch_bwd<bf16>(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_bwd<bf16, 32>(p, s);
+    case 64: return launch_bwd<bf16, 64>(p, s);
+    case 128: return launch_bwd<bf16, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
+  hipError_t e = launch_bwd_pre<T>(p, s);
+  if (e == hipSuccess) e = dispatch_bwd<T>(p, s);
+  if (e == hipSuccess) e = launch_bwd_post<T>(p, s);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr);
+  *bytes = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype));
+  return ok();
+}
+
+hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr);
+  *bytes = carve_workspace(p, nullptr, true, elem_bytes(desc->dtype));
+  return ok();
+}
+
+hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                          const int64_t* num_targets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time, const void* q,
+                          const void* k, const void* v, const void* u, void* o, float* a_saved,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  st = check_inputs(desc, seq_offsets, timestamps, rab_time, q, k, v, u);
+  if (st != HSTU_OK) return st;
+  if (desc->total_tokens > 0) {
+    if (!o) return fail(HSTU_EINVAL, "o is NULL");
+    if (!aligned(o, 16) || (a_saved && !aligned(a_saved, 16)))
+      return fail(HSTU_EINVAL, "o and a_saved must be 16-byte aligned");
+  }
+  AttnParams p = base_params(desc, seq_offsets, num_targets, timestamps, rab_pos, rab_time, q, k,
+                             v, u);
+  p.o = o;
+  p.a_saved = a_saved;
+  const size_t need = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype));
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  carve_workspace(p, workspace, false, elem_bytes(desc->dtype));
+  if (p.T == 0 || p.B == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prep(p, s);
+  if (e == hipSuccess) e = launch_schedule(p, 0, s);
+  if (e == hipSuccess)
+    e = desc->dtype == HSTU_DTYPE_BF16 ? dispatch_fwd<bf16>(p, s) : dispatch_fwd<float>(p, s);
+  if (e != hipSuccess) return hip_fail(e, "hstu_attn_fwd launch");
+  return ok();
+}
+
+hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                          const int64_t* num_targets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time, const void* q,
+                          const void* k, const void* v, const void* u, const float* a_saved,
+                          const void* d_o, void* dq, void* dk, void* dv, void* du,
+                          float* d_rab_pos, float* d_rab_time, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  st = check_inputs(desc, seq_offsets, timestamps, rab_time, q, k, v, u);
+  if (st != HSTU_OK) return st;
+  if (rab_pos && !d_rab_pos) return fail(HSTU_EINVAL, "rab_pos given but d_rab_pos is NULL");
+  if (rab_time && !d_rab_time) return fail(HSTU_EINVAL, "rab_time given but d_rab_time is NULL");
+  if (desc->total_tokens > 0) {
+    if (!d_o || !dq || !dk || !dv) return fail(HSTU_EINVAL, "d_o, dq, dk and dv are required");
+    if (u && (!du || !a_saved)) return fail(HSTU_EINVAL, "a gated call needs du and a_saved");
+    if (!aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        (du && !aligned(du, 16)) || (a_saved && !aligned(a_saved, 16)))
+      return fail(HSTU_EINVAL, "gradient buffers must be 16-byte aligned");
+  }
+  AttnParams p = base_params(desc, seq_offsets, num_targets, timestamps, rab_pos, rab_time, q, k,
+                             v, u);
+  p.a_in = a_saved;
+  p.d_o = d_o;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.du = du;
+  p.d_rab_pos = rab_pos ? d_rab_pos : nullptr;
+  p.d_rab_time = rab_time ? d_rab_time : nullptr;
+  const int eb = elem_bytes(desc->dtype);
+  const size_t need = carve_workspace(p, nullptr, true, eb);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  carve_workspace(p, workspace, true, eb);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (p.d_rab_pos)
+    e = launch_fill_f32(p.d_rab_pos, (int64_t)desc->rab_heads * (2 * (int64_t)desc->max_len - 1), 0.f, s);
+  if (e == hipSuccess && p.d_rab_time)
+    e = launch_fill_f32(p.d_rab_time, (int64_t)desc->rab_heads * desc->n_time_buckets, 0.f, s);
+  if (e == hipSuccess && p.T > 0 && p.B > 0) {
+    e = launch_prep(p, s);
+    if (e == hipSuccess) e = launch_schedule(p, 1, s);
+    if (e == hipSuccess) e = launch_fill_f32(p.dq_acc, p.T * p.H * p.D, 0.f, s);
+    if (e == hipSuccess)
+      e = desc->dtype == HSTU_DTYPE_BF16 ? run_bwd_main<bf16>(p, s) : run_bwd_main<float>(p, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hstu_attn_bwd launch");
+  return ok();
+}
+
+hstu_status hstu_rab_bucketize(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                               const int64_t* num_targets, const int64_t* timestamps,
+                               const int64_t* pair_offsets, uint16_t* bp_out, uint8_t* bt_out,
+                               void* stream) {
+  if (!desc) return fail(HSTU_EINVAL, "desc is NULL");
+  if (desc->batch < 0) return fail(HSTU_EINVAL, "batch %d < 0", desc->batch);
+  if (desc->max_len < 1 || desc->max_len > 32768)
+    return fail(HSTU_EINVAL, "max_len %d outside [1, 32768] for a uint16 position bucket", desc->max_len);
+  if (desc->batch > 0 && (!seq_offsets || !pair_offsets))
+    return fail(HSTU_EINVAL, "seq_offsets and pair_offsets are required");
+  if (bt_out && (!timestamps || desc->n_time_buckets < 1 || desc->n_time_buckets > 256))
+    return fail(HSTU_EINVAL, "bt_out needs timestamps and 1 <= n_time_buckets <= 256");
+  AttnParams p = {};
+  p.B = desc->batch;
+  p.max_len = desc->max_len;
+  p.n_time_buckets = desc->n_time_buckets;
+  p.seq_offsets = seq_offsets;
+  p.num_targets = num_targets;
+  p.timestamps = timestamps;
+  hipError_t e = launch_bucketize(p, pair_offsets, bp_out, bt_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_rab_bucketize launch");
+  return ok();
+}
+
+hstu_status hstu_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx, const void* w,
+                        const float* bias, void* y, int32_t apply_silu, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0) return fail(HSTU_EINVAL, "bad sizes M=%lld K=%lld N=%lld", (long long)M, (long long)K, (long long)N);
+  if (K % 32 || N % 128) return fail(HSTU_EUNSUPPORTED, "K must be a multiple of 32 and N of 128");
+  if (ldx < K || ldx % 8) return fail(HSTU_EINVAL, "ldx %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (M > 0 && (!x || !w || !y)) return fail(HSTU_EINVAL, "x, w and y are required");
+  if (!aligned(x, 16) || !aligned(w, 16)) return fail(HSTU_EINVAL, "x and w must be 16-byte aligned");
+  hipError_t e = launch_linear(M, K, N, x, ldx, w, bias, y, apply_silu, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_linear launch");
+  return ok();
+}
+
+hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, const void* u, int64_t ldu,
+                                float eps, void* out, void* stream) {
+  if (M < 0 || N <= 0 || N % 64 || N > 4096) return fail(HSTU_EINVAL, "N must be a positive multiple of 64, <= 4096");
+  if (ldu < N || ldu % 4) return fail(HSTU_EINVAL, "ldu %lld must be >= N and a multiple of 4", (long long)ldu);
+  if (!(eps >= 0.f)) return fail(HSTU_EINVAL, "eps must be >= 0");
+  if (M > 0 && (!a || !u || !out)) return fail(HSTU_EINVAL, "a, u and out are required");
+  if (!aligned(a, 16) || !aligned(u, 8) || !aligned(out, 8)) return fail(HSTU_EINVAL, "misaligned buffer");
+  hipError_t e = launch_layernorm_gate(M, N, a, u, ldu, eps, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_layernorm_gate launch");
+  return ok();
+}
+
+const char* hstu_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,409 @@
+// Fused backward of jagged HSTU pointwise attention for gfx950.
+//
+// One workgroup (4 waves) owns 128 keys of one sequence and one head; wave w
+// owns keys 32w..32w+31 and keeps their K, V fragments and the dK, dV
+// accumulators in registers for the whole loop over the 64-row query tiles
+// that can see those keys. Per query tile (Q and dA' = dO*U/L staged through
+// LDS, row-major and transposed):
+//   S    = Q K^T + bias            (recomputed; bias read as in the forward)
+//   dP   = dA' V^T
+//   sg   = sigma(S), s = S*sg, s' = sg + s*(1 - sg)   (SiLU and its derivative)
+//   dS   = dP * s'  (0 where masked)
+//   dV  += s^T dA',  dK += dS^T Q
+//   dQ  += dS K     (through LDS, then fp32 atomics into a workspace buffer)
+// The rab gradients are sums of dS over the pairs that read each table entry:
+// each element adds its dS into an LDS window over relative positions (one per
+// query tile, flushed with global atomics) and an LDS histogram over time
+// buckets (flushed once per workgroup).
+#include "internal.h"
+
+namespace hstu {
+
+namespace {
+
+template <typename T, int D>
+struct BwdCfg {
+  static constexpr int BN = 128;                 // keys per workgroup
+  static constexpr int BM = 64;                  // query rows per tile
+  static constexpr int NT = 256;
+  static constexpr int KC = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int QB = BM / 32;             // 32-row query blocks per tile
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int VPC = 16 / ES;
+  static constexpr int CPR = D / VPC;
+  static constexpr int Q_LD = D + VPC;           // row-major tiles [BM][D]
+  static constexpr int QT_LD = BM + VPC;         // transposed tiles [D][BM]
+  static constexpr int DS_LD = BN + VPC;         // dS tile [BM][BN]
+  static constexpr int KT_LD = BN + VPC;         // K^T of the key block [D][BN]
+  static constexpr int WIN = BN + BM;            // >= BN + BM - 1
+  static constexpr int UNITS = (BM / 2) * CPR;   // (row pair, chunk) staging units
+  static constexpr int UPT = (UNITS + NT - 1) / NT;
+  static constexpr int KUNITS = (BN / 2) * CPR;  // K^T staging units
+  static constexpr int KUPT = (KUNITS + NT - 1) / NT;
+  static constexpr int NDQ = (QB * DB + 3) / 4;  // dQ output blocks per wave (max)
+  static constexpr int MAX_TIME = 1024;
+};
+
+__device__ __forceinline__ int perm_pos(int idx) {
+  const int kk = idx & 15;
+  return (idx & ~15) + 8 * ((kk & 7) >> 2) + 4 * (kk >> 3) + (kk & 3);
+}
+
+template <typename T, int D>
+struct BwdSmem {
+  using C = BwdCfg<T, D>;
+  T qs[C::BM * C::Q_LD];
+  T das[C::BM * C::Q_LD];
+  T qt[D * C::QT_LD];
+  T dat[D * C::QT_LD];
+  T kt[D * C::KT_LD];            // K^T of the key block, resident for the loop
+  T dss[C::BM * C::DS_LD];
+  int64_t tsq[C::BM];
+  float win[C::WIN];
+  float wing[C::WIN];
+  float ttab[C::MAX_TIME];
+  float thist[C::MAX_TIME];
+};
+
+template <typename T, int D, bool WIDE>
+__device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
+                                         const SeqInfo si, const int head) {
+  using C = BwdCfg<T, D>;
+  using F = typename Frag<T>::type;
+  const int H = p.H;
+  const int L = si.len, hist = si.hist;
+  const int64_t start = si.start;
+  const int k0 = wi.blk * C::BN;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int jw = k0 + 32 * wave;                 // first key of this wave
+  const int jl = 32 * wave + l32;                // this lane's key within the block
+  const int j = k0 + jl;
+  const bool key_ok = j < L;
+  const int hr = p.rab_heads == 1 ? 0 : head;
+  const bool has_pos = p.rab_pos != nullptr;
+  const bool has_time = p.rab_time != nullptr;
+  const int n_pos = 2 * p.max_len - 1;
+  const int t_last = p.n_time_buckets - 1;
+  const int64_t HD = (int64_t)H * D;
+
+  const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
+  const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
+  const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
+  const T* __restrict__ dag = reinterpret_cast<const T*>(p.d_a);
+
+  for (int x = tid; x < p.n_time_buckets; x += C::NT) {
+    sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+    sm.thist[x] = 0.f;
+  }
+  for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
+
+  // Resident K, V fragments of this lane's key (B operands of Q K^T, dA' V^T).
+  F kf[C::KC], vf[C::KC];
+#pragma unroll
+  for (int c = 0; c < C::KC; ++c) {
+    if (key_ok) {
+      kf[c] = ld_frag(kg + (start + j) * p.sk + (int64_t)head * D + 16 * c + 8 * g);
+      vf[c] = ld_frag(vg + (start + j) * p.sv + (int64_t)head * D + 16 * c + 8 * g);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        kf[c][m] = from_f32<T>(0.f);
+        vf[c][m] = from_f32<T>(0.f);
+      }
+    }
+  }
+  int64_t ts_j = 0;
+  if (has_time && key_ok) ts_j = WIDE ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
+
+  // K^T of the whole key block into LDS; the dQ product reads this wave's
+  // operand from it: lane (d, g) of d-block db_w takes K[k0 + 16kc + 8g + 0..7][d].
+  const int db_w = wave % C::DB;
+  {
+#pragma unroll
+    for (int m = 0; m < C::KUPT; ++m) {
+      const int un = tid + C::NT * m;
+      if (un < C::KUNITS) {
+        const int pair = un / C::CPR, cc = un % C::CPR;
+        const int jj = k0 + 2 * pair;
+        const T* src = kg + (start + jj) * p.sk + (int64_t)head * D + cc * C::VPC;
+        const u32x4 r0 = jj < L ? ld16(src) : u32x4{0, 0, 0, 0};
+        const u32x4 r1 = jj + 1 < L ? ld16(src + p.sk) : u32x4{0, 0, 0, 0};
+        const T* a = reinterpret_cast<const T*>(&r0);
+        const T* b = reinterpret_cast<const T*>(&r1);
+#pragma unroll
+        for (int e = 0; e < C::VPC; ++e) {
+          T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + 2 * pair;
+          dst[0] = a[e];
+          dst[1] = b[e];
+        }
+      }
+    }
+  }
+
+  // Query tiles that can see this key block.
+  const int qt_first = k0 / C::BM;
+  const int last_row = k0 < hist ? L - 1 : min(k0 + C::BN - 1, L - 1);
+  const int n_qt = last_row / C::BM - qt_first + 1;
+
+  // ---------------------------------------------------------------- staging
+  u32x4 qreg[C::UPT][2], dreg[C::UPT][2];
+  int64_t tsreg = 0;
+  float winreg = 0.f;
+
+  auto load_tile = [&](int q0) {
+#pragma unroll
+    for (int m = 0; m < C::UPT; ++m) {
+      const int un = tid + C::NT * m;
+      const int pair = un / C::CPR, cc = un % C::CPR;
+      const int ii = q0 + 2 * pair;
+      const bool in = un < C::UNITS;
+      const T* qs = qg + (start + ii) * p.sq + (int64_t)head * D + cc * C::VPC;
+      const T* ds = dag + (start + ii) * HD + (int64_t)head * D + cc * C::VPC;
+      qreg[m][0] = (in && ii < L) ? ld16(qs) : u32x4{0, 0, 0, 0};
+      qreg[m][1] = (in && ii + 1 < L) ? ld16(qs + p.sq) : u32x4{0, 0, 0, 0};
+      dreg[m][0] = (in && ii < L) ? ld16(ds) : u32x4{0, 0, 0, 0};
+      dreg[m][1] = (in && ii + 1 < L) ? ld16(ds + HD) : u32x4{0, 0, 0, 0};
+    }
+    if (has_time && tid < C::BM) {
+      const int ii = q0 + tid;
+      tsreg = ii < L ? (WIDE ? p.timestamps[start + ii] : (int64_t)p.ts_rel[start + ii]) : 0;
+    }
+    if (has_pos && tid < C::WIN) {
+      // entry y: offset j - p_i = k0 + BN - 1 - p_min - y
+      const int p_min = min(q0, hist);
+      winreg = p.rab_pos[(int64_t)hr * n_pos + pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len)];
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int m = 0; m < C::UPT; ++m) {
+      const int un = tid + C::NT * m;
+      if (un < C::UNITS) {
+        const int pair = un / C::CPR, cc = un % C::CPR;
+        st16(sm.qs + (2 * pair) * C::Q_LD + cc * C::VPC, qreg[m][0]);
+        st16(sm.qs + (2 * pair + 1) * C::Q_LD + cc * C::VPC, qreg[m][1]);
+        st16(sm.das + (2 * pair) * C::Q_LD + cc * C::VPC, dreg[m][0]);
+        st16(sm.das + (2 * pair + 1) * C::Q_LD + cc * C::VPC, dreg[m][1]);
+        const int pos = perm_pos(2 * pair);
+        const T* qa = reinterpret_cast<const T*>(&qreg[m][0]);
+        const T* qb = reinterpret_cast<const T*>(&qreg[m][1]);
+        const T* da = reinterpret_cast<const T*>(&dreg[m][0]);
+        const T* db = reinterpret_cast<const T*>(&dreg[m][1]);
+#pragma unroll
+        for (int e = 0; e < C::VPC; ++e) {
+          T* qd = sm.qt + (cc * C::VPC + e) * C::QT_LD + pos;
+          T* dd = sm.dat + (cc * C::VPC + e) * C::QT_LD + pos;
+          qd[0] = qa[e];
+          qd[1] = qb[e];
+          dd[0] = da[e];
+          dd[1] = db[e];
+        }
+      }
+    }
+    if (has_time && tid < C::BM) sm.tsq[tid] = tsreg;
+    if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
+  };
+
+  f32x16 acc_dk[C::DB], acc_dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc_dk[db][r] = 0.f;
+      acc_dv[db][r] = 0.f;
+    }
+
+  load_tile(qt_first * C::BM);
+  store_tile();
+
+  for (int n = 0; n < n_qt; ++n) {
+    const int q0 = (qt_first + n) * C::BM;
+    const bool more = n + 1 < n_qt;
+    __syncthreads();                               // tile n staged; previous dQ done
+    if (more) load_tile(q0 + C::BM);
+
+    const bool skip = jw >= L || q0 + C::BM - 1 < jw ||
+                      (jw >= hist && (q0 > jw + 31 || q0 + C::BM - 1 < jw));
+    if (!skip) {
+      const bool need_mask = !(q0 >= jw + 31 && jw + 31 < hist && q0 + C::BM - 1 < L);
+      const int p_min = min(q0, hist);
+      f32x16 acc_s[C::QB], acc_p[C::QB];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_p[qb][r] = 0.f;
+        if (has_pos) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int y = (C::BN - 1 - jl) + min(q0 + ql, hist) - p_min;
+            acc_s[qb][r] = sm.win[y];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_s[qb][r] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc_s[qb], a, kf[c]);
+          const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc_p[qb], b, vf[c]);
+        }
+      }
+      // Elementwise: acc_s <- SiLU(S) (for dV), acc_p <- dS (for dK, dQ).
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const int i = q0 + ql;
+          float s = acc_s[qb][r];
+          int bt = 0;
+          if (has_time) {
+            const int64_t ti = sm.tsq[ql];
+            bt = WIDE ? time_bucket_wide(ti, ts_j, t_last)
+                      : time_bucket_rel((uint32_t)ti, (uint32_t)ts_j, t_last);
+            s += sm.ttab[bt];
+          }
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
+          float sl = s * sg;
+          float ds = acc_p[qb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
+          if (need_mask) {
+            const bool ok = j <= i && (j < hist || j == i) && i < L;
+            sl = ok ? sl : 0.f;
+            ds = ok ? ds : 0.f;
+          }
+          acc_s[qb][r] = sl;
+          acc_p[qb][r] = ds;
+          if (has_pos) {
+            const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
+            atomicAdd(&sm.wing[y], ds);
+          }
+          if (has_time) atomicAdd(&sm.thist[bt], ds);
+          sm.dss[ql * C::DS_LD + jl] = from_f32<T>(ds);
+        }
+      }
+      // dV += s^T dA', dK += dS^T Q (query chunks of 16 in the permuted order).
+#pragma unroll
+      for (int kc = 0; kc < C::BM / 16; ++kc) {
+        const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s[kc >> 1]) + 8 * (kc & 1));
+        const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p[kc >> 1]) + 8 * (kc & 1));
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const F a = ld_frag(sm.dat + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+          mfma_32x32x16(acc_dv[db], sf, a);
+          const F b = ld_frag(sm.qt + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+          mfma_32x32x16(acc_dk[db], df, b);
+        }
+      }
+    } else {
+      // This wave's dS rows of the shared tile are zero.
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sm.dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * C::DS_LD + jl] = from_f32<T>(0.f);
+    }
+    __syncthreads();                               // dS, rab partials complete
+
+    // Flush the position-gradient window of this tile.
+    if (has_pos && tid < C::WIN) {
+      const float gsum = sm.wing[tid];
+      if (gsum != 0.f) {
+        const int p_min = min(q0, hist);
+        atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
+                      pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len),
+                  gsum);
+        sm.wing[tid] = 0.f;
+      }
+    }
+    // dQ += dS K for this wave's output blocks.
+#pragma unroll
+    for (int m = 0; m < C::NDQ; ++m) {
+      const int blk = wave + 4 * m;
+      if (blk < C::QB * C::DB) {
+        const int qb = blk / C::DB;
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < C::BN / 16; ++kc) {
+          const F a = ld_frag(sm.dss + (32 * qb + l32) * C::DS_LD + 16 * kc + 8 * g);
+          const F b = ld_frag(sm.kt + (32 * db_w + l32) * C::KT_LD + 16 * kc + 8 * g);
+          mfma_32x32x16(acc, a, b);
+        }
+        const int d = 32 * db_w + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (i < L) atomicAdd(p.dq_acc + ((start + i) * H + head) * (int64_t)D + d, acc[r]);
+        }
+      }
+    }
+    if (more) store_tile();
+  }
+
+  // Time-gradient histogram of this workgroup.
+  if (has_time) {
+    __syncthreads();
+    for (int x = tid; x < p.n_time_buckets; x += C::NT) {
+      const float gsum = sm.thist[x];
+      if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
+    }
+  }
+
+  // dK, dV of this lane's keys: register r holds key 8(r/4) + 4g + r%4 of the
+  // wave, column d = 32 db + l32.
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jj = jw + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (jj < L) {
+        const int64_t o = ((start + jj) * H + head) * (int64_t)D + 32 * db + l32;
+        reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
+        reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void hstu_bwd_kernel(AttnParams p) {
+  __shared__ BwdSmem<T, D> sm;
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (si.flags & kSeqWideTs)
+    bwd_body<T, D, true>(p, sm, wi, si, head);
+  else
+    bwd_body<T, D, false>(p, sm, wi, si, head);
+}
+
+}  // namespace
+
+template <typename T, int D>
+hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
+  const int64_t grid = p.max_items * p.H;
+  if (grid == 0) return hipSuccess;
+  prof_before(kKBwd, s);
+  hipLaunchKernelGGL((hstu_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  prof_after(kKBwd, s);
+  return hipGetLastError();
+}
+
+template hipError_t launch_bwd<bf16, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd<bf16, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd<bf16, 128>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd<float, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd<float, 64>(const AttnParams&, hipStream_t);
+
+}  // namespace hstu

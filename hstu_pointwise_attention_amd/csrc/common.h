@@ -1,0 +1,138 @@
+// Device-side building blocks shared by the gfx950 kernels of the jagged
+// HSTU attention library: element types, MFMA fragment wrappers, rab bucket
+// arithmetic and the per-sequence metadata the kernels read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+// -log2(e) and -ln(2): SiLU(S) = S * sigma(S) with sigma(S) = 1 / (1 + 2^(S * -log2 e)).
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Fragments. Every MFMA operand in this library uses one register layout:
+// lane l holds 8 consecutive reduction-dim elements k = 8*(l/32) + 0..7 of
+// row (A) or column (B) l%32 of a 32 x 16 (or 16 x 32) operand block.
+// For bf16 that is exactly the operand of v_mfma_f32_32x32x16_bf16. For fp32
+// the same 8 values feed eight v_mfma_f32_32x32x2_f32, instruction m taking
+// element m: its k-slot l/32 then stands for k = 8*(l/32) + m, the same
+// pairing on both operands, so the sum over k is unchanged.
+// Accumulator (32 x 32 fp32, 16 per lane): register r of lane l holds row
+// 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ void mfma_32x32x16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_32x32x16(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], b[m], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// 8 accumulator values -> one fragment (bf16: round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type pack8(const float* v) {
+  typename Frag<T>::type f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) f[m] = from_f32<T>(v[m]);
+  return f;
+}
+
+// Unaligned-free 16-byte global / LDS vector accesses.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type ld_frag(const T* p) {
+  return *reinterpret_cast<const typename Frag<T>::type*>(p);
+}
+
+// Four consecutive elements <-> f32x4 (8-byte bf16 or 16-byte fp32 accesses).
+__device__ __forceinline__ f32x4 ld4_f32(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 ld4_f32(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4_from_f32(bf16* p, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void st4_from_f32(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// rab buckets. Position: clamp(j - p_i, -(max_len-1), max_len-1) + max_len-1.
+// Time: min(bitlen(|dt| + 1) - 1, n_buckets - 1), exact in integers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int pos_bucket(int rel, int max_len) {
+  const int lim = max_len - 1;
+  rel = rel < -lim ? -lim : rel;
+  rel = rel > lim ? lim : rel;
+  return rel + lim;
+}
+
+// Rebased timestamps (offsets from the sequence minimum) below 2^31 - 1:
+// |a - b| + 1 <= 2^31 - 1 cannot overflow.
+__device__ __forceinline__ int time_bucket_rel(uint32_t a, uint32_t b, int last) {
+  const uint32_t d = (a > b ? a - b : b - a) + 1u;
+  const int bkt = 31 - __builtin_clz(d);
+  return bkt < last ? bkt : last;
+}
+
+// Any pair of int64 timestamps (used for sequences whose span is too wide
+// for the 32-bit form).
+__device__ __forceinline__ int time_bucket_wide(int64_t a, int64_t b, int last) {
+  const uint64_t d = a >= b ? (uint64_t)a - (uint64_t)b : (uint64_t)b - (uint64_t)a;
+  const int bkt = (d == ~0ull) ? 64 : 63 - __builtin_clzll(d + 1ull);
+  return bkt < last ? bkt : last;
+}
+
+// ---------------------------------------------------------------------------
+// Per-sequence metadata (written by the prep kernel into the workspace).
+// ---------------------------------------------------------------------------
+enum : int32_t { kSeqWideTs = 1, kSeqSortedTs = 2 };
+
+struct SeqInfo {
+  int32_t start;    // first token of the sequence
+  int32_t len;      // L
+  int32_t hist;     // L - num_targets (history length)
+  int32_t flags;    // kSeqWideTs | kSeqSortedTs
+  float inv_len;    // 1 / L (0 for L == 0)
+  int32_t nblk;     // ceil(L / 128): query blocks (forward) = key blocks (backward)
+  int64_t ts_min;   // smallest timestamp (rebasing origin)
+};
+static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
+
+struct WorkItem {
+  int32_t seq;
+  int32_t blk;
+};
+
+// Both attention kernels tile a sequence in blocks of 128 tokens: 128 query
+// rows per forward workgroup and 128 keys per backward workgroup.
+constexpr int kBlk = 128;
+
+}  // namespace hstu

@@ -1,0 +1,325 @@
+// Fused forward of jagged HSTU pointwise attention for gfx950.
+//
+// One workgroup (4 waves) owns 128 query rows of one sequence and one head;
+// wave w owns rows 32w..32w+31. It walks the key tiles (64 keys) that hold at
+// least one unmasked pair for its rows, skipping the candidate-only tiles of
+// M-FALCON-style batches, with K and V staged through LDS in two buffers so
+// the global loads of tile t+1 overlap the math of tile t.
+//
+// Per tile and wave, with S^T = K Q^T computed as 32 x 32 MFMA blocks (keys on
+// rows, the wave's queries on columns):
+//   acc   = rab_pos window (read from LDS into the accumulator) + K Q^T
+//   S'    = -log2(e) * (acc + rab_time[bt])         (one FMA per element)
+//   p     = S' / (1 + 2^S')     = SiLU(S) / (-ln 2)
+//   p     = 0 where masked (selection, never multiplication)
+//   O^T  += V^T P^T            (V stored transposed in LDS)
+// and the epilogue applies the factor -ln(2)/L, stores A (fp32) and O = A*U.
+// The accumulator layout of S^T is already the B-operand layout of P^T for
+// the second product once V^T's keys are stored in the matching order, so P
+// never leaves registers.
+#include "internal.h"
+
+namespace hstu {
+
+namespace {
+
+template <typename T, int D>
+struct FwdCfg {
+  static constexpr int BM = 128;                 // query rows per workgroup
+  static constexpr int BN = 64;                  // keys per tile
+  static constexpr int NT = 256;                 // threads
+  static constexpr int KC = D / 16;              // reduction chunks over head dim
+  static constexpr int DB = D / 32;              // 32-wide blocks of head dim
+  static constexpr int KB = BN / 32;             // 32-key blocks per tile
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int VPC = 16 / ES;            // elements per 16-byte chunk
+  static constexpr int CPR = D / VPC;            // 16-byte chunks per row
+  static constexpr int K_LD = D + VPC;           // LDS row stride of K (elements)
+  static constexpr int V_LD = BN + VPC;          // LDS row stride of V^T (elements)
+  static constexpr int WIN = BN + BM;            // position-bias window (>= BN + BM - 1)
+  static constexpr int K_CH = BN * CPR / NT;     // K 16-byte chunks per thread
+  static constexpr int V_UNITS = (BN / 2) * CPR; // (key pair, chunk) units
+  static constexpr int V_CH = (V_UNITS + NT - 1) / NT;
+  static constexpr int MAX_TIME = 1024;
+  static_assert(BN * CPR % NT == 0, "K staging");
+};
+
+// Position of key kk (0..15) inside a 16-key chunk of V^T: swaps the middle
+// two groups of four, so positions 8g..8g+7 hold keys 4g..4g+3 and
+// 8+4g..8+4g+3 -- the keys lane group g holds in the S^T accumulator.
+__device__ __forceinline__ int vt_pos(int key) {
+  const int kk = key & 15;
+  return (key & ~15) + 8 * ((kk & 7) >> 2) + 4 * (kk >> 3) + (kk & 3);
+}
+
+template <typename T, int D>
+struct FwdSmem {
+  using C = FwdCfg<T, D>;
+  T k[2][C::BN * C::K_LD];
+  T vt[2][D * C::V_LD];
+  int64_t ts[2][C::BN];          // key timestamps: rebased (low 32 bits) or raw
+  float win[2][C::WIN];          // rab_pos window for the tile
+  float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr]
+};
+
+template <typename T, int D, bool WIDE>
+__device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm, const WorkItem wi,
+                                         const SeqInfo si, const int head) {
+  using C = FwdCfg<T, D>;
+  using F = typename Frag<T>::type;
+  const int H = p.H;
+  const int L = si.len, hist = si.hist;
+  const int64_t start = si.start;
+  const int i0 = wi.blk * C::BM;
+  const int i_last = min(i0 + C::BM, L) - 1;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int iw = i0 + 32 * wave;                 // first row of this wave
+  const int i = iw + l32;                        // this lane's query row
+  const bool row_ok = i < L;
+  const int hr = p.rab_heads == 1 ? 0 : head;
+  const bool has_pos = p.rab_pos != nullptr;
+  const bool has_time = p.rab_time != nullptr;
+  const int t_last = p.n_time_buckets - 1;
+
+  const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
+  const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
+  const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
+
+  if (has_time)
+    for (int x = tid; x < p.n_time_buckets; x += C::NT)
+      sm.ttab[x] = kNegLog2e * p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+
+  // Q fragments of this lane's row (B operand of S^T = K Q^T).
+  F qf[C::KC];
+#pragma unroll
+  for (int c = 0; c < C::KC; ++c) {
+    if (row_ok) {
+      qf[c] = ld_frag(qg + (start + i) * p.sq + (int64_t)head * D + 16 * c + 8 * g);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) qf[c][m] = from_f32<T>(0.f);
+    }
+  }
+  int64_t ts_i = 0;
+  if (has_time && row_ok)
+    ts_i = WIDE ? p.timestamps[start + i] : (int64_t)p.ts_rel[start + i];
+
+  // Position-bias window: entry x holds the bias of offset j - p_i = j0 - p_max + x.
+  const int p_max = min(i_last, hist);
+  const int p_i = row_ok ? min(i, hist) : p_max;
+  const int c_lane = p_max - p_i;                // >= 0, < BM
+
+  // Key tiles: [0, t_end) minus the candidate-only tiles [skip_lo, skip_hi).
+  const int t_end = i_last / C::BN + 1;
+  const int skip_lo = (hist + C::BN - 1) / C::BN;
+  const int skip_hi = max(i0, hist) / C::BN;
+  const int n_a = min(skip_lo, t_end);
+  const int b_start = max(skip_hi, n_a);
+  const int n_tiles = n_a + max(0, t_end - b_start);
+
+  // ---------------------------------------------------------------- staging
+  u32x4 kreg[C::K_CH];
+  u32x4 vreg[C::V_CH][2];
+  int64_t tsreg = 0;
+  float winreg = 0.f;
+
+  auto tile_j0 = [&](int n) { return (n < n_a ? n : b_start + (n - n_a)) * C::BN; };
+
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int m = 0; m < C::K_CH; ++m) {
+      const int ch = tid + C::NT * m;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      const int j = j0 + row;
+      kreg[m] = j < L ? ld16(kg + (start + j) * p.sk + (int64_t)head * D + cc * C::VPC)
+                      : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int m = 0; m < C::V_CH; ++m) {
+      const int un = tid + C::NT * m;
+      const int pair = un / C::CPR, cc = un % C::CPR;
+      const int j = j0 + 2 * pair;
+      const bool in = un < C::V_UNITS;
+      const T* src = vg + (start + j) * p.sv + (int64_t)head * D + cc * C::VPC;
+      vreg[m][0] = (in && j < L) ? ld16(src) : u32x4{0, 0, 0, 0};
+      vreg[m][1] = (in && j + 1 < L) ? ld16(src + p.sv) : u32x4{0, 0, 0, 0};
+    }
+    if (has_time && tid < C::BN) {
+      const int j = j0 + tid;
+      tsreg = j < L ? (WIDE ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j]) : 0;
+    }
+    if (has_pos && tid < C::WIN) {
+      const int rel = j0 - p_max + tid;
+      winreg = p.rab_pos[(int64_t)hr * (2 * p.max_len - 1) + pos_bucket(rel, p.max_len)];
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    T* ks = sm.k[buf];
+#pragma unroll
+    for (int m = 0; m < C::K_CH; ++m) {
+      const int ch = tid + C::NT * m;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      st16(ks + row * C::K_LD + cc * C::VPC, kreg[m]);
+    }
+    T* vt = sm.vt[buf];
+#pragma unroll
+    for (int m = 0; m < C::V_CH; ++m) {
+      const int un = tid + C::NT * m;
+      if (un < C::V_UNITS) {
+        const int pair = un / C::CPR, cc = un % C::CPR;
+        const int pos = vt_pos(2 * pair);
+        const T* a = reinterpret_cast<const T*>(&vreg[m][0]);
+        const T* b = reinterpret_cast<const T*>(&vreg[m][1]);
+#pragma unroll
+        for (int e = 0; e < C::VPC; ++e) {
+          T* dst = vt + (cc * C::VPC + e) * C::V_LD + pos;
+          dst[0] = a[e];
+          dst[1] = b[e];
+        }
+      }
+    }
+    if (has_time && tid < C::BN) sm.ts[buf][tid] = tsreg;
+    if (has_pos && tid < C::WIN) sm.win[buf][tid] = winreg;
+  };
+
+  f32x16 acc_o[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+
+  if (n_tiles > 0) {
+    load_tile(tile_j0(0));
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < n_tiles; ++n) {
+    const int buf = n & 1;
+    const int j0 = tile_j0(n);
+    const bool more = n + 1 < n_tiles;
+    if (more) load_tile(tile_j0(n + 1));
+
+    // Does this wave have any unmasked pair in the tile?
+    const bool skip = iw >= L || j0 > iw + 31 || (j0 >= hist && j0 + C::BN - 1 < iw);
+    if (!skip) {
+      const bool need_mask = j0 + C::BN - 1 > min(iw, hist - 1);
+      const T* ks = sm.k[buf];
+      const T* vt = sm.vt[buf];
+      float pv[C::KB][16];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        f32x16 acc;
+        if (has_pos) {
+          const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc, a, qf[c]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          float s;
+          if (has_time) {
+            const int64_t tj = sm.ts[buf][jl];
+            const int bt = WIDE ? time_bucket_wide(ts_i, tj, t_last)
+                                : time_bucket_rel((uint32_t)ts_i, (uint32_t)tj, t_last);
+            s = __builtin_fmaf(acc[r], kNegLog2e, sm.ttab[bt]);
+          } else {
+            s = acc[r] * kNegLog2e;
+          }
+          float pr = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s));
+          if (need_mask) {
+            const int j = j0 + jl;
+            const bool ok = j <= i && (j < hist || j == i);
+            pr = ok ? pr : 0.f;
+          }
+          pv[kb][r] = pr;
+        }
+      }
+#pragma unroll
+      for (int kc = 0; kc < C::BN / 16; ++kc) {
+        const F pf = pack8<T>(&pv[kc >> 1][8 * (kc & 1)]);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const F a = ld_frag(vt + (32 * db + l32) * C::V_LD + 16 * kc + 8 * g);
+          mfma_32x32x16(acc_o[db], a, pf);
+        }
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  if (!row_ok) return;
+  const float scale = kNegLn2 * si.inv_len;
+  const int64_t orow = ((start + i) * H + head) * (int64_t)D;
+  T* og = reinterpret_cast<T*>(p.o) + orow;
+  const T* ug = p.u ? reinterpret_cast<const T*>(p.u) + (start + i) * p.su + (int64_t)head * D
+                    : nullptr;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d = 32 * db + 8 * rq + 4 * g;
+      f32x4 a;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] = acc_o[db][4 * rq + m] * scale;
+      if (p.a_saved) *reinterpret_cast<f32x4*>(p.a_saved + orow + d) = a;
+      if (ug) {
+        const f32x4 uv = ld4_f32(ug + d);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] *= uv[m];
+      }
+      st4_from_f32(og + d, a);
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void hstu_fwd_kernel(AttnParams p) {
+  __shared__ FwdSmem<T, D> sm;
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  // Sequences whose timestamp span needs 64-bit bucket arithmetic take the
+  // second instantiation; the branch is uniform over the workgroup.
+  if (si.flags & kSeqWideTs)
+    fwd_body<T, D, true>(p, sm, wi, si, head);
+  else
+    fwd_body<T, D, false>(p, sm, wi, si, head);
+}
+
+}  // namespace
+
+template <typename T, int D>
+hipError_t launch_fwd(const AttnParams& p, hipStream_t s) {
+  const int64_t grid = p.max_items * p.H;
+  if (grid == 0) return hipSuccess;
+  prof_before(kKFwd, s);
+  hipLaunchKernelGGL((hstu_fwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  prof_after(kKFwd, s);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fwd<bf16, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd<bf16, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd<bf16, 128>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd<float, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd<float, 64>(const AttnParams&, hipStream_t);
+
+}  // namespace hstu

@@ -1,0 +1,76 @@
+// Host-side interface between the C ABI (api.hip) and the kernel sources.
+#pragma once
+
+#include "common.h"
+
+namespace hstu {
+
+// Everything one attention launch needs; filled and validated by api.hip.
+struct AttnParams {
+  int32_t B, H, D, max_len, n_time_buckets, rab_heads;
+  int64_t T;
+  int64_t sq, sk, sv, su;            // input row strides (elements)
+  const int64_t* seq_offsets;
+  const int64_t* num_targets;        // may be null
+  const int64_t* timestamps;         // may be null
+  const float* rab_pos;              // may be null
+  const float* rab_time;             // may be null
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* u;                     // may be null (no gate)
+  // forward outputs
+  void* o;
+  float* a_saved;                    // may be null
+  // backward inputs / outputs
+  const float* a_in;
+  const void* d_o;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* du;
+  float* d_rab_pos;
+  float* d_rab_time;
+  // workspace carve-up
+  SeqInfo* seq;
+  uint32_t* ts_rel;                  // [T] rebased timestamps
+  WorkItem* items;                   // [max_items]
+  int32_t* n_items;                  // [1]
+  int32_t* sched_scratch;            // schedule kernel scratch
+  float* dq_acc;                     // [T, H, D] fp32 (backward)
+  void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
+  int64_t max_items;                 // T / 128 + B
+};
+
+// Workspace layout: returns total bytes and fills the pointers in p (when
+// base != nullptr).
+size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
+
+// Kernel identities for the optional per-launch timing (hstu_profile_*).
+enum KernelId : int {
+  kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKBwdPost, kKFill, kKLinear, kKLayerNorm,
+  kKBucketize, kNumKernelIds
+};
+// Records a HIP event on `s` before / after a launch when timing is enabled.
+void prof_before(int id, hipStream_t s);
+void prof_after(int id, hipStream_t s);
+
+hipError_t launch_prep(const AttnParams& p, hipStream_t s);
+// mode 0: forward order (query block index descending); 1: backward order.
+hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s);
+hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, uint16_t* bp,
+                            uint8_t* bt, hipStream_t s);
+
+template <typename T, int D> hipError_t launch_fwd(const AttnParams& p, hipStream_t s);
+template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);
+template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
+template <typename T> hipError_t launch_bwd_post(const AttnParams& p, hipStream_t s);
+hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
+
+hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                         const void* w, const float* bias, void* y, int apply_silu,
+                         hipStream_t s);
+hipError_t launch_layernorm_gate(int64_t M, int64_t N, const float* a, const void* u,
+                                 int64_t ldu, float eps, void* out, hipStream_t s);
+
+}  // namespace hstu

@@ -1,0 +1,353 @@
+// Small kernels around the attention: per-sequence metadata and timestamp
+// rebasing, the longest-first work schedule, the rab bucket export, and the
+// elementwise passes before and after the fused backward.
+#include "internal.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+constexpr int kSchedThreads = 1024;
+
+template <typename V, typename Op>
+__device__ V block_reduce(V v, V* lds, Op op) {
+  // wave64 butterfly, then across waves through LDS
+  for (int off = 32; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off));
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) lds[w] = v;
+  __syncthreads();
+  v = lds[0];
+  for (int i = 1; i < nw; ++i) v = op(v, lds[i]);
+  return v;
+}
+
+struct MinOp { __device__ int64_t operator()(int64_t a, int64_t b) const { return a < b ? a : b; } };
+struct MaxOp { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
+struct AndOp { __device__ int32_t operator()(int32_t a, int32_t b) const { return a & b; } };
+
+// Smallest / largest timestamp and sortedness of tokens [s, e).
+struct TsStats { int64_t lo, hi; int32_t sorted; };
+
+__device__ TsStats ts_stats(const int64_t* ts, int64_t s, int64_t e, int64_t* lds64, int32_t* lds32) {
+  int64_t lo = INT64_MAX, hi = INT64_MIN;
+  int32_t sorted = 1;
+  for (int64_t t = s + threadIdx.x; t < e; t += blockDim.x) {
+    const int64_t x = ts[t];
+    lo = x < lo ? x : lo;
+    hi = x > hi ? x : hi;
+    if (t > s && ts[t - 1] > x) sorted = 0;
+  }
+  TsStats r;
+  r.lo = block_reduce(lo, lds64, MinOp());
+  r.hi = block_reduce(hi, lds64, MaxOp());
+  r.sorted = block_reduce(sorted, lds32, AndOp());
+  return r;
+}
+
+// A sequence whose timestamp span reaches 2^31 - 1 uses 64-bit bucket math.
+__device__ __forceinline__ bool span_is_wide(int64_t lo, int64_t hi) {
+  return (uint64_t)hi - (uint64_t)lo >= 0x7fffffffull;
+}
+
+// One workgroup per sequence: metadata + rebased timestamps.
+__global__ __launch_bounds__(kPrepThreads) void seq_prep_kernel(AttnParams p) {
+  __shared__ int64_t lds64[kPrepThreads / kWave];
+  __shared__ int32_t lds32[kPrepThreads / kWave];
+  const int b = blockIdx.x;
+  const int64_t s = p.seq_offsets[b];
+  const int64_t e = p.seq_offsets[b + 1];
+  const int L = (int)(e - s);
+  int nt = p.num_targets ? (int)p.num_targets[b] : 0;
+  nt = nt < 0 ? 0 : (nt > L ? L : nt);
+  int flags = 0;
+  int64_t lo = 0;
+  if (p.timestamps != nullptr && L > 0) {
+    TsStats st = ts_stats(p.timestamps, s, e, lds64, lds32);
+    lo = st.lo;
+    if (span_is_wide(st.lo, st.hi)) flags |= kSeqWideTs;
+    if (st.sorted) flags |= kSeqSortedTs;
+    if (!(flags & kSeqWideTs))
+      for (int64_t t = s + threadIdx.x; t < e; t += blockDim.x)
+        p.ts_rel[t] = (uint32_t)(p.timestamps[t] - lo);
+  }
+  if (threadIdx.x == 0) {
+    SeqInfo si;
+    si.start = (int32_t)s;
+    si.len = L;
+    si.hist = L - nt;
+    si.flags = flags;
+    si.inv_len = L > 0 ? 1.0f / (float)L : 0.0f;
+    si.nblk = (L + kBlk - 1) / kBlk;
+    si.ts_min = lo;
+    p.seq[b] = si;
+  }
+}
+
+// Exclusive prefix sum over n ints in place (forward or from the end), one
+// workgroup, chunks of blockDim.x with a running carry. Returns the total.
+__device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
+  int carry = 0;
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int idx = base + threadIdx.x;
+    const int pos = from_end ? n - 1 - idx : idx;
+    const int v = idx < n ? data[pos] : 0;
+    lds[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+      const int add = threadIdx.x >= (unsigned)off ? lds[threadIdx.x - off] : 0;
+      __syncthreads();
+      lds[threadIdx.x] += add;
+      __syncthreads();
+    }
+    const int incl = lds[threadIdx.x];
+    const int total = lds[blockDim.x - 1];
+    if (idx < n) data[pos] = carry + incl - v;
+    carry += total;
+    __syncthreads();
+  }
+  return carry;
+}
+
+// Work list ordered longest first. A sequence with n blocks gives items
+// x = 0..n-1 whose cost grows with x (forward: x is the query block index,
+// the causal row block that sees the most keys; backward: x = n-1-key block,
+// the key block that sees the most queries). Items are placed by x
+// descending: start[x] = number of items with a larger x.
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
+  __shared__ int lds[kSchedThreads];
+  const int B = p.B;
+  const int NB = (int)(p.T / kBlk) + 2;       // x ranges over [0, NB)
+  int* seq_base = p.sched_scratch;              // [B + 1]
+  int* hist = seq_base + (B + 1);               // [NB]: sequences with n blocks
+  int* cnt = hist + NB;                         // [NB]: sequences with more than x blocks
+  int* fill = cnt + NB;                         // [NB]
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; }
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int n = p.seq[b].nblk;
+    seq_base[b] = n;
+    atomicAdd(&hist[n < NB ? n : NB - 1], 1);
+  }
+  __syncthreads();
+  const int total = block_scan_excl(seq_base, B, false, lds);
+  if (threadIdx.x == 0) seq_base[B] = total;
+  // cnt[x] = sum_{n > x} hist[n]: exclusive scan from the end
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) cnt[i] = hist[i];
+  __syncthreads();
+  block_scan_excl(cnt, NB, true, lds);
+  __syncthreads();
+  // start[x] = sum_{x' > x} cnt[x'] (stored in hist)
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) hist[i] = cnt[i];
+  __syncthreads();
+  block_scan_excl(hist, NB, true, lds);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    int lo = 0, hi = B;                          // last b with seq_base[b] <= idx
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seq_base[mid] <= idx) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int blk = idx - seq_base[b];
+    const int n = seq_base[b + 1] - seq_base[b];
+    const int x = mode == 0 ? blk : n - 1 - blk;
+    const int pos = hist[x] + atomicAdd(&fill[x], 1);
+    WorkItem w;
+    w.seq = b;
+    w.blk = blk;
+    p.items[pos] = w;
+  }
+  if (threadIdx.x == 0) *p.n_items = total;
+}
+
+// rab bucket export: grid (64 row groups, B sequences).
+__global__ __launch_bounds__(kPrepThreads) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
+                                                                  uint16_t* bp, uint8_t* bt) {
+  __shared__ int64_t lds64[kPrepThreads / kWave];
+  __shared__ int32_t lds32[kPrepThreads / kWave];
+  const int b = blockIdx.y;
+  const int64_t s = p.seq_offsets[b];
+  const int64_t e = p.seq_offsets[b + 1];
+  const int L = (int)(e - s);
+  int nt = p.num_targets ? (int)p.num_targets[b] : 0;
+  nt = nt < 0 ? 0 : (nt > L ? L : nt);
+  const int hist = L - nt;
+  bool wide = false;
+  int64_t lo = 0;
+  const bool want_t = bt != nullptr;
+  if (want_t && L > 0) {
+    TsStats st = ts_stats(p.timestamps, s, e, lds64, lds32);
+    lo = st.lo;
+    wide = span_is_wide(st.lo, st.hi);
+  }
+  const int last = p.n_time_buckets - 1;
+  const int64_t base = pair_offsets[b];
+  const int64_t hist_pairs = (int64_t)hist * (hist + 1) / 2;
+  for (int i = blockIdx.x; i < L; i += gridDim.x) {
+    const int64_t row = i < hist ? (int64_t)i * (i + 1) / 2
+                                 : hist_pairs + (int64_t)(i - hist) * (hist + 1);
+    const int n = i < hist ? i + 1 : hist + 1;
+    const int pi = i < hist ? i : hist;
+    for (int c = threadIdx.x; c < n; c += blockDim.x) {
+      const int j = (i < hist || c < hist) ? c : i;
+      const int64_t o = base + row + c;
+      if (bp) bp[o] = (uint16_t)pos_bucket(j - pi, p.max_len);
+      if (want_t) {
+        const int64_t ti = p.timestamps[s + i], tj = p.timestamps[s + j];
+        bt[o] = (uint8_t)(wide ? time_bucket_wide(ti, tj, last)
+                               : time_bucket_rel((uint32_t)(ti - lo), (uint32_t)(tj - lo), last));
+      }
+    }
+  }
+}
+
+__global__ void fill_f32_kernel(float* x, int64_t n, float value) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    x[i] = value;
+}
+
+// Sequence index of token t (last b with seq_offsets[b] <= t).
+__device__ __forceinline__ int seq_of_token(const int64_t* offs, int B, int64_t t) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offs[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// dA' = dO * U / L (or dO / L without gate), dU = dO * A. Four elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnParams p) {
+  const int HD = p.H * p.D;
+  const int64_t n4 = p.T * HD / 4;
+  for (int64_t q4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q4 < n4;
+       q4 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = q4 * 4;
+    const int64_t t = e0 / HD;
+    const int hd = (int)(e0 - t * HD);
+    const float inv = p.seq[seq_of_token(p.seq_offsets, p.B, t)].inv_len;
+    const T* dop = reinterpret_cast<const T*>(p.d_o) + e0;
+    T* dap = reinterpret_cast<T*>(p.d_a) + e0;
+    float go[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) go[m] = to_f32(dop[m]);
+    if (p.u != nullptr) {
+      const T* up = reinterpret_cast<const T*>(p.u) + t * p.su + hd;
+      const float* ap = p.a_in + e0;
+      T* dup = reinterpret_cast<T*>(p.du) + e0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        dap[m] = from_f32<T>(go[m] * to_f32(up[m]) * inv);
+        dup[m] = from_f32<T>(go[m] * ap[m]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dap[m] = from_f32<T>(go[m] * inv);
+    }
+  }
+}
+
+// dQ: fp32 accumulator -> output dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_post_kernel(const float* acc, T* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = from_f32<T>(acc[i]);
+}
+
+int grid_for(int64_t n, int threads) {
+  int64_t g = (n + threads - 1) / threads;
+  if (g > 8192) g = 8192;
+  return g < 1 ? 1 : (int)g;
+}
+
+}  // namespace
+
+size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return base ? (void*)((char*)base + at) : nullptr;
+  };
+  p.max_items = p.T / kBlk + p.B + 1;
+  const int64_t NB = p.T / kBlk + 2;
+  p.seq = (SeqInfo*)take(sizeof(SeqInfo) * (size_t)(p.B > 0 ? p.B : 1));
+  p.ts_rel = (uint32_t*)take(sizeof(uint32_t) * (size_t)(p.T > 0 ? p.T : 1));
+  p.items = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
+  p.n_items = (int32_t*)take(sizeof(int32_t));
+  p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 3 * NB));
+  p.dq_acc = nullptr;
+  p.d_a = nullptr;
+  if (bwd) {
+    p.dq_acc = (float*)take(sizeof(float) * (size_t)p.T * p.H * p.D);
+    p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
+  }
+  return off;
+}
+
+hipError_t launch_prep(const AttnParams& p, hipStream_t s) {
+  if (p.B == 0) return hipSuccess;
+  prof_before(kKPrep, s);
+  hipLaunchKernelGGL(seq_prep_kernel, dim3(p.B), dim3(kPrepThreads), 0, s, p);
+  prof_after(kKPrep, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s) {
+  prof_before(kKSchedule, s);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p, mode);
+  prof_after(kKSchedule, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, uint16_t* bp,
+                            uint8_t* bt, hipStream_t s) {
+  if (p.B == 0) return hipSuccess;
+  prof_before(kKBucketize, s);
+  hipLaunchKernelGGL(bucketize_kernel, dim3(64, p.B), dim3(kPrepThreads), 0, s, p, pair_offsets,
+                     bp, bt);
+  prof_after(kKBucketize, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  prof_before(kKFill, s);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, x, n, value);
+  prof_after(kKFill, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s) {
+  const int64_t n4 = p.T * p.H * p.D / 4;
+  if (n4 == 0) return hipSuccess;
+  prof_before(kKBwdPre, s);
+  hipLaunchKernelGGL(bwd_pre_kernel<T>, dim3(grid_for(n4, 256)), dim3(256), 0, s, p);
+  prof_after(kKBwdPre, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_post(const AttnParams& p, hipStream_t s) {
+  const int64_t n = p.T * p.H * p.D;
+  if (n == 0) return hipSuccess;
+  prof_before(kKBwdPost, s);
+  hipLaunchKernelGGL(bwd_post_kernel<T>, dim3(grid_for(n, 256)), dim3(256), 0, s, p.dq_acc,
+                     reinterpret_cast<T*>(p.dq), n);
+  prof_after(kKBwdPost, s);
+  return hipGetLastError();
+}
+
+template hipError_t launch_bwd_pre<bf16>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd_pre<float>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd_post<bf16>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd_post<float>(const AttnParams&, hipStream_t);
+
+}  // namespace hstu

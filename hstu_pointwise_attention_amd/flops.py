@@ -1,0 +1,24 @@
+"""Host-side work accounting: unmasked pairs and algorithmic FLOPs.
+
+FLOPs are counted over unmasked (sequence, head, i, j) pairs only: the
+forward does 2*Dqk (Q K^T) + 2*Dv (P V) per pair; the backward recomputes
+Q K^T and does dA' V^T, s^T dA', dS^T Q and dS K, i.e. 6*Dqk + 4*Dv.
+"""
+from __future__ import annotations
+
+
+def unmasked_pairs_host(lengths, num_targets=None) -> int:
+    total = 0
+    for b, L in enumerate(lengths):
+        L = int(L)
+        nt = 0 if num_targets is None else min(max(int(num_targets[b]), 0), L)
+        hist = L - nt
+        total += hist * (hist + 1) // 2 + nt * (hist + 1)
+    return total
+
+
+def attention_flops(lengths, heads: int, d_qk: int, d_v: int, num_targets=None) -> dict:
+    pairs = unmasked_pairs_host(lengths, num_targets) * heads
+    fwd = pairs * (2 * d_qk + 2 * d_v)
+    bwd = pairs * (6 * d_qk + 4 * d_v)
+    return dict(pair_heads=pairs, fwd=fwd, bwd=bwd, total=fwd + bwd)

@@ -1,0 +1,184 @@
+"""Torch-facing wrappers of the C ABI: argument marshalling only.
+
+Tensors supply device memory, torch's current stream supplies the HIP stream;
+every step of the computation runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_FP32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _token_stride(t: torch.Tensor, name: str, H: int, D: int) -> int:
+    if t.dim() != 3 or t.shape[1] != H or t.shape[2] != D:
+        raise ValueError(f"{name} must be [T, {H}, {D}], got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != D:
+        raise ValueError(f"{name} must have contiguous heads and head dim (strides {t.stride()})")
+    return t.stride(0)
+
+
+def make_desc(q, k, v, u, seq_offsets, max_len, n_time_buckets=0, rab_heads=1) -> _lib.AttnDesc:
+    T, H, D = q.shape
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("u", u)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    d = _lib.AttnDesc()
+    d.batch = seq_offsets.numel() - 1
+    d.heads = H
+    d.d_qk = D
+    d.d_v = v.shape[2]
+    d.max_len = int(max_len)
+    d.n_time_buckets = int(n_time_buckets)
+    d.rab_heads = int(rab_heads)
+    d.dtype = _DTYPES[q.dtype]
+    d.total_tokens = T
+    d.stride_q = _token_stride(q, "q", H, D)
+    d.stride_k = _token_stride(k, "k", H, D)
+    d.stride_v = _token_stride(v, "v", H, v.shape[2])
+    d.stride_u = _token_stride(u, "u", H, v.shape[2]) if u is not None else 0
+    return d
+
+
+def _rab_meta(rab_pos, rab_time):
+    nt = rab_time.shape[1] if rab_time is not None else 0
+    tab = rab_pos if rab_pos is not None else rab_time
+    hr = tab.shape[0] if tab is not None else 1
+    return nt, hr
+
+
+def _i64(t):
+    return None if t is None else t.to(torch.int64).contiguous()
+
+
+def _f32c(t):
+    return None if t is None else t.to(torch.float32).contiguous()
+
+
+def attn_fwd(q, k, v, u, seq_offsets, max_len, *, num_targets=None, timestamps=None,
+             rab_pos=None, rab_time=None, save_a: bool = True):
+    """Returns (O [T,H,Dv] in q's dtype, A [T,H,Dv] fp32 or None)."""
+    lib = _lib.load()
+    seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
+    rab_pos, rab_time = _f32c(rab_pos), _f32c(rab_time)
+    nt, hr = _rab_meta(rab_pos, rab_time)
+    desc = make_desc(q, k, v, u, seq_offsets, max_len, nt, hr)
+    T, H, _ = q.shape
+    Dv = v.shape[2]
+    o = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
+    a = torch.empty((T, H, Dv), dtype=torch.float32, device=q.device) if save_a else None
+    nbytes = ctypes.c_size_t()
+    _lib.check(lib.hstu_attn_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.hstu_attn_fwd(ctypes.byref(desc), _ptr(seq_offsets), _ptr(num_targets),
+                                 _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(u), _ptr(o), _ptr(a), _ptr(ws), nbytes.value,
+                                 _stream()))
+    return o, a
+
+
+def attn_bwd(q, k, v, u, seq_offsets, max_len, a_saved, d_o, *, num_targets=None,
+             timestamps=None, rab_pos=None, rab_time=None):
+    """Returns dict dq, dk, dv, du (None without gate), d_rab_pos, d_rab_time."""
+    lib = _lib.load()
+    seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
+    rab_pos, rab_time = _f32c(rab_pos), _f32c(rab_time)
+    nt, hr = _rab_meta(rab_pos, rab_time)
+    desc = make_desc(q, k, v, u, seq_offsets, max_len, nt, hr)
+    d_o = d_o.contiguous()
+    T, H, D = q.shape
+    Dv = v.shape[2]
+    dq = torch.empty((T, H, D), dtype=q.dtype, device=q.device)
+    dk = torch.empty((T, H, D), dtype=q.dtype, device=q.device)
+    dv = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
+    du = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device) if u is not None else None
+    drp = torch.empty_like(rab_pos) if rab_pos is not None else None
+    drt = torch.empty_like(rab_time) if rab_time is not None else None
+    nbytes = ctypes.c_size_t()
+    _lib.check(lib.hstu_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.hstu_attn_bwd(ctypes.byref(desc), _ptr(seq_offsets), _ptr(num_targets),
+                                 _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(u), _ptr(a_saved), _ptr(d_o), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(du), _ptr(drp), _ptr(drt), _ptr(ws), nbytes.value,
+                                 _stream()))
+    return dict(dq=dq, dk=dk, dv=dv, du=du, d_rab_pos=drp, d_rab_time=drt)
+
+
+def pair_offsets_host(lengths, num_targets=None) -> list:
+    """First output slot of each sequence in the bucket export (host arithmetic)."""
+    offs = [0]
+    for b, L in enumerate(lengths):
+        L = int(L)
+        nt = 0 if num_targets is None else min(max(int(num_targets[b]), 0), L)
+        hist = L - nt
+        offs.append(offs[-1] + hist * (hist + 1) // 2 + (L - hist) * (hist + 1))
+    return offs
+
+
+def rab_bucketize(seq_offsets, max_len, *, num_targets=None, timestamps=None,
+                  n_time_buckets=0, want_pos=True):
+    """Bucket export over the unmasked pairs: (bp uint16 as int32 or None, bt uint8 or None)."""
+    lib = _lib.load()
+    dev = seq_offsets.device
+    seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
+    lengths = (seq_offsets[1:] - seq_offsets[:-1]).cpu().tolist()
+    nts = num_targets.cpu().tolist() if num_targets is not None else None
+    offs = pair_offsets_host(lengths, nts)
+    n = offs[-1]
+    po = torch.tensor(offs, dtype=torch.int64, device=dev)
+    bp = torch.empty(max(n, 1), dtype=torch.int16, device=dev) if want_pos else None
+    bt = torch.empty(max(n, 1), dtype=torch.uint8, device=dev) if timestamps is not None else None
+    d = _lib.AttnDesc()
+    d.batch = len(lengths)
+    d.heads = 1
+    d.max_len = int(max_len)
+    d.n_time_buckets = int(n_time_buckets)
+    _lib.check(lib.hstu_rab_bucketize(ctypes.byref(d), _ptr(seq_offsets), _ptr(num_targets),
+                                      _ptr(timestamps), _ptr(po), _ptr(bp), _ptr(bt), _stream()))
+    bp = bp[:n].to(torch.int32) & 0xFFFF if bp is not None else None
+    bt = bt[:n] if bt is not None else None
+    return bp, bt
+
+
+def linear(x, w, bias=None, silu: bool = False):
+    """y = act(x @ w + bias) in bf16 with fp32 accumulation."""
+    lib = _lib.load()
+    M, K = x.shape
+    N = w.shape[1]
+    if x.stride(1) != 1:
+        raise ValueError("x must have a contiguous last dim")
+    w = w.contiguous()
+    bias = _f32c(bias)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _lib.check(lib.hstu_linear(M, K, N, _ptr(x), x.stride(0), _ptr(w), _ptr(bias), _ptr(y),
+                               1 if silu else 0, _stream()))
+    return y
+
+
+def layernorm_gate(a, u, eps: float = 1e-5):
+    """LayerNorm(a) * u over the last dim; a fp32 [M, N], u bf16 [M, N] (row-strided)."""
+    lib = _lib.load()
+    M, N = a.shape
+    a = a.contiguous()
+    if u.stride(1) != 1:
+        raise ValueError("u must have a contiguous last dim")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _lib.check(lib.hstu_layernorm_gate(M, N, _ptr(a), _ptr(u), u.stride(0), float(eps), _ptr(out),
+                                       _stream()))
+    return out

@@ -1,0 +1,194 @@
+/*
+ * hstu_attn.h -- C ABI of the MI355X (gfx950) jagged HSTU attention library.
+ *
+ * What it computes. HSTU's pointwise attention, named in the Abstract of
+ * "Actions Speak Louder than Words: Trillion-Parameter Sequential Transducers
+ * for Generative Recommendations" and, as target-aware full causal
+ * self-attention with M-FALCON candidate scoring, in the Generative
+ * Recommenders README ("HSTU Ultra attention benchmark"). The pages print no
+ * equations; the definition implemented here, per jagged sequence b of length
+ * L (tokens seq_offsets[b] .. seq_offsets[b+1]-1), head h and in-sequence
+ * indices 0 <= i, j < L, is:
+ *
+ *   hist    = L - num_targets[b]            (num_targets NULL: hist = L)
+ *   M[i,j]  = (j <= i && j < hist) || j == i          causal + candidate mask
+ *   p_i     = min(i, hist)
+ *   bp(i,j) = clamp(j - p_i, -(max_len-1), max_len-1) + (max_len-1)
+ *   bt(i,j) = min(bitlen(|ts_i - ts_j| + 1) - 1, n_time_buckets - 1)
+ *   S[i,j]  = sum_d Q[i,h,d] K[j,h,d] + rab_pos[hr,bp] + rab_time[hr,bt]
+ *   A[i,h]  = (1/L) sum_j M[i,j] SiLU(S[i,j]) V[j,h],   SiLU(x) = x/(1+e^-x)
+ *   O[i,h]  = A[i,h] * U[i,h]        (u == NULL: O = A)
+ *
+ * hr = 0 when rab_heads == 1 (one table shared by all heads), else hr = h.
+ * The backward returns dQ, dK, dV, dU = dO*A and the rab-table gradients
+ * (sums of dS = M * (dO*U . V_j) * SiLU'(S) / L over the pairs reading each
+ * entry).
+ *
+ * Conventions for every call.
+ *  - Pointers marked (device) are device memory; (host) are host memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). Nothing synchronises with the host.
+ *  - The caller allocates and owns every buffer, including the workspace;
+ *    the library allocates nothing and keeps no state between calls, so calls
+ *    are reentrant. Calls that share a workspace must not overlap.
+ *  - Every call validates its host-side arguments before it launches
+ *    anything; on any error it returns a negative status without writing any
+ *    output and hstu_last_error() describes the problem. Device-side data
+ *    (offsets, timestamps) is not validated: offsets must be non-decreasing
+ *    from 0 to total_tokens and 0 <= num_targets[b] <= L_b.
+ *  - Token tensors are row-major [T, H, D]: element (t, h, d) is at
+ *    t*stride + h*D + d, with `stride` (elements, >= H*D) given per input.
+ *    Outputs and gradients are dense [T, H, D] (stride H*D).
+ */
+#ifndef HSTU_ATTN_H
+#define HSTU_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define HSTU_API __attribute__((visibility("default")))
+#else
+#define HSTU_API
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_EINVAL = -1,        /* an argument is invalid (null, negative, bad stride) */
+  HSTU_EUNSUPPORTED = -2,  /* valid but not supported by these kernels        */
+  HSTU_EWORKSPACE = -3,    /* workspace missing or smaller than required       */
+  HSTU_EHIP = -4           /* a HIP runtime call or kernel launch failed       */
+} hstu_status;
+
+typedef enum {
+  HSTU_DTYPE_BF16 = 0,     /* bfloat16 storage, fp32 accumulation (MFMA)       */
+  HSTU_DTYPE_FP32 = 1      /* float32 storage and arithmetic                   */
+} hstu_dtype;
+
+/* Shape and layout of one jagged attention call (host memory). */
+typedef struct {
+  int32_t batch;           /* B >= 0 sequences                                   */
+  int32_t heads;           /* H >= 1                                             */
+  int32_t d_qk;            /* head dim of Q, K: 32, 64 or 128 (bf16); 32, 64 (fp32) */
+  int32_t d_v;             /* head dim of V, U, O: must equal d_qk               */
+  int32_t max_len;         /* >= 1; rab_pos holds 2*max_len-1 buckets            */
+  int32_t n_time_buckets;  /* entries per rab_time row (0: no time bias), <= 1024 */
+  int32_t rab_heads;       /* rows of each rab table: 1 (shared) or heads        */
+  int32_t dtype;           /* hstu_dtype of Q,K,V,U,O,dO,dQ,dK,dV,dU             */
+  int64_t total_tokens;    /* T = seq_offsets[B], 0 <= T < 2^31                  */
+  int64_t stride_q, stride_k, stride_v, stride_u;  /* elements between tokens   */
+} hstu_attn_desc;
+
+/* Bytes of workspace hstu_attn_fwd / hstu_attn_bwd need for this shape. */
+HSTU_API hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
+HSTU_API hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
+
+/*
+ * Forward.
+ *  seq_offsets  (device) int64 [B+1]
+ *  num_targets  (device) int64 [B] or NULL (no candidates)
+ *  timestamps   (device) int64 [T]; required when n_time_buckets > 0
+ *  rab_pos      (device) fp32 [rab_heads, 2*max_len-1] or NULL (no position bias)
+ *  rab_time     (device) fp32 [rab_heads, n_time_buckets] or NULL
+ *  q, k         (device) dtype [T, H, d_qk], row strides stride_q / stride_k
+ *  v, u         (device) dtype [T, H, d_v]; u NULL = no gate (O = A)
+ *  o            (device) dtype [T, H, d_v], written
+ *  a_saved      (device) fp32 [T, H, d_v] or NULL; receives A (needed by the
+ *               backward when u != NULL, and by the layer's LayerNorm)
+ *  workspace    (device) >= hstu_attn_fwd_workspace_size bytes, 256-aligned
+ */
+HSTU_API hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                          const int64_t* num_targets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time,
+                          const void* q, const void* k, const void* v, const void* u,
+                          void* o, float* a_saved,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward. Inputs as in hstu_attn_fwd, plus
+ *  a_saved      (device) fp32 [T, H, d_v] from the forward; required if u != NULL
+ *  d_o          (device) dtype [T, H, d_v] dense
+ * Outputs (device, dense, all overwritten, never accumulated into):
+ *  dq, dk       dtype [T, H, d_qk]
+ *  dv           dtype [T, H, d_v]
+ *  du           dtype [T, H, d_v]; required iff u != NULL
+ *  d_rab_pos    fp32 [rab_heads, 2*max_len-1]; required iff rab_pos != NULL
+ *  d_rab_time   fp32 [rab_heads, n_time_buckets]; required iff rab_time != NULL
+ * dQ and the rab gradients are summed with floating-point atomics, so their
+ * last bits may differ between runs.
+ */
+HSTU_API hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                          const int64_t* num_targets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time,
+                          const void* q, const void* k, const void* v, const void* u,
+                          const float* a_saved, const void* d_o,
+                          void* dq, void* dk, void* dv, void* du,
+                          float* d_rab_pos, float* d_rab_time,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rab bucket export (for checking and debugging): for every unmasked pair,
+ * in sequence order, then query row i, then key j ascending, writes the
+ * position bucket bp(i,j) and the time bucket bt(i,j).
+ *  pair_offsets (device) int64 [B+1]: first output slot of each sequence;
+ *               sequence b has hist*(hist+1)/2 + (L-hist)*(hist+1) pairs
+ *  bp_out       (device) uint16 [pairs] or NULL (requires max_len <= 32768)
+ *  bt_out       (device) uint8 [pairs] or NULL (requires timestamps and
+ *               n_time_buckets >= 1)
+ */
+HSTU_API hstu_status hstu_rab_bucketize(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                               const int64_t* num_targets, const int64_t* timestamps,
+                               const int64_t* pair_offsets, uint16_t* bp_out,
+                               uint8_t* bt_out, void* stream);
+
+/*
+ * HSTU layer pieces around the attention (Generative Recommenders README,
+ * "HSTU Ultra attention benchmark": UVQK projection, attention, output
+ * normalisation, gating and projection). bf16 storage, fp32 accumulation.
+ *
+ * hstu_linear: y[M,N] = act(x[M,K] @ w[K,N] + bias[N]); act = SiLU when
+ *   apply_silu != 0, identity otherwise.
+ *   x (device) bf16, row stride ldx >= K; w (device) bf16 [K, N] dense;
+ *   bias (device) fp32 [N] or NULL; y (device) bf16 [M, N] dense.
+ *   K must be a multiple of 32 and N a multiple of 128; M >= 0 any.
+ */
+HSTU_API hstu_status hstu_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                        const void* w, const float* bias, void* y, int32_t apply_silu,
+                        void* stream);
+
+/*
+ * hstu_layernorm_gate: out[m, :] = LayerNorm(a[m, :]) * u[m, :] over N
+ *   features, eps given, unit scale and zero shift.
+ *   a (device) fp32 [M, N] dense; u (device) bf16, row stride ldu >= N;
+ *   out (device) bf16 [M, N] dense. N must be a multiple of 64, <= 4096;
+ *   ldu a multiple of 4.
+ */
+HSTU_API hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, const void* u,
+                                int64_t ldu, float eps, void* out, void* stream);
+
+/*
+ * Per-kernel timing for benchmarks (off by default). Between
+ * hstu_profile_begin() and hstu_profile_end() every kernel launch of the
+ * library is bracketed by two HIP events recorded on the caller's stream.
+ * hstu_profile_end waits for the recorded events, writes for each kernel id
+ * i < n the summed milliseconds total_ms[i] and launch count counts[i], and
+ * turns recording off. Kernel ids: 0 .. hstu_kernel_count()-1, named by
+ * hstu_kernel_name(id). Meant for one host thread at a time.
+ */
+HSTU_API hstu_status hstu_profile_begin(void);
+HSTU_API hstu_status hstu_profile_end(int32_t n, double* total_ms, int32_t* counts);
+HSTU_API const char* hstu_kernel_name(int32_t id);
+HSTU_API int32_t hstu_kernel_count(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+HSTU_API const char* hstu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_ATTN_H */

@@ -1,0 +1,149 @@
+"""The C ABI library loads, exports what the header declares, and rejects bad
+arguments before launching anything (so these tests need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hstu_pointwise_attention_amd import _lib
+from hstu_pointwise_attention_amd.flops import unmasked_pairs_host, attention_flops
+from hstu_pointwise_attention_amd.ops import pair_offsets_host
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu_attn.h")
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libhstu_attn.so not built", allow_module_level=True)
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: every case fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return set(re.findall(r"HSTU_API\s+[\w\s\*]+?\b(hstu_\w+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_symbols()
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def good_desc(**kw):
+    d = _lib.AttnDesc()
+    d.batch, d.heads, d.d_qk, d.d_v, d.max_len = 2, 2, 64, 64, 100
+    d.n_time_buckets, d.rab_heads, d.dtype, d.total_tokens = 16, 1, _lib.DTYPE_BF16, 50
+    d.stride_q = d.stride_k = d.stride_v = d.stride_u = 128
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def fwd_call(lib, d, ws_bytes=1 << 30, rab_time=FAKE, timestamps=FAKE, ws=ctypes.c_void_p(1 << 20)):
+    return lib.hstu_attn_fwd(ctypes.byref(d), FAKE, None, timestamps, None, rab_time, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", -1, _lib.HSTU_EINVAL),
+    ("heads", 0, _lib.HSTU_EINVAL),
+    ("d_qk", 48, _lib.HSTU_EUNSUPPORTED),
+    ("d_v", 32, _lib.HSTU_EUNSUPPORTED),
+    ("dtype", 7, _lib.HSTU_EINVAL),
+    ("max_len", 0, _lib.HSTU_EINVAL),
+    ("n_time_buckets", 2000, _lib.HSTU_EINVAL),
+    ("rab_heads", 3, _lib.HSTU_EINVAL),
+    ("total_tokens", -5, _lib.HSTU_EINVAL),
+    ("total_tokens", 1 << 31, _lib.HSTU_EINVAL),
+    ("stride_q", 64, _lib.HSTU_EINVAL),
+    ("stride_k", 130, _lib.HSTU_EINVAL),
+])
+def test_desc_validation(lib, field, value, status):
+    d = good_desc(**{field: value})
+    assert fwd_call(lib, d) == status
+    assert lib.hstu_last_error().decode()
+
+
+def test_fp32_d128_unsupported(lib):
+    d = good_desc(d_qk=128, d_v=128, dtype=_lib.DTYPE_FP32, stride_q=256, stride_k=256,
+                  stride_v=256, stride_u=256)
+    assert fwd_call(lib, d) == _lib.HSTU_EUNSUPPORTED
+
+
+def test_missing_inputs(lib):
+    d = good_desc()
+    assert fwd_call(lib, d, timestamps=None) == _lib.HSTU_EINVAL          # time bias without ts
+    d0 = good_desc(n_time_buckets=0)
+    assert fwd_call(lib, d0) == _lib.HSTU_EINVAL                           # table without buckets
+    assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, None, FAKE, 1 << 30, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_attn_fwd(ctypes.byref(d), FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE,
+                             FAKE, FAKE, None, FAKE, 1 << 30, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_attn_fwd(None, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             None, FAKE, 1 << 30, None) == _lib.HSTU_EINVAL
+
+
+def test_workspace_checks(lib):
+    d = good_desc()
+    need = ctypes.c_size_t()
+    assert lib.hstu_attn_fwd_workspace_size(ctypes.byref(d), ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert fwd_call(lib, d, ws_bytes=need.value - 1) == _lib.HSTU_EWORKSPACE
+    assert fwd_call(lib, d, ws=None) == _lib.HSTU_EWORKSPACE
+    assert fwd_call(lib, d, ws=ctypes.c_void_p((1 << 20) + 8)) == _lib.HSTU_EWORKSPACE  # misaligned
+    bneed = ctypes.c_size_t()
+    assert lib.hstu_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(bneed)) == 0
+    assert bneed.value >= need.value + 50 * 128 * 4        # holds the fp32 dQ accumulator
+    assert lib.hstu_attn_fwd_workspace_size(ctypes.byref(d), None) == _lib.HSTU_EINVAL
+
+
+def test_bwd_requires_gradients(lib):
+    d = good_desc()
+    # rab_pos given without d_rab_pos
+    st = lib.hstu_attn_bwd(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.HSTU_EINVAL
+    # gated without du
+    st = lib.hstu_attn_bwd(ctypes.byref(d), FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.HSTU_EINVAL
+
+
+def test_layer_validation(lib):
+    assert lib.hstu_linear(10, 48, 128, FAKE, 48, FAKE, None, FAKE, 1, None) == _lib.HSTU_EUNSUPPORTED
+    assert lib.hstu_linear(10, 64, 100, FAKE, 64, FAKE, None, FAKE, 1, None) == _lib.HSTU_EUNSUPPORTED
+    assert lib.hstu_linear(10, 64, 128, FAKE, 32, FAKE, None, FAKE, 1, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_linear(-1, 64, 128, FAKE, 64, FAKE, None, FAKE, 1, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate(4, 100, FAKE, FAKE, 100, 1e-5, FAKE, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate(4, 512, FAKE, FAKE, 500, 1e-5, FAKE, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate(4, 512, FAKE, FAKE, 512, -1.0, FAKE, None) == _lib.HSTU_EINVAL
+
+
+def test_bucketize_validation(lib):
+    d = good_desc(max_len=40000)
+    assert lib.hstu_rab_bucketize(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) \
+        == _lib.HSTU_EINVAL
+    d = good_desc(n_time_buckets=300)
+    assert lib.hstu_rab_bucketize(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, None) \
+        == _lib.HSTU_EINVAL
+
+
+def test_host_pair_accounting_matches_oracle():
+    import numpy as np
+    from oracle.attention import unmasked_pairs
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        L = rng.integers(0, 50, size=6)
+        nt = np.minimum(rng.integers(0, 10, size=6), L)
+        offs = np.concatenate([[0], np.cumsum(L)])
+        assert unmasked_pairs_host(L, nt) == unmasked_pairs(offs, nt)
+        assert pair_offsets_host(L, nt)[-1] == unmasked_pairs(offs, nt)
+    f = attention_flops([3, 4], heads=2, d_qk=32, d_v=32)
+    assert f["pair_heads"] == 2 * (6 + 10) and f["total"] == f["pair_heads"] * 14 * 32
