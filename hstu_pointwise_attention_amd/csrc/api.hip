@@ -59,9 +59,8 @@ hstu_status check_desc(const hstu_attn_desc* d) {
     return fail(HSTU_EINVAL, "rab_heads %d must be 1 or heads (%d)", d->rab_heads, d->heads);
   if (d->total_tokens < 0 || d->total_tokens >= ((int64_t)1 << 31))
     return fail(HSTU_EINVAL, "total_tokens %lld outside [0, 2^31)", (long long)d->total_tokens);
-  if ((int64_t)d->heads * d->d_qk * d->total_tokens / (d->total_tokens ? d->total_tokens : 1) !=
-      (int64_t)d->heads * d->d_qk)
-    return fail(HSTU_EINVAL, "size overflow");
+  if ((double)d->total_tokens * d->heads * d->d_qk >= 4.0e18)
+    return fail(HSTU_EINVAL, "total_tokens * heads * d overflows the index range");
   const int64_t hd = (int64_t)d->heads * d->d_qk;
   const int vec = 16 / elem_bytes(d->dtype);
   const int64_t strides[4] = {d->stride_q, d->stride_k, d->stride_v, d->stride_u};
