@@ -60,13 +60,14 @@ struct BwdSmem {
   T kt[D * C::KT_LD];            // K^T of the key block, resident for the loop
   T dss[C::BM * C::DS_LD];
   int64_t tsq[C::BM];
+  int64_t tsk[C::BN];            // timestamps of the key block
   float win[C::WIN];
   float wing[C::WIN];
   float ttab[C::MAX_TIME];
   float thist[C::MAX_TIME];
 };
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
@@ -85,6 +86,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const int hr = p.rab_heads == 1 ? 0 : head;
   const bool has_pos = p.rab_pos != nullptr;
   const bool has_time = p.rab_time != nullptr;
+  const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
+  // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
+  // timestamps; the flag is uniform over the workgroup.
+  const bool wide = (si.flags & kSeqWideTs) != 0;
   const int n_pos = 2 * p.max_len - 1;
   const int t_last = p.n_time_buckets - 1;
   const int64_t HD = (int64_t)H * D;
@@ -116,7 +121,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     }
   }
   int64_t ts_j = 0;
-  if (has_time && key_ok) ts_j = WIDE ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
+  if (has_time && key_ok) ts_j = wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
+  if (has_time) sm.tsk[jl] = ts_j;
 
   // K^T of the whole key block into LDS; the dQ product reads this wave's
   // operand from it: lane (d, g) of d-block db_w takes K[k0 + 16kc + 8g + 0..7][d].
@@ -169,7 +175,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     }
     if (has_time && tid < C::BM) {
       const int ii = q0 + tid;
-      tsreg = ii < L ? (WIDE ? p.timestamps[start + ii] : (int64_t)p.ts_rel[start + ii]) : 0;
+      tsreg = ii < L ? (wide ? p.timestamps[start + ii] : (int64_t)p.ts_rel[start + ii]) : 0;
     }
     if (has_pos && tid < C::WIN) {
       // entry y: offset j - p_i = k0 + BN - 1 - p_min - y
@@ -226,81 +232,145 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     __syncthreads();                               // tile n staged; previous dQ done
     if (more) load_tile(q0 + C::BM);
 
+    // Tiles of history rows only sum the position gradient along diagonals of
+    // the dS tile after it is complete; tiles with candidate rows (whose
+    // position is pinned to hist) add each element into a window instead.
+    const bool pos_diag = has_pos && q0 + C::BM - 1 < hist;
     const bool skip = jw >= L || q0 + C::BM - 1 < jw ||
                       (jw >= hist && (q0 > jw + 31 || q0 + C::BM - 1 < jw));
     if (!skip) {
       const bool need_mask = !(q0 >= jw + 31 && jw + 31 < hist && q0 + C::BM - 1 < L);
       const int p_min = min(q0, hist);
-      f32x16 acc_s[C::QB], acc_p[C::QB];
+      // Time-bias mode of this wave's sub-tile (its 32 keys x the 64 queries).
+      // With sorted timestamps and every key at or before every query, the
+      // bucket grows with the query and shrinks with the key, so the corners
+      // bound it: a single bucket (mode 0) or two adjacent ones split by a
+      // per-key threshold (mode 1). Everything else takes per-element buckets
+      // (mode 2).
+      int tmode = 2, b_lo = 0, b_hi = 0;
+      uint32_t thr = 0;
+      if (has_time && !wide && sorted_ts && q0 >= jw + 31) {
+        const int qi_hi = min(q0 + C::BM - 1, L - 1) - q0;
+        const int kj_hi = min(jw + 31, L - 1) - k0;
+        b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.tsk[jw - k0], t_last);
+        b_lo = time_bucket_rel((uint32_t)sm.tsq[0], (uint32_t)sm.tsk[kj_hi], t_last);
+        if (b_hi == b_lo) {
+          tmode = 0;
+        } else if (b_hi == b_lo + 1) {
+          tmode = 1;
+          thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);   // hi iff ts_i - ts_j + 1 >= 2^b_hi
+        }
+      }
+      // Per 32-query block: S = Q K^T + bias and dP = dA' V^T, elementwise
+      // (acc_s <- SiLU(S), acc_p <- dS), then dV += s^T dA' and dK += dS^T Q
+      // over that block's two 16-query chunks (in the permuted order).
+      auto tile_math = [&](auto tm) {
+        constexpr int TM = decltype(tm)::value;
+        const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
+        const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
+        float g_all = 0.f, g_hi = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
+        for (int qb = 0; qb < C::QB; ++qb) {
+          f32x16 acc_s, acc_p;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_p[qb][r] = 0.f;
-        if (has_pos) {
+          for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
+          if (pos_diag) {
+            // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
+            const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_s[r] = w[8 * (r >> 2) + (r & 3)];
+          } else if (has_pos) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+              acc_s[r] = sm.win[(C::BN - 1 - jl) + min(q0 + ql, hist) - p_min];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
+          }
+#pragma unroll
+          for (int c = 0; c < C::KC; ++c) {
+            const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+            mfma_32x32x16(acc_s, a, kf[c]);
+            const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+            mfma_32x32x16(acc_p, b, vf[c]);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int y = (C::BN - 1 - jl) + min(q0 + ql, hist) - p_min;
-            acc_s[qb][r] = sm.win[y];
+            const int i = q0 + ql;
+            float s = acc_s[r];
+            int bt = 0;
+            bool hi = false;
+            if (has_time) {
+              if constexpr (TM == 0) {
+                s += tb_lo;
+              } else if constexpr (TM == 1) {
+                hi = (uint32_t)sm.tsq[ql] >= thr;
+                s += hi ? tb_hi : tb_lo;
+              } else {
+                const int64_t ti = sm.tsq[ql];
+                bt = wide ? time_bucket_wide(ti, ts_j, t_last)
+                          : time_bucket_rel((uint32_t)ti, (uint32_t)ts_j, t_last);
+                s += sm.ttab[bt];
+              }
+            }
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
+            float sl = s * sg;
+            float ds = acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl));
+            if (need_mask) {
+              const bool ok = j <= i && (j < hist || j == i) && i < L;
+              sl = ok ? sl : 0.f;
+              ds = ok ? ds : 0.f;
+            }
+            acc_s[r] = sl;
+            acc_p[r] = ds;
+            if (has_pos && !pos_diag) {
+              const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
+              atomicAdd(&sm.wing[y], ds);
+            }
+            if (has_time) {
+              if constexpr (TM == 2) {
+                atomicAdd(&sm.thist[bt], ds);
+              } else {
+                g_all += ds;
+                if constexpr (TM == 1) g_hi += hi ? ds : 0.f;
+              }
+            }
+            sm.dss[ql * C::DS_LD + jl] = from_f32<T>(ds);
           }
-        } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_s[qb][r] = 0.f;
+          for (int h = 0; h < 2; ++h) {
+            const int kc = 2 * qb + h;
+            const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
+            const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const F a = ld_frag(sm.dat + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+              mfma_32x32x16(acc_dv[db], sf, a);
+              const F b = ld_frag(sm.qt + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+              mfma_32x32x16(acc_dk[db], df, b);
+            }
+          }
         }
-#pragma unroll
-        for (int c = 0; c < C::KC; ++c) {
-          const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
-          mfma_32x32x16(acc_s[qb], a, kf[c]);
-          const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
-          mfma_32x32x16(acc_p[qb], b, vf[c]);
-        }
-      }
-      // Elementwise: acc_s <- SiLU(S) (for dV), acc_p <- dS (for dK, dQ).
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const int i = q0 + ql;
-          float s = acc_s[qb][r];
-          int bt = 0;
+        if constexpr (TM < 2) {
           if (has_time) {
-            const int64_t ti = sm.tsq[ql];
-            bt = WIDE ? time_bucket_wide(ti, ts_j, t_last)
-                      : time_bucket_rel((uint32_t)ti, (uint32_t)ts_j, t_last);
-            s += sm.ttab[bt];
+            g_all = wave_sum(g_all);
+            if constexpr (TM == 1) g_hi = wave_sum(g_hi);
+            if (lane == 0) {
+              atomicAdd(&sm.thist[b_lo], g_all - g_hi);
+              if constexpr (TM == 1) atomicAdd(&sm.thist[b_hi], g_hi);
+            }
           }
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
-          float sl = s * sg;
-          float ds = acc_p[qb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
-          if (need_mask) {
-            const bool ok = j <= i && (j < hist || j == i) && i < L;
-            sl = ok ? sl : 0.f;
-            ds = ok ? ds : 0.f;
-          }
-          acc_s[qb][r] = sl;
-          acc_p[qb][r] = ds;
-          if (has_pos) {
-            const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
-            atomicAdd(&sm.wing[y], ds);
-          }
-          if (has_time) atomicAdd(&sm.thist[bt], ds);
-          sm.dss[ql * C::DS_LD + jl] = from_f32<T>(ds);
         }
-      }
-      // dV += s^T dA', dK += dS^T Q (query chunks of 16 in the permuted order).
-#pragma unroll
-      for (int kc = 0; kc < C::BM / 16; ++kc) {
-        const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s[kc >> 1]) + 8 * (kc & 1));
-        const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p[kc >> 1]) + 8 * (kc & 1));
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const F a = ld_frag(sm.dat + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
-          mfma_32x32x16(acc_dv[db], sf, a);
-          const F b = ld_frag(sm.qt + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
-          mfma_32x32x16(acc_dk[db], df, b);
-        }
-      }
+      };
+      if (tmode == 0)
+        tile_math(std::integral_constant<int, 0>());
+      else if (tmode == 1)
+        tile_math(std::integral_constant<int, 1>());
+      else
+        tile_math(std::integral_constant<int, 2>());
     } else {
       // This wave's dS rows of the shared tile are zero.
 #pragma unroll
@@ -311,8 +381,24 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     }
     __syncthreads();                               // dS, rab partials complete
 
-    // Flush the position-gradient window of this tile.
-    if (has_pos && tid < C::WIN) {
+    if (pos_diag) {
+      // Diagonal sums: entry dd = key - query (within the tile) gathers the
+      // elements whose position bucket is that of offset k0 - q0 + dd.
+      if (tid < C::BM + C::BN - 1) {
+        const int dd = tid - (C::BM - 1);
+        float sum = 0.f;
+#pragma unroll 16
+        for (int ql = 0; ql < C::BM; ++ql) {
+          const int c = ql + dd;
+          const int cc = c < 0 ? 0 : (c > C::BN - 1 ? C::BN - 1 : c);
+          const float x = to_f32(sm.dss[ql * C::DS_LD + cc]);
+          sum += (c == cc) ? x : 0.f;
+        }
+        if (sum != 0.f)
+          atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos + pos_bucket(k0 - q0 + dd, p.max_len), sum);
+      }
+    } else if (has_pos && tid < C::WIN) {
+      // Flush the position-gradient window of this tile.
       const float gsum = sm.wing[tid];
       if (gsum != 0.f) {
         const int p_min = min(q0, hist);
@@ -382,10 +468,7 @@ void hstu_bwd_kernel(AttnParams p) {
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
-  if (si.flags & kSeqWideTs)
-    bwd_body<T, D, true>(p, sm, wi, si, head);
-  else
-    bwd_body<T, D, false>(p, sm, wi, si, head);
+  bwd_body<T, D>(p, sm, wi, si, head);
 }
 
 }  // namespace

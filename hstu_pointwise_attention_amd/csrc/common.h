@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hstu {
 
 typedef __bf16 bf16;
@@ -82,6 +84,12 @@ __device__ __forceinline__ void st4_from_f32(bf16* p, f32x4 v) {
   *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 __device__ __forceinline__ void st4_from_f32(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 // rab buckets. Position: clamp(j - p_i, -(max_len-1), max_len-1) + max_len-1.

@@ -58,11 +58,12 @@ struct FwdSmem {
   T k[2][C::BN * C::K_LD];
   T vt[2][D * C::V_LD];
   int64_t ts[2][C::BN];          // key timestamps: rebased (low 32 bits) or raw
+  int64_t tsq[C::BM];            // query timestamps of the block
   float win[2][C::WIN];          // rab_pos window for the tile
   float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr]
 };
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = FwdCfg<T, D>;
@@ -81,6 +82,10 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   const int hr = p.rab_heads == 1 ? 0 : head;
   const bool has_pos = p.rab_pos != nullptr;
   const bool has_time = p.rab_time != nullptr;
+  const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
+  // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
+  // timestamps; the flag is uniform over the workgroup.
+  const bool wide = (si.flags & kSeqWideTs) != 0;
   const int t_last = p.n_time_buckets - 1;
 
   const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
@@ -104,7 +109,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   }
   int64_t ts_i = 0;
   if (has_time && row_ok)
-    ts_i = WIDE ? p.timestamps[start + i] : (int64_t)p.ts_rel[start + i];
+    ts_i = wide ? p.timestamps[start + i] : (int64_t)p.ts_rel[start + i];
+  if (has_time) sm.tsq[32 * wave + l32] = ts_i;     // both lane halves hold the same row
 
   // Position-bias window: entry x holds the bias of offset j - p_i = j0 - p_max + x.
   const int p_max = min(i_last, hist);
@@ -148,7 +154,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
     }
     if (has_time && tid < C::BN) {
       const int j = j0 + tid;
-      tsreg = j < L ? (WIDE ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j]) : 0;
+      tsreg = j < L ? (wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j]) : 0;
     }
     if (has_pos && tid < C::WIN) {
       const int rel = j0 - p_max + tid;
@@ -209,53 +215,92 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
       const bool need_mask = j0 + C::BN - 1 > min(iw, hist - 1);
       const T* ks = sm.k[buf];
       const T* vt = sm.vt[buf];
-      float pv[C::KB][16];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        f32x16 acc;
-        if (has_pos) {
-          const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      // Time-bias mode of this wave's sub-tile (its 32 queries x the 64 keys):
+      // with sorted timestamps and every key at or before every query, the
+      // corners bound the bucket: one bucket (mode 0), two adjacent ones split
+      // by a per-query threshold (mode 1), else per-element buckets (mode 2).
+      int tmode = 2, b_lo = 0, b_hi = 0;
+      int32_t thr = 0;
+      if (has_time && !wide && sorted_ts && j0 + C::BN - 1 <= iw) {
+        const int qi_hi = min(iw + 31, L - 1) - i0;
+        const int kj_hi = min(j0 + C::BN - 1, L - 1) - j0;
+        b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.ts[buf][0], t_last);
+        b_lo = time_bucket_rel((uint32_t)sm.tsq[iw - i0], (uint32_t)sm.ts[buf][kj_hi], t_last);
+        if (b_hi == b_lo) {
+          tmode = 0;
+        } else if (b_hi == b_lo + 1) {
+          tmode = 1;
+          thr = (int32_t)ts_i + 1 - (1 << b_hi);     // hi iff ts_j <= ts_i + 1 - 2^b_hi
         }
+      }
+      // One 32-key block at a time: S^T block, elementwise, then its two
+      // 16-key chunks of P V.
+      auto tile_math = [&](auto tm) {
+        constexpr int TM = decltype(tm)::value;
+        const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
+        const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
 #pragma unroll
-        for (int c = 0; c < C::KC; ++c) {
-          const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
-          mfma_32x32x16(acc, a, qf[c]);
-        }
+        for (int kb = 0; kb < C::KB; ++kb) {
+          f32x16 acc;
+          if (has_pos) {
+            const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          float s;
-          if (has_time) {
-            const int64_t tj = sm.ts[buf][jl];
-            const int bt = WIDE ? time_bucket_wide(ts_i, tj, t_last)
-                                : time_bucket_rel((uint32_t)ts_i, (uint32_t)tj, t_last);
-            s = __builtin_fmaf(acc[r], kNegLog2e, sm.ttab[bt]);
+            for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
           } else {
-            s = acc[r] * kNegLog2e;
-          }
-          float pr = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s));
-          if (need_mask) {
-            const int j = j0 + jl;
-            const bool ok = j <= i && (j < hist || j == i);
-            pr = ok ? pr : 0.f;
-          }
-          pv[kb][r] = pr;
-        }
-      }
 #pragma unroll
-      for (int kc = 0; kc < C::BN / 16; ++kc) {
-        const F pf = pack8<T>(&pv[kc >> 1][8 * (kc & 1)]);
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+          }
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const F a = ld_frag(vt + (32 * db + l32) * C::V_LD + 16 * kc + 8 * g);
-          mfma_32x32x16(acc_o[db], a, pf);
+          for (int c = 0; c < C::KC; ++c) {
+            const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
+            mfma_32x32x16(acc, a, qf[c]);
+          }
+          float pv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            float s;
+            if (has_time) {
+              if constexpr (TM == 0) {
+                s = __builtin_fmaf(acc[r], kNegLog2e, tb_lo);
+              } else if constexpr (TM == 1) {
+                const bool hi = (int32_t)sm.ts[buf][jl] <= thr;
+                s = __builtin_fmaf(acc[r], kNegLog2e, hi ? tb_hi : tb_lo);
+              } else {
+                const int64_t tj = sm.ts[buf][jl];
+                const int bt = wide ? time_bucket_wide(ts_i, tj, t_last)
+                                    : time_bucket_rel((uint32_t)ts_i, (uint32_t)tj, t_last);
+                s = __builtin_fmaf(acc[r], kNegLog2e, sm.ttab[bt]);
+              }
+            } else {
+              s = acc[r] * kNegLog2e;
+            }
+            float pr = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s));
+            if (need_mask) {
+              const int j = j0 + jl;
+              const bool ok = j <= i && (j < hist || j == i);
+              pr = ok ? pr : 0.f;
+            }
+            pv[r] = pr;
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const F pf = pack8<T>(&pv[8 * h]);
+            const int kc = 2 * kb + h;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const F a = ld_frag(vt + (32 * db + l32) * C::V_LD + 16 * kc + 8 * g);
+              mfma_32x32x16(acc_o[db], a, pf);
+            }
+          }
         }
-      }
+      };
+      if (tmode == 0)
+        tile_math(std::integral_constant<int, 0>());
+      else if (tmode == 1)
+        tile_math(std::integral_constant<int, 1>());
+      else
+        tile_math(std::integral_constant<int, 2>());
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
@@ -296,12 +341,7 @@ void hstu_fwd_kernel(AttnParams p) {
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
-  // Sequences whose timestamp span needs 64-bit bucket arithmetic take the
-  // second instantiation; the branch is uniform over the workgroup.
-  if (si.flags & kSeqWideTs)
-    fwd_body<T, D, true>(p, sm, wi, si, head);
-  else
-    fwd_body<T, D, false>(p, sm, wi, si, head);
+  fwd_body<T, D>(p, sm, wi, si, head);
 }
 
 }  // namespace
