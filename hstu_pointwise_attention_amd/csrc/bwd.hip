@@ -3,23 +3,35 @@
 // One workgroup (4 waves) owns 128 keys of one sequence and one head; wave w
 // owns keys 32w..32w+31 and keeps their K, V fragments and the dK, dV
 // accumulators in registers for the whole loop over the 64-row query tiles
-// that can see those keys. Per query tile (Q and dA' = dO*U/L staged through
-// LDS, row-major and transposed):
+// that can see those keys. Per query tile (Q and dA' = dO*U/L staged
+// row-major through LDS):
 //   S    = Q K^T + bias            (recomputed; bias read as in the forward)
 //   dP   = dA' V^T
 //   sg   = sigma(S), s = S*sg, s' = sg + s*(1 - sg)   (SiLU and its derivative)
 //   dS   = dP * s'  (0 where masked)
-//   dV  += s^T dA',  dK += dS^T Q
-//   dQ  += dS K     (through LDS, then fp32 atomics into a workspace buffer)
-// The rab gradients are sums of dS over the pairs that read each table entry:
-// each element adds its dS into an LDS window over relative positions (one per
-// query tile, flushed with global atomics) and an LDS histogram over time
-// buckets (flushed once per workgroup).
+//   dV  += s^T dA',  dK += dS^T Q   (Q, dA' fragments by LDS transpose reads)
+//   dQ  += dS K     (dS through LDS, then fp32 atomics into a workspace buffer)
+// The rab gradients are sums of dS over the pairs that read each table entry.
+// Time buckets: with sorted timestamps a wave's sub-tile below the diagonal
+// has one or two buckets, summed in registers; otherwise each element adds
+// into an LDS histogram. Positions: a second, diagonal-major copy of the dS
+// tile makes every diagonal a contiguous LDS row, summed after the tile;
+// tiles with candidate rows (positions pinned to hist) add into a window.
 #include "internal.h"
 
 namespace hstu {
 
 namespace {
+
+// Row stride (elements) of the row-major Q / dA' tiles: 16-byte row reads
+// need an odd multiple of 16 bytes, transpose reads need consecutive rows
+// >= 8 banks apart.
+template <typename T, int D> struct BwdLd;
+template <> struct BwdLd<bf16, 32> { static constexpr int Q = 56; };
+template <> struct BwdLd<bf16, 64> { static constexpr int Q = 72; };
+template <> struct BwdLd<bf16, 128> { static constexpr int Q = 152; };
+template <> struct BwdLd<float, 32> { static constexpr int Q = 36; };
+template <> struct BwdLd<float, 64> { static constexpr int Q = 68; };
 
 template <typename T, int D>
 struct BwdCfg {
@@ -32,33 +44,37 @@ struct BwdCfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VPC = 16 / ES;
   static constexpr int CPR = D / VPC;
-  static constexpr int Q_LD = D + VPC;           // row-major tiles [BM][D]
-  static constexpr int QT_LD = BM + VPC;         // transposed tiles [D][BM]
+  static constexpr int Q_LD = BwdLd<T, D>::Q;    // row-major tiles [BM][D]
   static constexpr int DS_LD = BN + VPC;         // dS tile [BM][BN]
   static constexpr int KT_LD = BN + VPC;         // K^T of the key block [D][BN]
+  static constexpr int NDIAG = BM + BN - 1;      // diagonals of a tile
+  // bf16: diagonal-major copy of dS, row dd = query - key + BN - 1 (so the
+  // address of a lane's elements is a per-lane base plus constants), 64
+  // queries (+8 padding: 16-byte aligned rows, at most 2-way write
+  // conflicts). fp32 sums the diagonals from the row-major tile instead.
+  static constexpr bool DIAG_COPY = sizeof(T) == 2;
+  static constexpr int DG_LD = BM + 8;
+  static constexpr int DG_ROWS = DIAG_COPY ? NDIAG : 1;
   static constexpr int WIN = BN + BM;            // >= BN + BM - 1
-  static constexpr int UNITS = (BM / 2) * CPR;   // (row pair, chunk) staging units
-  static constexpr int UPT = (UNITS + NT - 1) / NT;
+  static constexpr int CH = BM * CPR / NT;       // 16-byte chunks per thread per tile
   static constexpr int KUNITS = (BN / 2) * CPR;  // K^T staging units
   static constexpr int KUPT = (KUNITS + NT - 1) / NT;
   static constexpr int NDQ = (QB * DB + 3) / 4;  // dQ output blocks per wave (max)
   static constexpr int MAX_TIME = 1024;
+  // Issue the next query block's S / dP MFMAs before the current block's
+  // elementwise work (two blocks live); bf16 at d = 128 lacks the registers.
+  static constexpr bool PIPE = !(sizeof(T) == 2 && D == 128);
+  static_assert(BM * CPR % NT == 0, "staging");
 };
-
-__device__ __forceinline__ int perm_pos(int idx) {
-  const int kk = idx & 15;
-  return (idx & ~15) + 8 * ((kk & 7) >> 2) + 4 * (kk >> 3) + (kk & 3);
-}
 
 template <typename T, int D>
 struct BwdSmem {
   using C = BwdCfg<T, D>;
   T qs[C::BM * C::Q_LD];
   T das[C::BM * C::Q_LD];
-  T qt[D * C::QT_LD];
-  T dat[D * C::QT_LD];
   T kt[D * C::KT_LD];            // K^T of the key block, resident for the loop
   T dss[C::BM * C::DS_LD];
+  T dsd[C::DG_ROWS * C::DG_LD];
   int64_t tsq[C::BM];
   int64_t tsk[C::BN];            // timestamps of the key block
   float win[C::WIN];
@@ -67,7 +83,18 @@ struct BwdSmem {
   float thist[C::MAX_TIME];
 };
 
-template <typename T, int D>
+__device__ __forceinline__ float sum8(const bf16x8& v) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bf16x2 pr = {v[2 * m], v[2 * m + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+  }
+  return s;
+}
+
+template <typename T, int D, bool WIDE>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
@@ -88,8 +115,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const bool has_time = p.rab_time != nullptr;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
-  // timestamps; the flag is uniform over the workgroup.
-  const bool wide = (si.flags & kSeqWideTs) != 0;
+  // timestamps and run in the second instantiation of the kernel.
+  constexpr bool wide = WIDE;
   const int n_pos = 2 * p.max_len - 1;
   const int t_last = p.n_time_buckets - 1;
   const int64_t HD = (int64_t)H * D;
@@ -104,6 +131,9 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     sm.thist[x] = 0.f;
   }
   for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
+  // Diagonal-copy entries that no element maps to stay zero for the whole loop.
+  if (C::DIAG_COPY && has_pos)
+    for (int x = tid; x < C::DG_ROWS * C::DG_LD; x += C::NT) sm.dsd[x] = from_f32<T>(0.f);
 
   // Resident K, V fragments of this lane's key (B operands of Q K^T, dA' V^T).
   F kf[C::KC], vf[C::KC];
@@ -127,24 +157,22 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   // K^T of the whole key block into LDS; the dQ product reads this wave's
   // operand from it: lane (d, g) of d-block db_w takes K[k0 + 16kc + 8g + 0..7][d].
   const int db_w = wave % C::DB;
-  {
 #pragma unroll
-    for (int m = 0; m < C::KUPT; ++m) {
-      const int un = tid + C::NT * m;
-      if (un < C::KUNITS) {
-        const int pair = un / C::CPR, cc = un % C::CPR;
-        const int jj = k0 + 2 * pair;
-        const T* src = kg + (start + jj) * p.sk + (int64_t)head * D + cc * C::VPC;
-        const u32x4 r0 = jj < L ? ld16(src) : u32x4{0, 0, 0, 0};
-        const u32x4 r1 = jj + 1 < L ? ld16(src + p.sk) : u32x4{0, 0, 0, 0};
-        const T* a = reinterpret_cast<const T*>(&r0);
-        const T* b = reinterpret_cast<const T*>(&r1);
+  for (int m = 0; m < C::KUPT; ++m) {
+    const int un = tid + C::NT * m;
+    if (un < C::KUNITS) {
+      const int pair = un / C::CPR, cc = un % C::CPR;
+      const int jj = k0 + 2 * pair;
+      const T* src = kg + (start + jj) * p.sk + (int64_t)head * D + cc * C::VPC;
+      const u32x4 r0 = jj < L ? ld16(src) : u32x4{0, 0, 0, 0};
+      const u32x4 r1 = jj + 1 < L ? ld16(src + p.sk) : u32x4{0, 0, 0, 0};
+      const T* a = reinterpret_cast<const T*>(&r0);
+      const T* b = reinterpret_cast<const T*>(&r1);
 #pragma unroll
-        for (int e = 0; e < C::VPC; ++e) {
-          T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + 2 * pair;
-          dst[0] = a[e];
-          dst[1] = b[e];
-        }
+      for (int e = 0; e < C::VPC; ++e) {
+        T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + 2 * pair;
+        dst[0] = a[e];
+        dst[1] = b[e];
       }
     }
   }
@@ -155,23 +183,20 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const int n_qt = last_row / C::BM - qt_first + 1;
 
   // ---------------------------------------------------------------- staging
-  u32x4 qreg[C::UPT][2], dreg[C::UPT][2];
+  u32x4 qreg[C::CH], dreg[C::CH];
   int64_t tsreg = 0;
   float winreg = 0.f;
 
   auto load_tile = [&](int q0) {
 #pragma unroll
-    for (int m = 0; m < C::UPT; ++m) {
-      const int un = tid + C::NT * m;
-      const int pair = un / C::CPR, cc = un % C::CPR;
-      const int ii = q0 + 2 * pair;
-      const bool in = un < C::UNITS;
-      const T* qs = qg + (start + ii) * p.sq + (int64_t)head * D + cc * C::VPC;
-      const T* ds = dag + (start + ii) * HD + (int64_t)head * D + cc * C::VPC;
-      qreg[m][0] = (in && ii < L) ? ld16(qs) : u32x4{0, 0, 0, 0};
-      qreg[m][1] = (in && ii + 1 < L) ? ld16(qs + p.sq) : u32x4{0, 0, 0, 0};
-      dreg[m][0] = (in && ii < L) ? ld16(ds) : u32x4{0, 0, 0, 0};
-      dreg[m][1] = (in && ii + 1 < L) ? ld16(ds + HD) : u32x4{0, 0, 0, 0};
+    for (int m = 0; m < C::CH; ++m) {
+      const int ch = tid + C::NT * m;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      const int ii = q0 + row;
+      qreg[m] = ii < L ? ld16(qg + (start + ii) * p.sq + (int64_t)head * D + cc * C::VPC)
+                       : u32x4{0, 0, 0, 0};
+      dreg[m] = ii < L ? ld16(dag + (start + ii) * HD + (int64_t)head * D + cc * C::VPC)
+                       : u32x4{0, 0, 0, 0};
     }
     if (has_time && tid < C::BM) {
       const int ii = q0 + tid;
@@ -186,29 +211,11 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
 
   auto store_tile = [&]() {
 #pragma unroll
-    for (int m = 0; m < C::UPT; ++m) {
-      const int un = tid + C::NT * m;
-      if (un < C::UNITS) {
-        const int pair = un / C::CPR, cc = un % C::CPR;
-        st16(sm.qs + (2 * pair) * C::Q_LD + cc * C::VPC, qreg[m][0]);
-        st16(sm.qs + (2 * pair + 1) * C::Q_LD + cc * C::VPC, qreg[m][1]);
-        st16(sm.das + (2 * pair) * C::Q_LD + cc * C::VPC, dreg[m][0]);
-        st16(sm.das + (2 * pair + 1) * C::Q_LD + cc * C::VPC, dreg[m][1]);
-        const int pos = perm_pos(2 * pair);
-        const T* qa = reinterpret_cast<const T*>(&qreg[m][0]);
-        const T* qb = reinterpret_cast<const T*>(&qreg[m][1]);
-        const T* da = reinterpret_cast<const T*>(&dreg[m][0]);
-        const T* db = reinterpret_cast<const T*>(&dreg[m][1]);
-#pragma unroll
-        for (int e = 0; e < C::VPC; ++e) {
-          T* qd = sm.qt + (cc * C::VPC + e) * C::QT_LD + pos;
-          T* dd = sm.dat + (cc * C::VPC + e) * C::QT_LD + pos;
-          qd[0] = qa[e];
-          qd[1] = qb[e];
-          dd[0] = da[e];
-          dd[1] = db[e];
-        }
-      }
+    for (int m = 0; m < C::CH; ++m) {
+      const int ch = tid + C::NT * m;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      st16(sm.qs + row * C::Q_LD + cc * C::VPC, qreg[m]);
+      st16(sm.das + row * C::Q_LD + cc * C::VPC, dreg[m]);
     }
     if (has_time && tid < C::BM) sm.tsq[tid] = tsreg;
     if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
@@ -249,7 +256,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // (mode 2).
       int tmode = 2, b_lo = 0, b_hi = 0;
       uint32_t thr = 0;
-      if (has_time && !wide && sorted_ts && q0 >= jw + 31) {
+      if (has_time && !wide && !need_mask && sorted_ts) {
         const int qi_hi = min(q0 + C::BM - 1, L - 1) - q0;
         const int kj_hi = min(jw + 31, L - 1) - k0;
         b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.tsk[jw - k0], t_last);
@@ -261,46 +268,56 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);   // hi iff ts_i - ts_j + 1 >= 2^b_hi
         }
       }
-      // Per 32-query block: S = Q K^T + bias and dP = dA' V^T, elementwise
-      // (acc_s <- SiLU(S), acc_p <- dS), then dV += s^T dA' and dK += dS^T Q
-      // over that block's two 16-query chunks (in the permuted order).
-      auto tile_math = [&](auto tm) {
+      // S = Q K^T + bias and dP = dA' V^T for one 32-query block.
+      auto sp_block = [&](int qb, f32x16& acc_s, f32x16& acc_p) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
+        if (pos_diag) {
+          // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
+          const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_s[r] = w[8 * (r >> 2) + (r & 3)];
+        } else if (has_pos) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+            acc_s[r] = sm.win[(C::BN - 1 - jl) + min(q0 + ql, hist) - p_min];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc_s, a, kf[c]);
+          const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc_p, b, vf[c]);
+        }
+      };
+      // Elementwise (acc_s <- SiLU(S), acc_p <- dS), then dV += s^T dA' and
+      // dK += dS^T Q over the block's two 16-query chunks. The next block's
+      // S and dP MFMAs are issued first so they overlap the elementwise work.
+      auto tile_math = [&](auto tm, auto mk) {
         constexpr int TM = decltype(tm)::value;
+        constexpr bool MASK = decltype(mk)::value;
         const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
+        f32x16 acc_s[C::QB], acc_p[C::QB];
+        if constexpr (C::PIPE) sp_block(0, acc_s[0], acc_p[0]);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
-          f32x16 acc_s, acc_p;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
-          if (pos_diag) {
-            // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
-            const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_s[r] = w[8 * (r >> 2) + (r & 3)];
-          } else if (has_pos) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-              acc_s[r] = sm.win[(C::BN - 1 - jl) + min(q0 + ql, hist) - p_min];
-            }
+          if constexpr (C::PIPE) {
+            if (qb + 1 < C::QB) sp_block(qb + 1, acc_s[qb + 1], acc_p[qb + 1]);
           } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_s[r] = 0.f;
-          }
-#pragma unroll
-          for (int c = 0; c < C::KC; ++c) {
-            const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
-            mfma_32x32x16(acc_s, a, kf[c]);
-            const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
-            mfma_32x32x16(acc_p, b, vf[c]);
+            sp_block(qb, acc_s[qb], acc_p[qb]);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
             const int i = q0 + ql;
-            float s = acc_s[r];
+            float s = acc_s[qb][r];
             int bt = 0;
             bool hi = false;
             if (has_time) {
@@ -309,47 +326,51 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
               } else if constexpr (TM == 1) {
                 hi = (uint32_t)sm.tsq[ql] >= thr;
                 s += hi ? tb_hi : tb_lo;
+              } else if constexpr (TM == 2) {
+                bt = time_bucket_rel((uint32_t)sm.tsq[ql], (uint32_t)ts_j, t_last);
+                s += sm.ttab[bt];
               } else {
-                const int64_t ti = sm.tsq[ql];
-                bt = wide ? time_bucket_wide(ti, ts_j, t_last)
-                          : time_bucket_rel((uint32_t)ti, (uint32_t)ts_j, t_last);
+                bt = time_bucket_wide(sm.tsq[ql], ts_j, t_last);
                 s += sm.ttab[bt];
               }
             }
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
             float sl = s * sg;
-            float ds = acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl));
-            if (need_mask) {
+            float ds = acc_p[qb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
+            if constexpr (MASK) {
               const bool ok = j <= i && (j < hist || j == i) && i < L;
               sl = ok ? sl : 0.f;
               ds = ok ? ds : 0.f;
             }
-            acc_s[r] = sl;
-            acc_p[r] = ds;
+            acc_s[qb][r] = sl;
+            acc_p[qb][r] = ds;
             if (has_pos && !pos_diag) {
               const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
               atomicAdd(&sm.wing[y], ds);
             }
             if (has_time) {
-              if constexpr (TM == 2) {
+              if constexpr (TM >= 2) {
                 atomicAdd(&sm.thist[bt], ds);
               } else {
                 g_all += ds;
                 if constexpr (TM == 1) g_hi += hi ? ds : 0.f;
               }
             }
-            sm.dss[ql * C::DS_LD + jl] = from_f32<T>(ds);
+            const T dst = from_f32<T>(ds);
+            sm.dss[ql * C::DS_LD + jl] = dst;
+            if constexpr (C::DIAG_COPY)
+              if (pos_diag) sm.dsd[(C::BN - 1 - jl) * C::DG_LD + ql * (C::DG_LD + 1)] = dst;
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int kc = 2 * qb + h;
-            const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
-            const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
+            const int kr = 32 * qb + 16 * h;
+            const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s[qb]) + 8 * h);
+            const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p[qb]) + 8 * h);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const F a = ld_frag(sm.dat + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+              const F a = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8);
               mfma_32x32x16(acc_dv[db], sf, a);
-              const F b = ld_frag(sm.qt + (32 * db + l32) * C::QT_LD + 16 * kc + 8 * g);
+              const F b = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8);
               mfma_32x32x16(acc_dk[db], df, b);
             }
           }
@@ -365,37 +386,63 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           }
         }
       };
-      if (tmode == 0)
-        tile_math(std::integral_constant<int, 0>());
-      else if (tmode == 1)
-        tile_math(std::integral_constant<int, 1>());
-      else
-        tile_math(std::integral_constant<int, 2>());
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
+      using NoMask = std::integral_constant<bool, false>;
+      using Mask = std::integral_constant<bool, true>;
+      if constexpr (WIDE) {
+        tile_math(I3(), Mask());
+      } else {
+        if (need_mask)
+          tile_math(I2(), Mask());
+        else if (tmode == 0)
+          tile_math(I0(), NoMask());
+        else if (tmode == 1)
+          tile_math(I1(), NoMask());
+        else
+          tile_math(I2(), NoMask());
+      }
     } else {
-      // This wave's dS rows of the shared tile are zero.
+      // This wave's dS entries of the shared tile are zero.
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sm.dss[(32 * qb + 8 * (r >> 2) + 4 * g + (r & 3)) * C::DS_LD + jl] = from_f32<T>(0.f);
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+          sm.dss[ql * C::DS_LD + jl] = from_f32<T>(0.f);
+          if constexpr (C::DIAG_COPY)
+            if (pos_diag) sm.dsd[(C::BN - 1 - jl) * C::DG_LD + ql * (C::DG_LD + 1)] = from_f32<T>(0.f);
+        }
     }
     __syncthreads();                               // dS, rab partials complete
 
     if (pos_diag) {
-      // Diagonal sums: entry dd = key - query (within the tile) gathers the
-      // elements whose position bucket is that of offset k0 - q0 + dd.
-      if (tid < C::BM + C::BN - 1) {
-        const int dd = tid - (C::BM - 1);
+      // Diagonal sums: diagonal dd (query - key + BN - 1 within the tile)
+      // gathers the elements whose position bucket is that of offset
+      // k0 - q0 + (BN - 1) - dd.
+      if (tid < C::NDIAG) {
+        const int dd = tid;
         float sum = 0.f;
+        if constexpr (C::DIAG_COPY) {
+          const T* row = sm.dsd + dd * C::DG_LD;
+#pragma unroll
+          for (int c = 0; c < C::BM / 8; ++c) sum += sum8(ld_frag(row + 8 * c));
+        } else {
+          const int off = (C::BN - 1) - dd;   // key - query
 #pragma unroll 16
-        for (int ql = 0; ql < C::BM; ++ql) {
-          const int c = ql + dd;
-          const int cc = c < 0 ? 0 : (c > C::BN - 1 ? C::BN - 1 : c);
-          const float x = to_f32(sm.dss[ql * C::DS_LD + cc]);
-          sum += (c == cc) ? x : 0.f;
+          for (int ql = 0; ql < C::BM; ++ql) {
+            const int c = ql + off;
+            const int cc = c < 0 ? 0 : (c > C::BN - 1 ? C::BN - 1 : c);
+            const float x = to_f32(sm.dss[ql * C::DS_LD + cc]);
+            sum += (c == cc) ? x : 0.f;
+          }
         }
         if (sum != 0.f)
-          atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos + pos_bucket(k0 - q0 + dd, p.max_len), sum);
+          atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
+                        pos_bucket(k0 - q0 + (C::BN - 1) - dd, p.max_len),
+                    sum);
       }
     } else if (has_pos && tid < C::WIN) {
       // Flush the position-gradient window of this tile.
@@ -459,7 +506,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void hstu_bwd_kernel(AttnParams p) {
   __shared__ BwdSmem<T, D> sm;
@@ -468,7 +515,8 @@ void hstu_bwd_kernel(AttnParams p) {
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
-  bwd_body<T, D>(p, sm, wi, si, head);
+  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
+  bwd_body<T, D, WIDE>(p, sm, wi, si, head);
 }
 
 }  // namespace
@@ -478,8 +526,12 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
   prof_before(kKBwd, s);
-  hipLaunchKernelGGL((hstu_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
   prof_after(kKBwd, s);
+  hipError_t e = hipGetLastError();
+  // Only a time bias can mark a sequence as needing 64-bit timestamps.
+  if (e != hipSuccess || p.rab_time == nullptr) return e;
+  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -74,6 +74,41 @@ __device__ __forceinline__ typename Frag<T>::type ld_frag(const T* p) {
   return *reinterpret_cast<const typename Frag<T>::type*>(p);
 }
 
+// Operand fragment gathered along the reduction dimension from a row-major
+// LDS tile X (row = reduction index k, ld elements per row): lane l = 32g + c
+// receives X[k][n0 + c] for the eight rows k = kr0 + 4g + {0..3} and
+// kr1 + 4g + {0..3}. For bf16 this is two ds_read_b64_tr_b16: within each
+// 16-lane group, lane s points at row (s >> 2) of a 4-row block and columns
+// 4(s & 3)..4(s & 3)+3 of a 16-column block, and the transpose hands lane s
+// column s of the block, rows 0..3. fp32 gathers element by element.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ bf16x8 ld_frag_kmajor(const bf16* X, int ld, int n0, int kr0, int kr1) {
+  const int l = threadIdx.x & 63, s = l & 15, g = l >> 5;
+  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+  const bf16* p0 = X + (kr0 + 4 * g + (s >> 2)) * ld + col;
+  const bf16* p1 = X + (kr1 + 4 * g + (s >> 2)) * ld + col;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+  // joined as integers and cast once: element-wise bf16 casts of the
+  // results were mis-compiled (every element became element 0)
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+__device__ __forceinline__ f32x8 ld_frag_kmajor(const float* X, int ld, int n0, int kr0, int kr1) {
+  const int l = threadIdx.x & 63, g = l >> 5, n = n0 + (l & 31);
+  f32x8 f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f[m] = X[(kr0 + 4 * g + m) * ld + n];
+    f[4 + m] = X[(kr1 + 4 * g + m) * ld + n];
+  }
+  return f;
+}
+
 // Four consecutive elements <-> f32x4 (8-byte bf16 or 16-byte fp32 accesses).
 __device__ __forceinline__ f32x4 ld4_f32(const bf16* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);

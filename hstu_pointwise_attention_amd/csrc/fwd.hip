@@ -3,8 +3,8 @@
 // One workgroup (4 waves) owns 128 query rows of one sequence and one head;
 // wave w owns rows 32w..32w+31. It walks the key tiles (64 keys) that hold at
 // least one unmasked pair for its rows, skipping the candidate-only tiles of
-// M-FALCON-style batches, with K and V staged through LDS in two buffers so
-// the global loads of tile t+1 overlap the math of tile t.
+// M-FALCON-style batches. K and V tiles are staged row-major through LDS in
+// two buffers so the global loads of tile t+1 overlap the math of tile t.
 //
 // Per tile and wave, with S^T = K Q^T computed as 32 x 32 MFMA blocks (keys on
 // rows, the wave's queries on columns):
@@ -12,16 +12,28 @@
 //   S'    = -log2(e) * (acc + rab_time[bt])         (one FMA per element)
 //   p     = S' / (1 + 2^S')     = SiLU(S) / (-ln 2)
 //   p     = 0 where masked (selection, never multiplication)
-//   O^T  += V^T P^T            (V stored transposed in LDS)
+//   O^T  += V^T P^T            (V^T fragments by LDS transpose reads)
 // and the epilogue applies the factor -ln(2)/L, stores A (fp32) and O = A*U.
-// The accumulator layout of S^T is already the B-operand layout of P^T for
-// the second product once V^T's keys are stored in the matching order, so P
-// never leaves registers.
+// The accumulator layout of S^T is the B-operand layout of P^T, so P never
+// leaves registers; the key order it implies is absorbed by the rows each
+// transpose read starts from. The MFMAs of the next 32-key block are issued
+// before the elementwise work of the current one so the two overlap.
 #include "internal.h"
 
 namespace hstu {
 
 namespace {
+
+// Row strides (elements) of the LDS tiles. K is read with 16-byte row
+// fragments (conflict-free when the stride is an odd multiple of 16 bytes);
+// V is read with transpose reads, four consecutive rows of 32 bytes per
+// 16-lane group, conflict-free when consecutive rows start >= 8 banks apart.
+template <typename T, int D> struct FwdLd;
+template <> struct FwdLd<bf16, 32> { static constexpr int K = 40, V = 56; };
+template <> struct FwdLd<bf16, 64> { static constexpr int K = 72, V = 72; };
+template <> struct FwdLd<bf16, 128> { static constexpr int K = 136, V = 152; };
+template <> struct FwdLd<float, 32> { static constexpr int K = 36, V = 36; };
+template <> struct FwdLd<float, 64> { static constexpr int K = 68, V = 68; };
 
 template <typename T, int D>
 struct FwdCfg {
@@ -34,36 +46,26 @@ struct FwdCfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VPC = 16 / ES;            // elements per 16-byte chunk
   static constexpr int CPR = D / VPC;            // 16-byte chunks per row
-  static constexpr int K_LD = D + VPC;           // LDS row stride of K (elements)
-  static constexpr int V_LD = BN + VPC;          // LDS row stride of V^T (elements)
+  static constexpr int K_LD = FwdLd<T, D>::K;
+  static constexpr int V_LD = FwdLd<T, D>::V;
   static constexpr int WIN = BN + BM;            // position-bias window (>= BN + BM - 1)
-  static constexpr int K_CH = BN * CPR / NT;     // K 16-byte chunks per thread
-  static constexpr int V_UNITS = (BN / 2) * CPR; // (key pair, chunk) units
-  static constexpr int V_CH = (V_UNITS + NT - 1) / NT;
+  static constexpr int CH = BN * CPR / NT;       // 16-byte chunks per thread per tile (K or V)
   static constexpr int MAX_TIME = 1024;
-  static_assert(BN * CPR % NT == 0, "K staging");
+  static_assert(BN * CPR % NT == 0, "staging");
 };
-
-// Position of key kk (0..15) inside a 16-key chunk of V^T: swaps the middle
-// two groups of four, so positions 8g..8g+7 hold keys 4g..4g+3 and
-// 8+4g..8+4g+3 -- the keys lane group g holds in the S^T accumulator.
-__device__ __forceinline__ int vt_pos(int key) {
-  const int kk = key & 15;
-  return (key & ~15) + 8 * ((kk & 7) >> 2) + 4 * (kk >> 3) + (kk & 3);
-}
 
 template <typename T, int D>
 struct FwdSmem {
   using C = FwdCfg<T, D>;
   T k[2][C::BN * C::K_LD];
-  T vt[2][D * C::V_LD];
+  T v[2][C::BN * C::V_LD];
   int64_t ts[2][C::BN];          // key timestamps: rebased (low 32 bits) or raw
   int64_t tsq[C::BM];            // query timestamps of the block
   float win[2][C::WIN];          // rab_pos window for the tile
   float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr]
 };
 
-template <typename T, int D>
+template <typename T, int D, bool WIDE>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = FwdCfg<T, D>;
@@ -84,8 +86,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   const bool has_time = p.rab_time != nullptr;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
-  // timestamps; the flag is uniform over the workgroup.
-  const bool wide = (si.flags & kSeqWideTs) != 0;
+  // timestamps and run in the second instantiation of the kernel.
+  constexpr bool wide = WIDE;
   const int t_last = p.n_time_buckets - 1;
 
   const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
@@ -126,8 +128,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   const int n_tiles = n_a + max(0, t_end - b_start);
 
   // ---------------------------------------------------------------- staging
-  u32x4 kreg[C::K_CH];
-  u32x4 vreg[C::V_CH][2];
+  u32x4 kreg[C::CH], vreg[C::CH];
   int64_t tsreg = 0;
   float winreg = 0.f;
 
@@ -135,22 +136,13 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 
   auto load_tile = [&](int j0) {
 #pragma unroll
-    for (int m = 0; m < C::K_CH; ++m) {
+    for (int m = 0; m < C::CH; ++m) {
       const int ch = tid + C::NT * m;
       const int row = ch / C::CPR, cc = ch % C::CPR;
       const int j = j0 + row;
-      kreg[m] = j < L ? ld16(kg + (start + j) * p.sk + (int64_t)head * D + cc * C::VPC)
-                      : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int m = 0; m < C::V_CH; ++m) {
-      const int un = tid + C::NT * m;
-      const int pair = un / C::CPR, cc = un % C::CPR;
-      const int j = j0 + 2 * pair;
-      const bool in = un < C::V_UNITS;
-      const T* src = vg + (start + j) * p.sv + (int64_t)head * D + cc * C::VPC;
-      vreg[m][0] = (in && j < L) ? ld16(src) : u32x4{0, 0, 0, 0};
-      vreg[m][1] = (in && j + 1 < L) ? ld16(src + p.sv) : u32x4{0, 0, 0, 0};
+      const int64_t off = (int64_t)head * D + cc * C::VPC;
+      kreg[m] = j < L ? ld16(kg + (start + j) * p.sk + off) : u32x4{0, 0, 0, 0};
+      vreg[m] = j < L ? ld16(vg + (start + j) * p.sv + off) : u32x4{0, 0, 0, 0};
     }
     if (has_time && tid < C::BN) {
       const int j = j0 + tid;
@@ -163,29 +155,12 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   };
 
   auto store_tile = [&](int buf) {
-    T* ks = sm.k[buf];
 #pragma unroll
-    for (int m = 0; m < C::K_CH; ++m) {
+    for (int m = 0; m < C::CH; ++m) {
       const int ch = tid + C::NT * m;
       const int row = ch / C::CPR, cc = ch % C::CPR;
-      st16(ks + row * C::K_LD + cc * C::VPC, kreg[m]);
-    }
-    T* vt = sm.vt[buf];
-#pragma unroll
-    for (int m = 0; m < C::V_CH; ++m) {
-      const int un = tid + C::NT * m;
-      if (un < C::V_UNITS) {
-        const int pair = un / C::CPR, cc = un % C::CPR;
-        const int pos = vt_pos(2 * pair);
-        const T* a = reinterpret_cast<const T*>(&vreg[m][0]);
-        const T* b = reinterpret_cast<const T*>(&vreg[m][1]);
-#pragma unroll
-        for (int e = 0; e < C::VPC; ++e) {
-          T* dst = vt + (cc * C::VPC + e) * C::V_LD + pos;
-          dst[0] = a[e];
-          dst[1] = b[e];
-        }
-      }
+      st16(sm.k[buf] + row * C::K_LD + cc * C::VPC, kreg[m]);
+      st16(sm.v[buf] + row * C::V_LD + cc * C::VPC, vreg[m]);
     }
     if (has_time && tid < C::BN) sm.ts[buf][tid] = tsreg;
     if (has_pos && tid < C::WIN) sm.win[buf][tid] = winreg;
@@ -214,14 +189,14 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
     if (!skip) {
       const bool need_mask = j0 + C::BN - 1 > min(iw, hist - 1);
       const T* ks = sm.k[buf];
-      const T* vt = sm.vt[buf];
+      const T* vs = sm.v[buf];
       // Time-bias mode of this wave's sub-tile (its 32 queries x the 64 keys):
       // with sorted timestamps and every key at or before every query, the
       // corners bound the bucket: one bucket (mode 0), two adjacent ones split
       // by a per-query threshold (mode 1), else per-element buckets (mode 2).
       int tmode = 2, b_lo = 0, b_hi = 0;
       int32_t thr = 0;
-      if (has_time && !wide && sorted_ts && j0 + C::BN - 1 <= iw) {
+      if (has_time && !wide && !need_mask && sorted_ts && j0 + C::BN - 1 <= iw) {
         const int qi_hi = min(iw + 31, L - 1) - i0;
         const int kj_hi = min(j0 + C::BN - 1, L - 1) - j0;
         b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.ts[buf][0], t_last);
@@ -233,50 +208,57 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
           thr = (int32_t)ts_i + 1 - (1 << b_hi);     // hi iff ts_j <= ts_i + 1 - 2^b_hi
         }
       }
-      // One 32-key block at a time: S^T block, elementwise, then its two
-      // 16-key chunks of P V.
-      auto tile_math = [&](auto tm) {
+      auto s_block = [&](int kb, f32x16& acc) {
+        if (has_pos) {
+          const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc, a, qf[c]);
+        }
+      };
+      // TM: time-bias mode (3: 64-bit timestamps); MASK: causal / candidate
+      // masking (only tiles that cross the diagonal or hold candidates).
+      auto tile_math = [&](auto tm, auto mk) {
         constexpr int TM = decltype(tm)::value;
+        constexpr bool MASK = decltype(mk)::value;
         const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
+        f32x16 sacc[C::KB];
+        s_block(0, sacc[0]);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
-          f32x16 acc;
-          if (has_pos) {
-            const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-          }
-#pragma unroll
-          for (int c = 0; c < C::KC; ++c) {
-            const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
-            mfma_32x32x16(acc, a, qf[c]);
-          }
+          if (kb + 1 < C::KB) s_block(kb + 1, sacc[kb + 1]);
           float pv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+            const float a = sacc[kb][r];
             float s;
             if (has_time) {
               if constexpr (TM == 0) {
-                s = __builtin_fmaf(acc[r], kNegLog2e, tb_lo);
+                s = __builtin_fmaf(a, kNegLog2e, tb_lo);
               } else if constexpr (TM == 1) {
                 const bool hi = (int32_t)sm.ts[buf][jl] <= thr;
-                s = __builtin_fmaf(acc[r], kNegLog2e, hi ? tb_hi : tb_lo);
+                s = __builtin_fmaf(a, kNegLog2e, hi ? tb_hi : tb_lo);
+              } else if constexpr (TM == 2) {
+                const int bt = time_bucket_rel((uint32_t)ts_i, (uint32_t)sm.ts[buf][jl], t_last);
+                s = __builtin_fmaf(a, kNegLog2e, sm.ttab[bt]);
               } else {
-                const int64_t tj = sm.ts[buf][jl];
-                const int bt = wide ? time_bucket_wide(ts_i, tj, t_last)
-                                    : time_bucket_rel((uint32_t)ts_i, (uint32_t)tj, t_last);
-                s = __builtin_fmaf(acc[r], kNegLog2e, sm.ttab[bt]);
+                const int bt = time_bucket_wide(ts_i, sm.ts[buf][jl], t_last);
+                s = __builtin_fmaf(a, kNegLog2e, sm.ttab[bt]);
               }
             } else {
-              s = acc[r] * kNegLog2e;
+              s = a * kNegLog2e;
             }
             float pr = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s));
-            if (need_mask) {
+            if constexpr (MASK) {
               const int j = j0 + jl;
               const bool ok = j <= i && (j < hist || j == i);
               pr = ok ? pr : 0.f;
@@ -286,21 +268,33 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const F pf = pack8<T>(&pv[8 * h]);
-            const int kc = 2 * kb + h;
+            const int kr = 32 * kb + 16 * h;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const F a = ld_frag(vt + (32 * db + l32) * C::V_LD + 16 * kc + 8 * g);
+              const F a = ld_frag_kmajor(vs, C::V_LD, 32 * db, kr, kr + 8);
               mfma_32x32x16(acc_o[db], a, pf);
             }
           }
         }
       };
-      if (tmode == 0)
-        tile_math(std::integral_constant<int, 0>());
-      else if (tmode == 1)
-        tile_math(std::integral_constant<int, 1>());
-      else
-        tile_math(std::integral_constant<int, 2>());
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
+      using NoMask = std::integral_constant<bool, false>;
+      using Mask = std::integral_constant<bool, true>;
+      if constexpr (WIDE) {
+        tile_math(I3(), Mask());
+      } else {
+        if (need_mask)
+          tile_math(I2(), Mask());
+        else if (tmode == 0)
+          tile_math(I0(), NoMask());
+        else if (tmode == 1)
+          tile_math(I1(), NoMask());
+        else
+          tile_math(I2(), NoMask());
+      }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
@@ -332,7 +326,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D> sm;
@@ -341,7 +335,8 @@ void hstu_fwd_kernel(AttnParams p) {
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
-  fwd_body<T, D>(p, sm, wi, si, head);
+  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
+  fwd_body<T, D, WIDE>(p, sm, wi, si, head);
 }
 
 }  // namespace
@@ -351,8 +346,12 @@ hipError_t launch_fwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
   prof_before(kKFwd, s);
-  hipLaunchKernelGGL((hstu_fwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
   prof_after(kKFwd, s);
+  hipError_t e = hipGetLastError();
+  // Only a time bias can mark a sequence as needing 64-bit timestamps.
+  if (e != hipSuccess || p.rab_time == nullptr) return e;
+  hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
