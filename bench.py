@@ -37,11 +37,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--workload", default="efficiency_8192_bf16")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(steps: int) -> None:
+    """A plain device-to-device copy of known size: FETCH_SIZE / WRITE_SIZE of
+    this kernel against its 256 MiB read + 256 MiB write calibrate the
+    counters used for the traffic figures."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": max(steps, 1)}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by sequence, see the design notes).", file=sys.stderr)

@@ -94,7 +94,7 @@ __device__ __forceinline__ float sum8(const bf16x8& v) {
   return s;
 }
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
@@ -111,8 +111,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const int j = k0 + jl;
   const bool key_ok = j < L;
   const int hr = p.rab_heads == 1 ? 0 : head;
-  const bool has_pos = p.rab_pos != nullptr;
-  const bool has_time = p.rab_time != nullptr;
+  // Which bias terms exist is a compile-time choice so the tile loop is
+  // straight-line code the scheduler can interleave.
+  constexpr bool has_pos = POS;
+  constexpr bool has_time = TIME;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
   // timestamps and run in the second instantiation of the kernel.
@@ -152,7 +154,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   }
   int64_t ts_j = 0;
   if (has_time && key_ok) ts_j = wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
-  if (has_time) sm.tsk[jl] = ts_j;
+  if constexpr (has_time) sm.tsk[jl] = ts_j;
 
   // K^T of the whole key block into LDS; the dQ product reads this wave's
   // operand from it: lane (d, g) of d-block db_w takes K[k0 + 16kc + 8g + 0..7][d].
@@ -277,7 +279,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_s[r] = w[8 * (r >> 2) + (r & 3)];
-        } else if (has_pos) {
+        } else if constexpr (has_pos) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -320,7 +322,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             float s = acc_s[qb][r];
             int bt = 0;
             bool hi = false;
-            if (has_time) {
+            if constexpr (has_time) {
               if constexpr (TM == 0) {
                 s += tb_lo;
               } else if constexpr (TM == 1) {
@@ -348,7 +350,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
               const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
               atomicAdd(&sm.wing[y], ds);
             }
-            if (has_time) {
+            if constexpr (has_time) {
               if constexpr (TM >= 2) {
                 atomicAdd(&sm.thist[bt], ds);
               } else {
@@ -376,7 +378,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           }
         }
         if constexpr (TM < 2) {
-          if (has_time) {
+          if constexpr (has_time) {
             g_all = wave_sum(g_all);
             if constexpr (TM == 1) g_hi = wave_sum(g_hi);
             if (lane == 0) {
@@ -482,7 +484,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   }
 
   // Time-gradient histogram of this workgroup.
-  if (has_time) {
+  if constexpr (has_time) {
     __syncthreads();
     for (int x = tid; x < p.n_time_buckets; x += C::NT) {
       const float gsum = sm.thist[x];
@@ -506,7 +508,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   }
 }
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void hstu_bwd_kernel(AttnParams p) {
   __shared__ BwdSmem<T, D> sm;
@@ -516,7 +518,7 @@ void hstu_bwd_kernel(AttnParams p) {
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
   if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  bwd_body<T, D, WIDE>(p, sm, wi, si, head);
+  bwd_body<T, D, WIDE, POS, TIME>(p, sm, wi, si, head);
 }
 
 }  // namespace
@@ -525,13 +527,19 @@ template <typename T, int D>
 hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
+  const dim3 g((unsigned)grid), b(256);
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(kKBwd, s);
-  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (pos && time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, true, true>), g, b, 0, s, p);
+  else if (pos) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, true, false>), g, b, 0, s, p);
+  else if (time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, false, true>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, false, false>), g, b, 0, s, p);
   prof_after(kKBwd, s);
   hipError_t e = hipGetLastError();
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (e != hipSuccess || p.rab_time == nullptr) return e;
-  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (e != hipSuccess || !time) return e;
+  if (pos) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, true, true>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, false, true>), g, b, 0, s, p);
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ struct FwdSmem {
   float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr]
 };
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = FwdCfg<T, D>;
@@ -82,8 +82,10 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   const int i = iw + l32;                        // this lane's query row
   const bool row_ok = i < L;
   const int hr = p.rab_heads == 1 ? 0 : head;
-  const bool has_pos = p.rab_pos != nullptr;
-  const bool has_time = p.rab_time != nullptr;
+  // Which bias terms exist is a compile-time choice so the tile loop is
+  // straight-line code the scheduler can interleave.
+  constexpr bool has_pos = POS;
+  constexpr bool has_time = TIME;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
   // timestamps and run in the second instantiation of the kernel.
@@ -94,7 +96,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
   const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
 
-  if (has_time)
+  if constexpr (has_time)
     for (int x = tid; x < p.n_time_buckets; x += C::NT)
       sm.ttab[x] = kNegLog2e * p.rab_time[(int64_t)hr * p.n_time_buckets + x];
 
@@ -112,7 +114,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   int64_t ts_i = 0;
   if (has_time && row_ok)
     ts_i = wide ? p.timestamps[start + i] : (int64_t)p.ts_rel[start + i];
-  if (has_time) sm.tsq[32 * wave + l32] = ts_i;     // both lane halves hold the same row
+  if constexpr (has_time) sm.tsq[32 * wave + l32] = ts_i;     // both lane halves hold the same row
 
   // Position-bias window: entry x holds the bias of offset j - p_i = j0 - p_max + x.
   const int p_max = min(i_last, hist);
@@ -209,7 +211,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
         }
       }
       auto s_block = [&](int kb, f32x16& acc) {
-        if (has_pos) {
+        if constexpr (has_pos) {
           const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
@@ -241,7 +243,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
             const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
             const float a = sacc[kb][r];
             float s;
-            if (has_time) {
+            if constexpr (has_time) {
               if constexpr (TM == 0) {
                 s = __builtin_fmaf(a, kNegLog2e, tb_lo);
               } else if constexpr (TM == 1) {
@@ -326,7 +328,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
   }
 }
 
-template <typename T, int D, bool WIDE>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D> sm;
@@ -336,7 +338,7 @@ void hstu_fwd_kernel(AttnParams p) {
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
   if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  fwd_body<T, D, WIDE>(p, sm, wi, si, head);
+  fwd_body<T, D, WIDE, POS, TIME>(p, sm, wi, si, head);
 }
 
 }  // namespace
@@ -345,13 +347,19 @@ template <typename T, int D>
 hipError_t launch_fwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
+  const dim3 g((unsigned)grid), b(256);
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(kKFwd, s);
-  hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (pos && time) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, true, true>), g, b, 0, s, p);
+  else if (pos) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, true, false>), g, b, 0, s, p);
+  else if (time) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, false, true>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, false, false>), g, b, 0, s, p);
   prof_after(kKFwd, s);
   hipError_t e = hipGetLastError();
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (e != hipSuccess || p.rab_time == nullptr) return e;
-  hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  if (e != hipSuccess || !time) return e;
+  if (pos) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true, true, true>), g, b, 0, s, p);
+  else hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true, false, true>), g, b, 0, s, p);
   return hipGetLastError();
 }
 
