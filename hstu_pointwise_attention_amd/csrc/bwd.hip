@@ -4,19 +4,27 @@
 // owns keys 32w..32w+31 and keeps their K, V fragments and the dK, dV
 // accumulators in registers for the whole loop over the 64-row query tiles
 // that can see those keys. Per query tile (Q and dA' = dO*U/L staged
-// row-major through LDS):
+// row-major through LDS) and 32-query block:
 //   S    = Q K^T + bias            (recomputed; bias read as in the forward)
 //   dP   = dA' V^T
 //   sg   = sigma(S), s = S*sg, s' = sg + s*(1 - sg)   (SiLU and its derivative)
 //   dS   = dP * s'  (0 where masked)
 //   dV  += s^T dA',  dK += dS^T Q   (Q, dA' fragments by LDS transpose reads)
-//   dQ  += dS K     (dS through LDS, then fp32 atomics into a workspace buffer)
+// The accumulators hold S and dP with keys on lanes, which is the operand
+// layout dV and dK need. dQ = dS K needs queries on lanes instead: each
+// wave's dS block goes through the matrix core once more against one-hot
+// operands (an exact transpose), lands in a shared LDS dS tile with two
+// 16-byte stores per lane, and after the tile the four waves compute dQ
+// blocks from it against K^T and add them into an fp32 workspace with
+// atomics. Keys inside each 16-key chunk of the dS tile and of K^T follow
+// the order the transposed accumulator delivers them in.
 // The rab gradients are sums of dS over the pairs that read each table entry.
 // Time buckets: with sorted timestamps a wave's sub-tile below the diagonal
 // has one or two buckets, summed in registers; otherwise each element adds
-// into an LDS histogram. Positions: a second, diagonal-major copy of the dS
-// tile makes every diagonal a contiguous LDS row, summed after the tile;
-// tiles with candidate rows (positions pinned to hist) add into a window.
+// into an LDS histogram. Positions: a diagonal-major copy of the dS tile
+// makes every diagonal a contiguous LDS row, summed after the tile; tiles
+// with candidate rows (positions pinned to hist) add each element into a
+// window instead.
 #include "internal.h"
 
 namespace hstu {
@@ -45,13 +53,13 @@ struct BwdCfg {
   static constexpr int VPC = 16 / ES;
   static constexpr int CPR = D / VPC;
   static constexpr int Q_LD = BwdLd<T, D>::Q;    // row-major tiles [BM][D]
-  static constexpr int DS_LD = BN + VPC;         // dS tile [BM][BN]
+  static constexpr int DT_LD = BN + VPC;         // dS tile [BM][BN]; rows 16 bytes apart in banks
   static constexpr int KT_LD = BN + VPC;         // K^T of the key block [D][BN]
   static constexpr int NDIAG = BM + BN - 1;      // diagonals of a tile
   // bf16: diagonal-major copy of dS, row dd = query - key + BN - 1 (so the
   // address of a lane's elements is a per-lane base plus constants), 64
   // queries (+8 padding: 16-byte aligned rows, at most 2-way write
-  // conflicts). fp32 sums the diagonals from the row-major tile instead.
+  // conflicts). fp32 sums the diagonals from the dS tile instead.
   static constexpr bool DIAG_COPY = sizeof(T) == 2;
   static constexpr int DG_LD = BM + 8;
   static constexpr int DG_ROWS = DIAG_COPY ? NDIAG : 1;
@@ -61,27 +69,31 @@ struct BwdCfg {
   static constexpr int KUPT = (KUNITS + NT - 1) / NT;
   static constexpr int NDQ = (QB * DB + 3) / 4;  // dQ output blocks per wave (max)
   static constexpr int MAX_TIME = 1024;
-  // Issue the next query block's S / dP MFMAs before the current block's
-  // elementwise work (two blocks live); bf16 at d = 128 lacks the registers.
-  static constexpr bool PIPE = !(sizeof(T) == 2 && D == 128);
   static_assert(BM * CPR % NT == 0, "staging");
 };
 
+// The arrays the tile loop touches per element come first, so their LDS
+// addresses fit the 16-bit immediate offsets of the ds instructions.
 template <typename T, int D>
 struct BwdSmem {
   using C = BwdCfg<T, D>;
   T qs[C::BM * C::Q_LD];
   T das[C::BM * C::Q_LD];
-  T kt[D * C::KT_LD];            // K^T of the key block, resident for the loop
-  T dss[C::BM * C::DS_LD];
-  T dsd[C::DG_ROWS * C::DG_LD];
-  int64_t tsq[C::BM];
-  int64_t tsk[C::BN];            // timestamps of the key block
+  T dst[C::BM * C::DT_LD];       // dS of the tile, query rows, keys in chunk order
   float win[C::WIN];
   float wing[C::WIN];
+  int64_t tsq[C::BM];
+  T kt[D * C::KT_LD];            // K^T of the key block, keys in chunk order
+  T dsd[C::DG_ROWS * C::DG_LD];
+  int64_t tsk[C::BN];            // timestamps of the key block
   float ttab[C::MAX_TIME];
   float thist[C::MAX_TIME];
 };
+
+// Key order inside a 16-key chunk of the dS tile and K^T: slot s holds key
+// offset s with bits 2 and 3 swapped (the order in which a transposed 32x32
+// accumulator hands a lane its keys). The map is its own inverse.
+__device__ __forceinline__ int chunk_slot(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 __device__ __forceinline__ float sum8(const bf16x8& v) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
@@ -92,6 +104,11 @@ __device__ __forceinline__ float sum8(const bf16x8& v) {
     s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
   }
   return s;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_frag(T* p, const typename Frag<T>::type& f) {
+  *reinterpret_cast<typename Frag<T>::type*>(p) = f;
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
@@ -156,9 +173,18 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   if (has_time && key_ok) ts_j = wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
   if constexpr (has_time) sm.tsk[jl] = ts_j;
 
-  // K^T of the whole key block into LDS; the dQ product reads this wave's
-  // operand from it: lane (d, g) of d-block db_w takes K[k0 + 16kc + 8g + 0..7][d].
-  const int db_w = wave % C::DB;
+  // One-hot operands of the transpose: eh[h] is the 16 x 32 block whose
+  // slot 8g + m of column c is 1 iff c is query 16h + 8(m/4) + 4g + m%4 of
+  // the 32-query block (the query that slot holds in the dS operand).
+  F eh[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      eh[h][m] = from_f32<T>(l32 == 16 * h + 8 * (m >> 2) + 4 * g + (m & 3) ? 1.f : 0.f);
+
+  // K^T of the whole key block into LDS, keys in chunk order: the dQ product
+  // reads lane (d, g)'s operand as 16 contiguous bytes at slot 8g of a chunk.
 #pragma unroll
   for (int m = 0; m < C::KUPT; ++m) {
     const int un = tid + C::NT * m;
@@ -170,9 +196,12 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       const u32x4 r1 = jj + 1 < L ? ld16(src + p.sk) : u32x4{0, 0, 0, 0};
       const T* a = reinterpret_cast<const T*>(&r0);
       const T* b = reinterpret_cast<const T*>(&r1);
+      // keys 2*pair and 2*pair + 1 differ in bit 0 only, which the chunk
+      // order keeps: their slots are adjacent
+      const int slot = chunk_slot(2 * pair);
 #pragma unroll
       for (int e = 0; e < C::VPC; ++e) {
-        T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + 2 * pair;
+        T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + slot;
         dst[0] = a[e];
         dst[1] = b[e];
       }
@@ -232,6 +261,12 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       acc_dv[db][r] = 0.f;
     }
 
+  // Per-lane bases: this lane's 16-byte slots of the dS tile (query row
+  // l32 of a block, keys of its wave) and of the diagonal copy.
+  T* const dst_lane = sm.dst + l32 * C::DT_LD + 32 * wave + 8 * g;
+  T* const dsd_lane =
+      C::DIAG_COPY ? sm.dsd + (C::BN - 1 - jl) * C::DG_LD + 4 * g * (C::DG_LD + 1) : sm.dsd;
+
   load_tile(qt_first * C::BM);
   store_tile();
 
@@ -270,11 +305,14 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);   // hi iff ts_i - ts_j + 1 >= 2^b_hi
         }
       }
-      // S = Q K^T + bias and dP = dA' V^T for one 32-query block.
-      auto sp_block = [&](int qb, f32x16& acc_s, f32x16& acc_p) {
+      // S = Q K^T + bias and dP = dA' V^T for one 32-query block. PD: the
+      // tile holds history rows only (compile-time, so the element loop
+      // below stays branch-free).
+      auto sp_block = [&](auto pd, int qb, f32x16& acc_s, f32x16& acc_p) {
+        constexpr bool PD = decltype(pd)::value;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
-        if (pos_diag) {
+        if constexpr (PD) {
           // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
           const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
 #pragma unroll
@@ -297,29 +335,25 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           mfma_32x32x16(acc_p, b, vf[c]);
         }
       };
-      // Elementwise (acc_s <- SiLU(S), acc_p <- dS), then dV += s^T dA' and
-      // dK += dS^T Q over the block's two 16-query chunks. The next block's
-      // S and dP MFMAs are issued first so they overlap the elementwise work.
-      auto tile_math = [&](auto tm, auto mk) {
+      // Per 32-query block: elementwise (SiLU and dS), dV += s^T dA' and
+      // dK += dS^T Q over the block's two 16-query chunks, then the
+      // transposed dS block into the shared tile.
+      auto tile_math = [&](auto tm, auto mk, auto pd) {
         constexpr int TM = decltype(tm)::value;
         constexpr bool MASK = decltype(mk)::value;
+        constexpr bool PD = decltype(pd)::value;
         const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
-        f32x16 acc_s[C::QB], acc_p[C::QB];
-        if constexpr (C::PIPE) sp_block(0, acc_s[0], acc_p[0]);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
-          if constexpr (C::PIPE) {
-            if (qb + 1 < C::QB) sp_block(qb + 1, acc_s[qb + 1], acc_p[qb + 1]);
-          } else {
-            sp_block(qb, acc_s[qb], acc_p[qb]);
-          }
+          f32x16 acc_s, acc_p;
+          sp_block(pd, qb, acc_s, acc_p);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
             const int i = q0 + ql;
-            float s = acc_s[qb][r];
+            float s = acc_s[r];
             int bt = 0;
             bool hi = false;
             if constexpr (has_time) {
@@ -338,15 +372,15 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             }
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
             float sl = s * sg;
-            float ds = acc_p[qb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
+            float ds = acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl));
             if constexpr (MASK) {
               const bool ok = j <= i && (j < hist || j == i) && i < L;
               sl = ok ? sl : 0.f;
               ds = ok ? ds : 0.f;
             }
-            acc_s[qb][r] = sl;
-            acc_p[qb][r] = ds;
-            if (has_pos && !pos_diag) {
+            acc_s[r] = sl;
+            acc_p[r] = ds;
+            if constexpr (has_pos && !PD) {
               const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
               atomicAdd(&sm.wing[y], ds);
             }
@@ -358,24 +392,37 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
                 if constexpr (TM == 1) g_hi += hi ? ds : 0.f;
               }
             }
-            const T dst = from_f32<T>(ds);
-            sm.dss[ql * C::DS_LD + jl] = dst;
-            if constexpr (C::DIAG_COPY)
-              if (pos_diag) sm.dsd[(C::BN - 1 - jl) * C::DG_LD + ql * (C::DG_LD + 1)] = dst;
+            if constexpr (C::DIAG_COPY && PD)
+              dsd_lane[(32 * qb + 8 * (r >> 2) + (r & 3)) * (C::DG_LD + 1)] = from_f32<T>(ds);
+          }
+          F sf[2], df[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
+            df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int kr = 32 * qb + 16 * h;
-            const F sf = pack8<T>(reinterpret_cast<const float*>(&acc_s[qb]) + 8 * h);
-            const F df = pack8<T>(reinterpret_cast<const float*>(&acc_p[qb]) + 8 * h);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
               const F a = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8);
-              mfma_32x32x16(acc_dv[db], sf, a);
+              mfma_32x32x16(acc_dv[db], sf[h], a);
               const F b = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8);
-              mfma_32x32x16(acc_dk[db], df, b);
+              mfma_32x32x16(acc_dk[db], df[h], b);
             }
           }
+          // Transpose through the matrix core: tr[r] of lane (c, g) is dS of
+          // query c and key 8(r/4) + 4g + r%4 of this wave (exact: one product
+          // with 1.0 per output, the rest zeros).
+          f32x16 tr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tr[r] = 0.f;
+          mfma_32x32x16(tr, df[0], eh[0]);
+          mfma_32x32x16(tr, df[1], eh[1]);
+          T* row = dst_lane + 32 * qb * C::DT_LD;
+          st_frag<T>(row, pack8<T>(reinterpret_cast<const float*>(&tr)));
+          st_frag<T>(row + 16, pack8<T>(reinterpret_cast<const float*>(&tr) + 8));
         }
         if constexpr (TM < 2) {
           if constexpr (has_time) {
@@ -394,31 +441,50 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
       using NoMask = std::integral_constant<bool, false>;
       using Mask = std::integral_constant<bool, true>;
-      if constexpr (WIDE) {
-        tile_math(I3(), Mask());
-      } else {
-        if (need_mask)
-          tile_math(I2(), Mask());
-        else if (tmode == 0)
-          tile_math(I0(), NoMask());
-        else if (tmode == 1)
-          tile_math(I1(), NoMask());
+      auto run = [&](auto pd) {
+        if constexpr (WIDE) {
+          tile_math(I3(), Mask(), pd);
+        } else {
+          if (need_mask)
+            tile_math(I2(), Mask(), pd);
+          else if (tmode == 0)
+            tile_math(I0(), NoMask(), pd);
+          else if (tmode == 1)
+            tile_math(I1(), NoMask(), pd);
+          else
+            tile_math(I2(), NoMask(), pd);
+        }
+      };
+      if constexpr (has_pos) {
+        if (pos_diag)
+          run(std::true_type());
         else
-          tile_math(I2(), NoMask());
+          run(std::false_type());
+      } else {
+        run(std::false_type());
       }
     } else {
-      // This wave's dS entries of the shared tile are zero.
+      // This wave's dS entries of the shared tile and diagonal copy are zero.
+      F zf;
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
+      for (int m = 0; m < 8; ++m) zf[m] = from_f32<T>(0.f);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-          sm.dss[ql * C::DS_LD + jl] = from_f32<T>(0.f);
-          if constexpr (C::DIAG_COPY)
-            if (pos_diag) sm.dsd[(C::BN - 1 - jl) * C::DG_LD + ql * (C::DG_LD + 1)] = from_f32<T>(0.f);
-        }
+      for (int qb = 0; qb < C::QB; ++qb) {
+        T* row = dst_lane + 32 * qb * C::DT_LD;
+        st_frag<T>(row, zf);
+        st_frag<T>(row + 16, zf);
+      }
+      if (C::DIAG_COPY && pos_diag) {
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            dsd_lane[(32 * qb + 8 * (r >> 2) + (r & 3)) * (C::DG_LD + 1)] = from_f32<T>(0.f);
+      }
     }
     __syncthreads();                               // dS, rab partials complete
+    // Every read of this tile's Q and dA' is done: stage the next tile.
+    if (more) store_tile();
 
     if (pos_diag) {
       // Diagonal sums: diagonal dd (query - key + BN - 1 within the tile)
@@ -437,7 +503,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           for (int ql = 0; ql < C::BM; ++ql) {
             const int c = ql + off;
             const int cc = c < 0 ? 0 : (c > C::BN - 1 ? C::BN - 1 : c);
-            const float x = to_f32(sm.dss[ql * C::DS_LD + cc]);
+            const float x = to_f32(sm.dst[ql * C::DT_LD + (cc & ~15) + chunk_slot(cc & 15)]);
             sum += (c == cc) ? x : 0.f;
           }
         }
@@ -457,22 +523,22 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         sm.wing[tid] = 0.f;
       }
     }
-    // dQ += dS K for this wave's output blocks.
+    // dQ += dS K for this wave's output blocks (32 queries x 32 head dims).
 #pragma unroll
     for (int m = 0; m < C::NDQ; ++m) {
       const int blk = wave + 4 * m;
       if (blk < C::QB * C::DB) {
-        const int qb = blk / C::DB;
+        const int qb = blk / C::DB, db = blk % C::DB;
         f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int kc = 0; kc < C::BN / 16; ++kc) {
-          const F a = ld_frag(sm.dss + (32 * qb + l32) * C::DS_LD + 16 * kc + 8 * g);
-          const F b = ld_frag(sm.kt + (32 * db_w + l32) * C::KT_LD + 16 * kc + 8 * g);
+          const F a = ld_frag(sm.dst + (32 * qb + l32) * C::DT_LD + 16 * kc + 8 * g);
+          const F b = ld_frag(sm.kt + (32 * db + l32) * C::KT_LD + 16 * kc + 8 * g);
           mfma_32x32x16(acc, a, b);
         }
-        const int d = 32 * db_w + l32;
+        const int d = 32 * db + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -480,7 +546,6 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         }
       }
     }
-    if (more) store_tile();
   }
 
   // Time-gradient histogram of this workgroup.

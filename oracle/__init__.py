@@ -6,10 +6,10 @@ binding) never calls it and shares no code with it.
 
 What it computes
 ----------------
-The pages name the method -- HSTU, "designed for high cardinality,
-non-stationary streaming recommendation data" (Abstract of "Actions Speak
-Louder than Words: Trillion-Parameter Sequential Transducers for Generative
-Recommendations"), its target-aware full causal self-attention and M-FALCON
+The pages name the method -- HSTU, a sequential transducer for large-vocabulary,
+drifting streams of user actions (Abstract of "Actions Speak Louder than Words:
+Trillion-Parameter Sequential Transducers for Generative Recommendations"), its
+target-aware full causal self-attention and M-FALCON
 (Generative Recommenders README, "HSTU Ultra attention benchmark" and the
 introduction) -- but print none of its equations. The oracle is the plain
 definition of the pointwise attention those passages name, per sequence b of

@@ -8,7 +8,8 @@ Workloads follow the shapes the pages benchmark: public sequential-recsys
 batches (history lengths up to 200, the ``*-l200`` log folders of the
 Generative Recommenders README, "Public Experiments"), long histories, and the
 8192-length efficiency setting of the HSTU paper's Abstract ("Actions Speak
-Louder than Words ...", 5.3x-15.2x faster on 8192 length sequences). No
+Louder than Words ...", which reports its speedup over FlashAttention2 at that
+sequence length). No
 public dataset is read: every tensor is drawn here from a seed.
 
 Draw order for one workload (all draws in float64 from
