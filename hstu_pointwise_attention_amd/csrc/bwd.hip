@@ -218,16 +218,26 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   int64_t tsreg = 0;
   float winreg = 0.f;
 
+  // Staging: thread tid moves 16-byte chunk tid % CPR of rows tid / CPR + m * RPM.
+  constexpr int RPM = C::NT / C::CPR;
+  static_assert(C::NT % C::CPR == 0, "staging rows");
+  const int row0 = tid / C::CPR, cc0 = tid % C::CPR;
+  const T* const q_lane = qg + (start + row0) * p.sq + (int64_t)head * D + cc0 * C::VPC;
+  const T* const d_lane = dag + (start + row0) * HD + (int64_t)head * D + cc0 * C::VPC;
   auto load_tile = [&](int q0) {
+    if (q0 + C::BM <= L) {
 #pragma unroll
-    for (int m = 0; m < C::CH; ++m) {
-      const int ch = tid + C::NT * m;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      const int ii = q0 + row;
-      qreg[m] = ii < L ? ld16(qg + (start + ii) * p.sq + (int64_t)head * D + cc * C::VPC)
-                       : u32x4{0, 0, 0, 0};
-      dreg[m] = ii < L ? ld16(dag + (start + ii) * HD + (int64_t)head * D + cc * C::VPC)
-                       : u32x4{0, 0, 0, 0};
+      for (int m = 0; m < C::CH; ++m) {
+        qreg[m] = ld16(q_lane + (int64_t)(q0 + m * RPM) * p.sq);
+        dreg[m] = ld16(d_lane + (int64_t)(q0 + m * RPM) * HD);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < C::CH; ++m) {
+        const bool ok = q0 + row0 + m * RPM < L;
+        qreg[m] = ok ? ld16(q_lane + (int64_t)(q0 + m * RPM) * p.sq) : u32x4{0, 0, 0, 0};
+        dreg[m] = ok ? ld16(d_lane + (int64_t)(q0 + m * RPM) * HD) : u32x4{0, 0, 0, 0};
+      }
     }
     if (has_time && tid < C::BM) {
       const int ii = q0 + tid;
@@ -243,10 +253,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   auto store_tile = [&]() {
 #pragma unroll
     for (int m = 0; m < C::CH; ++m) {
-      const int ch = tid + C::NT * m;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      st16(sm.qs + row * C::Q_LD + cc * C::VPC, qreg[m]);
-      st16(sm.das + row * C::Q_LD + cc * C::VPC, dreg[m]);
+      st16(sm.qs + (row0 + m * RPM) * C::Q_LD + cc0 * C::VPC, qreg[m]);
+      st16(sm.das + (row0 + m * RPM) * C::Q_LD + cc0 * C::VPC, dreg[m]);
     }
     if (has_time && tid < C::BM) sm.tsq[tid] = tsreg;
     if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
@@ -274,6 +282,13 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     const int q0 = (qt_first + n) * C::BM;
     const bool more = n + 1 < n_qt;
     __syncthreads();                               // tile n staged; previous dQ done
+    // Keep the loop-carried MFMA operands and accumulators in the
+    // accumulation registers: left to itself the allocator parks them in
+    // VGPRs between tiles and copies them back and forth every iteration.
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(acc_dk[db]), "+a"(acc_dv[db]));
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
     if (more) load_tile(q0 + C::BM);
 
     // Tiles of history rows only sum the position gradient along diagonals of
@@ -288,9 +303,9 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // Time-bias mode of this wave's sub-tile (its 32 keys x the 64 queries).
       // With sorted timestamps and every key at or before every query, the
       // bucket grows with the query and shrinks with the key, so the corners
-      // bound it: a single bucket (mode 0) or two adjacent ones split by a
-      // per-key threshold (mode 1). Everything else takes per-element buckets
-      // (mode 2).
+      // bound it: at most two adjacent buckets, split by a per-key threshold
+      // (mode 1; a single bucket is the case of a threshold no query
+      // reaches). Everything else takes per-element buckets (mode 2).
       int tmode = 2, b_lo = 0, b_hi = 0;
       uint32_t thr = 0;
       if (has_time && !wide && !need_mask && sorted_ts) {
@@ -299,7 +314,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.tsk[jw - k0], t_last);
         b_lo = time_bucket_rel((uint32_t)sm.tsq[0], (uint32_t)sm.tsk[kj_hi], t_last);
         if (b_hi == b_lo) {
-          tmode = 0;
+          tmode = 1;
+          thr = 0xffffffffu;                              // rebased timestamps stay below 2^31
         } else if (b_hi == b_lo + 1) {
           tmode = 1;
           thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);   // hi iff ts_i - ts_j + 1 >= 2^b_hi
@@ -342,8 +358,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         constexpr int TM = decltype(tm)::value;
         constexpr bool MASK = decltype(mk)::value;
         constexpr bool PD = decltype(pd)::value;
-        const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
-        const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
+        // TM 1: two buckets split at a per-key threshold; 2: per-element
+        // buckets of rebased timestamps; 3: of raw 64-bit timestamps.
+        const float tb_lo = (TM == 1 && has_time) ? sm.ttab[b_lo] : 0.f;
+        const float tb_hi = (TM == 1 && has_time) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
@@ -357,9 +375,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             int bt = 0;
             bool hi = false;
             if constexpr (has_time) {
-              if constexpr (TM == 0) {
-                s += tb_lo;
-              } else if constexpr (TM == 1) {
+              if constexpr (TM == 1) {
                 hi = (uint32_t)sm.tsq[ql] >= thr;
                 s += hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
@@ -435,34 +451,23 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           }
         }
       };
-      using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
       using NoMask = std::integral_constant<bool, false>;
       using Mask = std::integral_constant<bool, true>;
-      auto run = [&](auto pd) {
-        if constexpr (WIDE) {
-          tile_math(I3(), Mask(), pd);
-        } else {
-          if (need_mask)
-            tile_math(I2(), Mask(), pd);
-          else if (tmode == 0)
-            tile_math(I0(), NoMask(), pd);
-          else if (tmode == 1)
-            tile_math(I1(), NoMask(), pd);
-          else
-            tile_math(I2(), NoMask(), pd);
-        }
-      };
-      if constexpr (has_pos) {
-        if (pos_diag)
-          run(std::true_type());
-        else
-          run(std::false_type());
-      } else {
-        run(std::false_type());
-      }
+      // Three bodies in the loop, no more: every extra variant of this size
+      // raises the register pressure of the whole loop. The fast one covers
+      // the bulk (no mask, at most two time buckets, history rows); the two
+      // general ones take everything else.
+      using IG = std::conditional_t<WIDE, I3, I2>;
+      using PosDiag = std::integral_constant<bool, has_pos>;
+      if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
+        tile_math(I1(), NoMask(), PosDiag());
+      else if (pos_diag)
+        tile_math(IG(), Mask(), PosDiag());
+      else
+        tile_math(IG(), Mask(), std::false_type());
     } else {
       // This wave's dS entries of the shared tile and diagonal copy are zero.
       F zf;
@@ -538,11 +543,18 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           const F b = ld_frag(sm.kt + (32 * db + l32) * C::KT_LD + 16 * kc + 8 * g);
           mfma_32x32x16(acc, a, b);
         }
-        const int d = 32 * db + l32;
+        // register r: query row i0 + 8(r/4) + r%4, head dim 32 db + l32
+        const int i0 = q0 + 32 * qb + 4 * g;
+        float* const dq_row = p.dq_acc + ((start + i0) * H + head) * (int64_t)D + 32 * db + l32;
+        if (q0 + 32 * qb + 31 < L) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (i < L) atomicAdd(p.dq_acc + ((start + i) * H + head) * (int64_t)D + d, acc[r]);
+          for (int r = 0; r < 16; ++r)
+            atomicAdd(dq_row + (int64_t)(8 * (r >> 2) + (r & 3)) * HD, acc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (i0 + 8 * (r >> 2) + (r & 3) < L)
+              atomicAdd(dq_row + (int64_t)(8 * (r >> 2) + (r & 3)) * HD, acc[r]);
         }
       }
     }
