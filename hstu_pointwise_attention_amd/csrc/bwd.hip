@@ -27,6 +27,10 @@
 // window instead.
 #include "internal.h"
 
+#ifndef BWD_PIPE
+#define BWD_PIPE true
+#endif
+
 namespace hstu {
 
 namespace {
@@ -69,6 +73,14 @@ struct BwdCfg {
   static constexpr int KUPT = (KUNITS + NT - 1) / NT;
   static constexpr int NDQ = (QB * DB + 3) / 4;  // dQ output blocks per wave (max)
   static constexpr int MAX_TIME = 1024;
+  static constexpr int MAX_QT = 2048;            // tiles whose fast/general flag is kept in LDS
+  // Time-gradient histogram: with up to HREP_NT buckets, HREP copies (lane
+  // l adds into copy l % HREP, HREP_LD floats apart so a bucket's copies sit
+  // in different banks) keep the per-element adds of one instruction from
+  // piling onto one address; larger tables use a single copy.
+  static constexpr int HREP = 16, HREP_NT = 128, HREP_LD = HREP_NT + 1;
+  static constexpr int THIST = HREP * HREP_LD > MAX_TIME ? HREP * HREP_LD : MAX_TIME;
+  static constexpr bool PIPE = BWD_PIPE;
   static_assert(BM * CPR % NT == 0, "staging");
 };
 
@@ -87,7 +99,8 @@ struct BwdSmem {
   T dsd[C::DG_ROWS * C::DG_LD];
   int64_t tsk[C::BN];            // timestamps of the key block
   float ttab[C::MAX_TIME];
-  float thist[C::MAX_TIME];
+  float thist[C::THIST];
+  uint8_t tflag[C::MAX_QT];      // 1: the tile takes the fast body (see tile_fast)
 };
 
 // Key order inside a 16-key chunk of the dS tile and K^T: slot s holds key
@@ -111,7 +124,10 @@ __device__ __forceinline__ void st_frag(T* p, const typename Frag<T>::type& f) {
   *reinterpret_cast<typename Frag<T>::type*>(p) = f;
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+// PART 0: every tile of the key block; 1: only the tiles the fast body does
+// not take, dK / dV partials to the workspace; 2: only the fast tiles,
+// starting from those partials.
+template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
@@ -145,10 +161,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
   const T* __restrict__ dag = reinterpret_cast<const T*>(p.d_a);
 
-  for (int x = tid; x < p.n_time_buckets; x += C::NT) {
-    sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
-    sm.thist[x] = 0.f;
-  }
+  for (int x = tid; x < p.n_time_buckets; x += C::NT) sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+  for (int x = tid; x < C::THIST; x += C::NT) sm.thist[x] = 0.f;
+  const bool hrep = p.n_time_buckets <= C::HREP_NT;
+  float* const thist_lane = sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
   for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
   // Diagonal-copy entries that no element maps to stay zero for the whole loop.
   if (C::DIAG_COPY && has_pos)
@@ -260,14 +276,74 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
   };
 
+  // Partial dK / dV of this lane: register r of block db is key
+  // jw + 8(r/4) + 4g + r%4, head dim 32 db + l32.
+  const int64_t THD = p.T * HD;
+  auto part_off = [&](int db, int r) {
+    return ((start + jw + 8 * (r >> 2) + 4 * g + (r & 3)) * H + head) * (int64_t)D + 32 * db + l32;
+  };
   f32x16 acc_dk[C::DB], acc_dv[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      acc_dk[db][r] = 0.f;
-      acc_dv[db][r] = 0.f;
+      const bool in = PART == 2 && jw + 8 * (r >> 2) + 4 * g + (r & 3) < L;
+      acc_dk[db][r] = in ? p.dkv_part[part_off(db, r)] : 0.f;
+      acc_dv[db][r] = in ? p.dkv_part[THD + part_off(db, r)] : 0.f;
     }
+
+  // Wave w of tile n takes the fast body when none of its pairs is masked,
+  // the rows it sees are history rows (or there is no position bias) and,
+  // with sorted timestamps, its time buckets span at most two adjacent
+  // values. Every wave evaluates the test for all four, from global memory,
+  // so both parts of a split launch agree on each (tile, wave).
+  auto wave_skip = [&](int n, int w) -> bool {
+    const int q0 = (qt_first + n) * C::BM, jv = k0 + 32 * w;
+    return jv >= L || q0 + C::BM - 1 < jv || (jv >= hist && (q0 > jv + 31 || q0 + C::BM - 1 < jv));
+  };
+  auto wave_fast = [&](int n, int w) -> bool {
+    if (WIDE) return false;
+    const int q0 = (qt_first + n) * C::BM, jv = k0 + 32 * w;
+    if (q0 < jv + 31 || jv + 31 >= hist || q0 + C::BM - 1 >= (has_pos ? hist : L)) return false;
+    if (has_time) {
+      if (!sorted_ts) return false;
+      const uint32_t* tr = p.ts_rel + start;
+      const int bh = time_bucket_rel(tr[q0 + C::BM - 1], tr[jv], t_last);
+      const int bl = time_bucket_rel(tr[q0], tr[jv + 31], t_last);
+      if (bh > bl + 1) return false;
+    }
+    return true;
+  };
+  // Bit w: wave w takes the fast body in tile n.
+  auto fast_mask = [&](int n) -> int {
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m |= wave_fast(n, w) ? 1 << w : 0;
+    return m;
+  };
+  if (PART != 0) {
+    for (int t = tid; t < min(n_qt, C::MAX_QT); t += C::NT) sm.tflag[t] = (uint8_t)fast_mask(t);
+    __syncthreads();
+  }
+  auto tile_mask = [&](int n) -> int { return n < C::MAX_QT ? sm.tflag[n] : fast_mask(n); };
+  // Part 2 visits the tiles with a fast wave, part 1 those with a wave that
+  // computes but is not fast.
+  auto selected = [&](int n) -> bool {
+    if constexpr (PART == 0) {
+      return true;
+    } else {
+      const int m = tile_mask(n);
+      if constexpr (PART == 2) return m != 0;
+      bool any = false;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) any |= !((m >> w) & 1) && !wave_skip(n, w);
+      return any;
+    }
+  };
+  auto next_sel = [&](int n) {
+    while (n < n_qt && !selected(n)) ++n;
+    return n;
+  };
 
   // Per-lane bases: this lane's 16-byte slots of the dS tile (query row
   // l32 of a block, keys of its wave) and of the diagonal copy.
@@ -275,12 +351,20 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   T* const dsd_lane =
       C::DIAG_COPY ? sm.dsd + (C::BN - 1 - jl) * C::DG_LD + 4 * g * (C::DG_LD + 1) : sm.dsd;
 
-  load_tile(qt_first * C::BM);
-  store_tile();
+  int n = next_sel(0);
+  if (n < n_qt) {
+    load_tile((qt_first + n) * C::BM);
+    store_tile();
+  }
+  // Nothing loaded before the loop is still in flight when it starts: the
+  // memory counters inside the loop then only ever wait for the loop's own
+  // loads, never behind the dQ atomics of the previous tile.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  for (int n = 0; n < n_qt; ++n) {
+  while (n < n_qt) {
     const int q0 = (qt_first + n) * C::BM;
-    const bool more = n + 1 < n_qt;
+    const int n_next = next_sel(n + 1);
+    const bool more = n_next < n_qt;
     __syncthreads();                               // tile n staged; previous dQ done
     // Keep the loop-carried MFMA operands and accumulators in the
     // accumulation registers: left to itself the allocator parks them in
@@ -289,7 +373,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(acc_dk[db]), "+a"(acc_dv[db]));
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
-    if (more) load_tile(q0 + C::BM);
+    asm volatile("" : "+a"(eh[0]), "+a"(eh[1]));
+    if (more) load_tile((qt_first + n_next) * C::BM);
 
     // Tiles of history rows only sum the position gradient along diagonals of
     // the dS tile after it is complete; tiles with candidate rows (whose
@@ -297,7 +382,11 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     const bool pos_diag = has_pos && q0 + C::BM - 1 < hist;
     const bool skip = jw >= L || q0 + C::BM - 1 < jw ||
                       (jw >= hist && (q0 > jw + 31 || q0 + C::BM - 1 < jw));
-    if (!skip) {
+    // In a split launch each (tile, wave) is computed by one part only; in
+    // the other it contributes zeros like a wave without pairs.
+    bool mine = true;
+    if constexpr (PART != 0) mine = (((tile_mask(n) >> wave) & 1) != 0) == (PART == 2);
+    if (!skip && mine) {
       const bool need_mask = !(q0 >= jw + 31 && jw + 31 < hist && q0 + C::BM - 1 < L);
       const int p_min = min(q0, hist);
       // Time-bias mode of this wave's sub-tile (its 32 keys x the 64 queries).
@@ -363,10 +452,28 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         const float tb_lo = (TM == 1 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1 && has_time) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
+        // PIPE: the next block's S and dP MFMAs are issued before this
+        // block's elementwise work so the two overlap.
+        f32x16 acc_sb[C::QB], acc_pb[C::QB];
+        constexpr bool PIPE = C::PIPE && PART != 1;   // the general part keeps registers instead
+        if constexpr (PIPE) sp_block(pd, 0, acc_sb[0], acc_pb[0]);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
-          f32x16 acc_s, acc_p;
-          sp_block(pd, qb, acc_s, acc_p);
+          if constexpr (PIPE) {
+            if (qb + 1 < C::QB) sp_block(pd, qb + 1, acc_sb[qb + 1], acc_pb[qb + 1]);
+          } else {
+            sp_block(pd, qb, acc_sb[qb], acc_pb[qb]);
+          }
+          f32x16& acc_s = acc_sb[qb];
+          f32x16& acc_p = acc_pb[qb];
+          // B operands of the first 16-query chunk's dV / dK products, read
+          // now so the elementwise work below covers the LDS latency.
+          F bv0[C::DB], bk0[C::DB];
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+            bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+          }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -402,7 +509,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             }
             if constexpr (has_time) {
               if constexpr (TM >= 2) {
-                atomicAdd(&sm.thist[bt], ds);
+                atomicAdd(thist_lane + bt, ds);
               } else {
                 g_all += ds;
                 if constexpr (TM == 1) g_hi += hi ? ds : 0.f;
@@ -417,16 +524,22 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
             df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
           }
+          // second chunk's operands in flight while the first chunk's MFMAs run
+          F bv1[C::DB], bk1[C::DB];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int kr = 32 * qb + 16 * h;
+          for (int db = 0; db < C::DB; ++db) {
+            bv1[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+            bk1[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+          }
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              const F a = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8);
-              mfma_32x32x16(acc_dv[db], sf[h], a);
-              const F b = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8);
-              mfma_32x32x16(acc_dk[db], df[h], b);
-            }
+          for (int db = 0; db < C::DB; ++db) {
+            mfma_32x32x16(acc_dv[db], sf[0], bv0[db]);
+            mfma_32x32x16(acc_dk[db], df[0], bk0[db]);
+          }
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
+            mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
           }
           // Transpose through the matrix core: tr[r] of lane (c, g) is dS of
           // query c and key 8(r/4) + 4g + r%4 of this wave (exact: one product
@@ -456,18 +569,43 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
       using NoMask = std::integral_constant<bool, false>;
       using Mask = std::integral_constant<bool, true>;
-      // Three bodies in the loop, no more: every extra variant of this size
-      // raises the register pressure of the whole loop. The fast one covers
-      // the bulk (no mask, at most two time buckets, history rows); the two
-      // general ones take everything else.
+      // Every body of this size in the loop raises the register pressure of
+      // the whole loop, so a split launch compiles one per kernel: the fast
+      // body (no mask, at most two time buckets, history rows, position
+      // gradient through the diagonal copy) in part 2, the general one
+      // (masks, per-element buckets, position gradient through the window)
+      // in part 1; part 0 holds both.
       using IG = std::conditional_t<WIDE, I3, I2>;
       using PosDiag = std::integral_constant<bool, has_pos>;
-      if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
-        tile_math(I1(), NoMask(), PosDiag());
-      else if (pos_diag)
-        tile_math(IG(), Mask(), PosDiag());
-      else
+      auto general = [&]() {
+        // Without the diagonal copy (fp32) the diagonal sums of a history
+        // tile read the dS tile itself, which holds this wave's entries.
+        if constexpr (!C::DIAG_COPY && has_pos) {
+          if (pos_diag) {
+            tile_math(IG(), Mask(), PosDiag());
+            return;
+          }
+        }
         tile_math(IG(), Mask(), std::false_type());
+        // the diagonal sums of a history tile read this wave's copy entries too
+        if (PART == 0 && C::DIAG_COPY && pos_diag) {
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              dsd_lane[(32 * qb + 8 * (r >> 2) + (r & 3)) * (C::DG_LD + 1)] = from_f32<T>(0.f);
+        }
+      };
+      if constexpr (PART == 2) {
+        tile_math(I1(), NoMask(), PosDiag());
+      } else if constexpr (PART == 1) {
+        general();
+      } else {
+        if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
+          tile_math(I1(), NoMask(), PosDiag());
+        else
+          general();
+      }
     } else {
       // This wave's dS entries of the shared tile and diagonal copy are zero.
       F zf;
@@ -491,7 +629,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     // Every read of this tile's Q and dA' is done: stage the next tile.
     if (more) store_tile();
 
-    if (pos_diag) {
+    if (pos_diag && PART != 1) {
       // Diagonal sums: diagonal dd (query - key + BN - 1 within the tile)
       // gathers the elements whose position bucket is that of offset
       // k0 - q0 + (BN - 1) - dd.
@@ -517,8 +655,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
                         pos_bucket(k0 - q0 + (C::BN - 1) - dd, p.max_len),
                     sum);
       }
-    } else if (has_pos && tid < C::WIN) {
-      // Flush the position-gradient window of this tile.
+    }
+    if (has_pos && PART != 2 && tid < C::WIN) {
+      // Flush the position-gradient window of this tile (the general body's
+      // adds; entries it did not touch are zero).
       const float gsum = sm.wing[tid];
       if (gsum != 0.f) {
         const int p_min = min(q0, hist);
@@ -558,34 +698,41 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         }
       }
     }
+    n = n_next;
   }
 
   // Time-gradient histogram of this workgroup.
   if constexpr (has_time) {
     __syncthreads();
     for (int x = tid; x < p.n_time_buckets; x += C::NT) {
-      const float gsum = sm.thist[x];
+      float gsum = 0.f;
+      for (int c = 0; c < (hrep ? C::HREP : 1); ++c) gsum += sm.thist[c * C::HREP_LD + x];
       if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
     }
   }
 
-  // dK, dV of this lane's keys: register r holds key 8(r/4) + 4g + r%4 of the
-  // wave, column d = 32 db + l32.
+  // dK, dV of this lane's keys (partials in fp32 for part 1): register r
+  // holds key 8(r/4) + 4g + r%4 of the wave, column d = 32 db + l32.
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jj = jw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (jj < L) {
-        const int64_t o = ((start + jj) * H + head) * (int64_t)D + 32 * db + l32;
-        reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
-        reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
+        const int64_t o = part_off(db, r);
+        if constexpr (PART == 1) {
+          p.dkv_part[o] = acc_dk[db][r];
+          p.dkv_part[THD + o] = acc_dv[db][r];
+        } else {
+          reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
+          reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
+        }
       }
     }
   }
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void hstu_bwd_kernel(AttnParams p) {
   __shared__ BwdSmem<T, D> sm;
@@ -595,7 +742,21 @@ void hstu_bwd_kernel(AttnParams p) {
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
   if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  bwd_body<T, D, WIDE, POS, TIME>(p, sm, wi, si, head);
+  bwd_body<T, D, WIDE, POS, TIME, PART>(p, sm, wi, si, head);
+}
+
+template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
+void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
+  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME, PART>), g, dim3(256), 0, s, p);
+}
+
+template <typename T, int D, bool WIDE, int PART>
+void launch_rab(const AttnParams& p, dim3 g, hipStream_t s) {
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
+  if (pos && time) launch_one<T, D, WIDE, true, true, PART>(p, g, s);
+  else if (pos) launch_one<T, D, WIDE, true, false, PART>(p, g, s);
+  else if (time) launch_one<T, D, WIDE, false, true, PART>(p, g, s);
+  else launch_one<T, D, WIDE, false, false, PART>(p, g, s);
 }
 
 }  // namespace
@@ -604,19 +765,22 @@ template <typename T, int D>
 hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
-  const dim3 g((unsigned)grid), b(256);
-  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
+  const dim3 g((unsigned)grid);
+  constexpr bool split = bwd_split_shape((int)sizeof(T), D);
+  if (split != bwd_split(p)) return hipErrorInvalidValue;   // workspace carved for the other form
   prof_before(kKBwd, s);
-  if (pos && time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, true, true>), g, b, 0, s, p);
-  else if (pos) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, true, false>), g, b, 0, s, p);
-  else if (time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, false, true>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, false, false>), g, b, 0, s, p);
-  prof_after(kKBwd, s);
-  hipError_t e = hipGetLastError();
+  if constexpr (split) {
+    launch_rab<T, D, false, 1>(p, g, s);
+    launch_rab<T, D, false, 2>(p, g, s);
+  } else {
+    launch_rab<T, D, false, 0>(p, g, s);
+  }
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (e != hipSuccess || !time) return e;
-  if (pos) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, true, true>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, false, true>), g, b, 0, s, p);
+  if (p.rab_time != nullptr) {
+    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true, 0>(p, g, s);
+    else launch_one<T, D, true, false, true, 0>(p, g, s);
+  }
+  prof_after(kKBwd, s);
   return hipGetLastError();
 }
 

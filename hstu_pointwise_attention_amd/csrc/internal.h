@@ -38,6 +38,7 @@ struct AttnParams {
   int32_t* n_items;                  // [1]
   int32_t* sched_scratch;            // schedule kernel scratch
   float* dq_acc;                     // [T, H, D] fp32 (backward)
+  float* dkv_part;                   // [2, T, H, D] fp32 partial dK, dV (split backward)
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
 };
@@ -45,6 +46,11 @@ struct AttnParams {
 // Workspace layout: returns total bytes and fills the pointers in p (when
 // base != nullptr).
 size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
+
+// bf16 at head dim 128 runs the backward as two launches (general tiles,
+// then fast tiles) that meet through fp32 dK / dV partials.
+constexpr bool bwd_split_shape(int elem_bytes, int D) { return elem_bytes == 2 && D == 128; }
+inline bool bwd_split(const AttnParams& p) { return p.dkv_part != nullptr; }
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
