@@ -153,10 +153,31 @@ hipError_t dispatch_bwd<bf16>(const AttnParams& p, hipStream_t s) {
 }
 
 template <typename T>
+hipError_t dispatch_dq(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_dq<T, 32>(p, s);
+    case 64: return launch_dq<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <>
+hipError_t dispatch_dq<bf16>(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_dq<bf16, 32>(p, s);
+    case 64: return launch_dq<bf16, 64>(p, s);
+    case 128: return launch_dq<bf16, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// dA' and dU, then dK / dV / d_rab per key block, then dQ per query block
+// (its own schedule, the forward's).
+template <typename T>
 hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
   hipError_t e = launch_bwd_pre<T>(p, s);
   if (e == hipSuccess) e = dispatch_bwd<T>(p, s);
-  if (e == hipSuccess) e = launch_bwd_post<T>(p, s);
+  if (e == hipSuccess) e = launch_schedule(p, 0, s);
+  if (e == hipSuccess) e = dispatch_dq<T>(p, s);
   return e;
 }
 
@@ -262,7 +283,6 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   if (e == hipSuccess && p.T > 0 && p.B > 0) {
     e = launch_prep(p, s);
     if (e == hipSuccess) e = launch_schedule(p, 1, s);
-    if (e == hipSuccess) e = launch_fill_f32(p.dq_acc, p.T * p.H * p.D, 0.f, s);
     if (e == hipSuccess)
       e = desc->dtype == HSTU_DTYPE_BF16 ? run_bwd_main<bf16>(p, s) : run_bwd_main<float>(p, s);
   }

@@ -11,13 +11,10 @@
 //   dS   = dP * s'  (0 where masked)
 //   dV  += s^T dA',  dK += dS^T Q   (Q, dA' fragments by LDS transpose reads)
 // The accumulators hold S and dP with keys on lanes, which is the operand
-// layout dV and dK need. dQ = dS K needs queries on lanes instead: each
-// wave's dS block goes through the matrix core once more against one-hot
-// operands (an exact transpose), lands in a shared LDS dS tile with two
-// 16-byte stores per lane, and after the tile the four waves compute dQ
-// blocks from it against K^T and add them into an fp32 workspace with
-// atomics. Keys inside each 16-key chunk of the dS tile and of K^T follow
-// the order the transposed accumulator delivers them in.
+// layout dV and dK need. dQ needs queries on lanes and a sum over all keys:
+// adding per-block partials with fp32 atomics costs more than recomputing
+// S and dP per query block, so dQ comes from a separate pass (the forward's
+// tiling, in fwd.hip) and this kernel computes dK, dV and the rab gradients.
 // The rab gradients are sums of dS over the pairs that read each table entry.
 // Time buckets: with sorted timestamps a wave's sub-tile below the diagonal
 // has one or two buckets, summed in registers; otherwise each element adds
@@ -57,21 +54,14 @@ struct BwdCfg {
   static constexpr int VPC = 16 / ES;
   static constexpr int CPR = D / VPC;
   static constexpr int Q_LD = BwdLd<T, D>::Q;    // row-major tiles [BM][D]
-  static constexpr int DT_LD = BN + VPC;         // dS tile [BM][BN]; rows 16 bytes apart in banks
-  static constexpr int KT_LD = BN + VPC;         // K^T of the key block [D][BN]
   static constexpr int NDIAG = BM + BN - 1;      // diagonals of a tile
-  // bf16: diagonal-major copy of dS, row dd = query - key + BN - 1 (so the
+  // Diagonal-major copy of dS, row dd = query - key + BN - 1 (so the
   // address of a lane's elements is a per-lane base plus constants), 64
   // queries (+8 padding: 16-byte aligned rows, at most 2-way write
-  // conflicts). fp32 sums the diagonals from the dS tile instead.
-  static constexpr bool DIAG_COPY = sizeof(T) == 2;
+  // conflicts).
   static constexpr int DG_LD = BM + 8;
-  static constexpr int DG_ROWS = DIAG_COPY ? NDIAG : 1;
   static constexpr int WIN = BN + BM;            // >= BN + BM - 1
   static constexpr int CH = BM * CPR / NT;       // 16-byte chunks per thread per tile
-  static constexpr int KUNITS = (BN / 2) * CPR;  // K^T staging units
-  static constexpr int KUPT = (KUNITS + NT - 1) / NT;
-  static constexpr int NDQ = (QB * DB + 3) / 4;  // dQ output blocks per wave (max)
   static constexpr int MAX_TIME = 1024;
   static constexpr int MAX_QT = 2048;            // tiles whose fast/general flag is kept in LDS
   // Time-gradient histogram: with up to HREP_NT buckets, HREP copies (lane
@@ -91,22 +81,15 @@ struct BwdSmem {
   using C = BwdCfg<T, D>;
   T qs[C::BM * C::Q_LD];
   T das[C::BM * C::Q_LD];
-  T dst[C::BM * C::DT_LD];       // dS of the tile, query rows, keys in chunk order
   float win[C::WIN];
   float wing[C::WIN];
   int64_t tsq[C::BM];
-  T kt[D * C::KT_LD];            // K^T of the key block, keys in chunk order
-  T dsd[C::DG_ROWS * C::DG_LD];
+  T dsd[C::NDIAG * C::DG_LD];
   int64_t tsk[C::BN];            // timestamps of the key block
   float ttab[C::MAX_TIME];
   float thist[C::THIST];
   uint8_t tflag[C::MAX_QT];      // 1: the tile takes the fast body (see tile_fast)
 };
-
-// Key order inside a 16-key chunk of the dS tile and K^T: slot s holds key
-// offset s with bits 2 and 3 swapped (the order in which a transposed 32x32
-// accumulator hands a lane its keys). The map is its own inverse.
-__device__ __forceinline__ int chunk_slot(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 __device__ __forceinline__ float sum8(const bf16x8& v) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
@@ -119,9 +102,8 @@ __device__ __forceinline__ float sum8(const bf16x8& v) {
   return s;
 }
 
-template <typename T>
-__device__ __forceinline__ void st_frag(T* p, const typename Frag<T>::type& f) {
-  *reinterpret_cast<typename Frag<T>::type*>(p) = f;
+__device__ __forceinline__ float sum8(const f32x8& v) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
 // PART 0: every tile of the key block; 1: only the tiles the fast body does
@@ -167,8 +149,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   float* const thist_lane = sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
   for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
   // Diagonal-copy entries that no element maps to stay zero for the whole loop.
-  if (C::DIAG_COPY && has_pos)
-    for (int x = tid; x < C::DG_ROWS * C::DG_LD; x += C::NT) sm.dsd[x] = from_f32<T>(0.f);
+  if (has_pos)
+    for (int x = tid; x < C::NDIAG * C::DG_LD; x += C::NT) sm.dsd[x] = from_f32<T>(0.f);
 
   // Resident K, V fragments of this lane's key (B operands of Q K^T, dA' V^T).
   F kf[C::KC], vf[C::KC];
@@ -188,41 +170,6 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   int64_t ts_j = 0;
   if (has_time && key_ok) ts_j = wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j];
   if constexpr (has_time) sm.tsk[jl] = ts_j;
-
-  // One-hot operands of the transpose: eh[h] is the 16 x 32 block whose
-  // slot 8g + m of column c is 1 iff c is query 16h + 8(m/4) + 4g + m%4 of
-  // the 32-query block (the query that slot holds in the dS operand).
-  F eh[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-      eh[h][m] = from_f32<T>(l32 == 16 * h + 8 * (m >> 2) + 4 * g + (m & 3) ? 1.f : 0.f);
-
-  // K^T of the whole key block into LDS, keys in chunk order: the dQ product
-  // reads lane (d, g)'s operand as 16 contiguous bytes at slot 8g of a chunk.
-#pragma unroll
-  for (int m = 0; m < C::KUPT; ++m) {
-    const int un = tid + C::NT * m;
-    if (un < C::KUNITS) {
-      const int pair = un / C::CPR, cc = un % C::CPR;
-      const int jj = k0 + 2 * pair;
-      const T* src = kg + (start + jj) * p.sk + (int64_t)head * D + cc * C::VPC;
-      const u32x4 r0 = jj < L ? ld16(src) : u32x4{0, 0, 0, 0};
-      const u32x4 r1 = jj + 1 < L ? ld16(src + p.sk) : u32x4{0, 0, 0, 0};
-      const T* a = reinterpret_cast<const T*>(&r0);
-      const T* b = reinterpret_cast<const T*>(&r1);
-      // keys 2*pair and 2*pair + 1 differ in bit 0 only, which the chunk
-      // order keeps: their slots are adjacent
-      const int slot = chunk_slot(2 * pair);
-#pragma unroll
-      for (int e = 0; e < C::VPC; ++e) {
-        T* dst = sm.kt + (cc * C::VPC + e) * C::KT_LD + slot;
-        dst[0] = a[e];
-        dst[1] = b[e];
-      }
-    }
-  }
 
   // Query tiles that can see this key block.
   const int qt_first = k0 / C::BM;
@@ -345,11 +292,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     return n;
   };
 
-  // Per-lane bases: this lane's 16-byte slots of the dS tile (query row
-  // l32 of a block, keys of its wave) and of the diagonal copy.
-  T* const dst_lane = sm.dst + l32 * C::DT_LD + 32 * wave + 8 * g;
-  T* const dsd_lane =
-      C::DIAG_COPY ? sm.dsd + (C::BN - 1 - jl) * C::DG_LD + 4 * g * (C::DG_LD + 1) : sm.dsd;
+  // Per-lane base of this lane's entries in the diagonal copy.
+  T* const dsd_lane = sm.dsd + (C::BN - 1 - jl) * C::DG_LD + 4 * g * (C::DG_LD + 1);
 
   int n = next_sel(0);
   if (n < n_qt) {
@@ -373,7 +317,6 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(acc_dk[db]), "+a"(acc_dv[db]));
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
-    asm volatile("" : "+a"(eh[0]), "+a"(eh[1]));
     if (more) load_tile((qt_first + n_next) * C::BM);
 
     // Tiles of history rows only sum the position gradient along diagonals of
@@ -452,6 +395,18 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         const float tb_lo = (TM == 1 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1 && has_time) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
+        // Per-element buckets: the gradient of the lane's four largest
+        // buckets in the tile (b_top - k, k < 4) is summed in registers and
+        // added once per tile; only elements below that window add into the
+        // LDS histogram one by one. With sorted timestamps the bucket grows
+        // with the query, so nearly all elements land in the window.
+        float gw[4] = {0.f, 0.f, 0.f, 0.f};
+        int b_top = 0;
+        if constexpr (has_time && TM >= 2) {
+          const int q_hi = min(q0 + C::BM - 1, L - 1) - q0;
+          b_top = TM == 2 ? time_bucket_rel((uint32_t)sm.tsq[q_hi], (uint32_t)ts_j, t_last)
+                          : time_bucket_wide(sm.tsq[q_hi], ts_j, t_last);
+        }
         // PIPE: the next block's S and dP MFMAs are issued before this
         // block's elementwise work so the two overlap.
         f32x16 acc_sb[C::QB], acc_pb[C::QB];
@@ -474,6 +429,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
             bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
           }
+          int bts[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -503,19 +459,35 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             }
             acc_s[r] = sl;
             acc_p[r] = ds;
-            if constexpr (has_pos && !PD) {
-              const int y = (C::BN - 1 - jl) + min(i, hist) - p_min;
-              atomicAdd(&sm.wing[y], ds);
+            bts[r] = bt;
+            if constexpr (TM == 1 && has_time) {
+              g_all += ds;
+              g_hi += hi ? ds : 0.f;
             }
-            if constexpr (has_time) {
-              if constexpr (TM >= 2) {
-                atomicAdd(thist_lane + bt, ds);
-              } else {
-                g_all += ds;
-                if constexpr (TM == 1) g_hi += hi ? ds : 0.f;
+          }
+          // Side effects after all the block's LDS reads: the compiler cannot
+          // move a table read above an LDS write it cannot disambiguate, so
+          // interleaving them would serialize the elements.
+          // The position gradient goes through the diagonal copy in history
+          // tiles (plain stores) and through window adds only in tiles with
+          // candidate rows; LDS float atomics cost far more than stores.
+          const bool to_copy = has_pos && (PD || pos_diag);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float ds = acc_p[r];
+            if constexpr (has_pos && !PD) {
+              if (!pos_diag) {
+                const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
+                atomicAdd(&sm.wing[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
               }
             }
-            if constexpr (C::DIAG_COPY && PD)
+            if constexpr (has_time && TM >= 2) {
+              const int k = b_top - bts[r];
+#pragma unroll
+              for (int w = 0; w < 4; ++w) gw[w] += k == w ? ds : 0.f;
+              if ((unsigned)k >= 4u && ds != 0.f) atomicAdd(thist_lane + bts[r], ds);
+            }
+            if (to_copy)
               dsd_lane[(32 * qb + 8 * (r >> 2) + (r & 3)) * (C::DG_LD + 1)] = from_f32<T>(ds);
           }
           F sf[2], df[2];
@@ -541,17 +513,11 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
             mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
           }
-          // Transpose through the matrix core: tr[r] of lane (c, g) is dS of
-          // query c and key 8(r/4) + 4g + r%4 of this wave (exact: one product
-          // with 1.0 per output, the rest zeros).
-          f32x16 tr;
+        }
+        if constexpr (has_time && TM >= 2) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tr[r] = 0.f;
-          mfma_32x32x16(tr, df[0], eh[0]);
-          mfma_32x32x16(tr, df[1], eh[1]);
-          T* row = dst_lane + 32 * qb * C::DT_LD;
-          st_frag<T>(row, pack8<T>(reinterpret_cast<const float*>(&tr)));
-          st_frag<T>(row + 16, pack8<T>(reinterpret_cast<const float*>(&tr) + 8));
+          for (int w = 0; w < 4; ++w)
+            if (gw[w] != 0.f) atomicAdd(thist_lane + (b_top - w), gw[w]);
         }
         if constexpr (TM < 2) {
           if constexpr (has_time) {
@@ -577,25 +543,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // in part 1; part 0 holds both.
       using IG = std::conditional_t<WIDE, I3, I2>;
       using PosDiag = std::integral_constant<bool, has_pos>;
-      auto general = [&]() {
-        // Without the diagonal copy (fp32) the diagonal sums of a history
-        // tile read the dS tile itself, which holds this wave's entries.
-        if constexpr (!C::DIAG_COPY && has_pos) {
-          if (pos_diag) {
-            tile_math(IG(), Mask(), PosDiag());
-            return;
-          }
-        }
-        tile_math(IG(), Mask(), std::false_type());
-        // the diagonal sums of a history tile read this wave's copy entries too
-        if (PART == 0 && C::DIAG_COPY && pos_diag) {
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              dsd_lane[(32 * qb + 8 * (r >> 2) + (r & 3)) * (C::DG_LD + 1)] = from_f32<T>(0.f);
-        }
-      };
+      auto general = [&]() { tile_math(IG(), Mask(), std::false_type()); };
       if constexpr (PART == 2) {
         tile_math(I1(), NoMask(), PosDiag());
       } else if constexpr (PART == 1) {
@@ -607,17 +555,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           general();
       }
     } else {
-      // This wave's dS entries of the shared tile and diagonal copy are zero.
-      F zf;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) zf[m] = from_f32<T>(0.f);
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-        T* row = dst_lane + 32 * qb * C::DT_LD;
-        st_frag<T>(row, zf);
-        st_frag<T>(row + 16, zf);
-      }
-      if (C::DIAG_COPY && pos_diag) {
+      // This wave's entries of the diagonal copy are zero.
+      if (pos_diag) {
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
@@ -629,36 +568,24 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     // Every read of this tile's Q and dA' is done: stage the next tile.
     if (more) store_tile();
 
-    if (pos_diag && PART != 1) {
+    if (pos_diag) {
       // Diagonal sums: diagonal dd (query - key + BN - 1 within the tile)
       // gathers the elements whose position bucket is that of offset
       // k0 - q0 + (BN - 1) - dd.
       if (tid < C::NDIAG) {
         const int dd = tid;
         float sum = 0.f;
-        if constexpr (C::DIAG_COPY) {
-          const T* row = sm.dsd + dd * C::DG_LD;
+        const T* row = sm.dsd + dd * C::DG_LD;
 #pragma unroll
-          for (int c = 0; c < C::BM / 8; ++c) sum += sum8(ld_frag(row + 8 * c));
-        } else {
-          const int off = (C::BN - 1) - dd;   // key - query
-#pragma unroll 16
-          for (int ql = 0; ql < C::BM; ++ql) {
-            const int c = ql + off;
-            const int cc = c < 0 ? 0 : (c > C::BN - 1 ? C::BN - 1 : c);
-            const float x = to_f32(sm.dst[ql * C::DT_LD + (cc & ~15) + chunk_slot(cc & 15)]);
-            sum += (c == cc) ? x : 0.f;
-          }
-        }
+        for (int c = 0; c < C::BM / 8; ++c) sum += sum8(ld_frag(row + 8 * c));
         if (sum != 0.f)
           atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
                         pos_bucket(k0 - q0 + (C::BN - 1) - dd, p.max_len),
                     sum);
       }
     }
-    if (has_pos && PART != 2 && tid < C::WIN) {
-      // Flush the position-gradient window of this tile (the general body's
-      // adds; entries it did not touch are zero).
+    if (has_pos && !pos_diag && tid < C::WIN) {
+      // Flush the position-gradient window of this tile.
       const float gsum = sm.wing[tid];
       if (gsum != 0.f) {
         const int p_min = min(q0, hist);
@@ -666,36 +593,6 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
                       pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len),
                   gsum);
         sm.wing[tid] = 0.f;
-      }
-    }
-    // dQ += dS K for this wave's output blocks (32 queries x 32 head dims).
-#pragma unroll
-    for (int m = 0; m < C::NDQ; ++m) {
-      const int blk = wave + 4 * m;
-      if (blk < C::QB * C::DB) {
-        const int qb = blk / C::DB, db = blk % C::DB;
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int kc = 0; kc < C::BN / 16; ++kc) {
-          const F a = ld_frag(sm.dst + (32 * qb + l32) * C::DT_LD + 16 * kc + 8 * g);
-          const F b = ld_frag(sm.kt + (32 * db + l32) * C::KT_LD + 16 * kc + 8 * g);
-          mfma_32x32x16(acc, a, b);
-        }
-        // register r: query row i0 + 8(r/4) + r%4, head dim 32 db + l32
-        const int i0 = q0 + 32 * qb + 4 * g;
-        float* const dq_row = p.dq_acc + ((start + i0) * H + head) * (int64_t)D + 32 * db + l32;
-        if (q0 + 32 * qb + 31 < L) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            atomicAdd(dq_row + (int64_t)(8 * (r >> 2) + (r & 3)) * HD, acc[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (i0 + 8 * (r >> 2) + (r & 3) < L)
-              atomicAdd(dq_row + (int64_t)(8 * (r >> 2) + (r & 3)) * HD, acc[r]);
-        }
       }
     }
     n = n_next;

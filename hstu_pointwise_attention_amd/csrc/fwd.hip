@@ -20,6 +20,13 @@
 // before the elementwise work of the current one so the two overlap.
 #include "internal.h"
 
+#ifndef DQ_WAVES
+#define DQ_WAVES 2
+#endif
+#ifndef DQ_PIPE
+#define DQ_PIPE 0
+#endif
+
 namespace hstu {
 
 namespace {
@@ -35,7 +42,9 @@ template <> struct FwdLd<bf16, 128> { static constexpr int K = 136, V = 152; };
 template <> struct FwdLd<float, 32> { static constexpr int K = 36, V = 36; };
 template <> struct FwdLd<float, 64> { static constexpr int K = 68, V = 68; };
 
-template <typename T, int D>
+// GRAD: the query-block pass of the backward, which computes dQ with the
+// same tiling (see the comment of fwd_body).
+template <typename T, int D, bool GRAD = false>
 struct FwdCfg {
   static constexpr int BM = 128;                 // query rows per workgroup
   static constexpr int BN = 64;                  // keys per tile
@@ -46,29 +55,37 @@ struct FwdCfg {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int VPC = 16 / ES;            // elements per 16-byte chunk
   static constexpr int CPR = D / VPC;            // 16-byte chunks per row
-  static constexpr int K_LD = FwdLd<T, D>::K;
-  static constexpr int V_LD = FwdLd<T, D>::V;
+  // The gradient pass reads K both ways (rows for K Q^T, transposed for
+  // K^T dS^T) and V only by rows, so the two strides swap.
+  static constexpr int K_LD = GRAD ? FwdLd<T, D>::V : FwdLd<T, D>::K;
+  static constexpr int V_LD = GRAD ? FwdLd<T, D>::K : FwdLd<T, D>::V;
   static constexpr int WIN = BN + BM;            // position-bias window (>= BN + BM - 1)
   static constexpr int CH = BN * CPR / NT;       // 16-byte chunks per thread per tile (K or V)
   static constexpr int MAX_TIME = 1024;
   static_assert(BN * CPR % NT == 0, "staging");
 };
 
-template <typename T, int D>
+template <typename T, int D, bool GRAD>
 struct FwdSmem {
-  using C = FwdCfg<T, D>;
+  using C = FwdCfg<T, D, GRAD>;
   T k[2][C::BN * C::K_LD];
   T v[2][C::BN * C::V_LD];
   int64_t ts[2][C::BN];          // key timestamps: rebased (low 32 bits) or raw
   int64_t tsq[C::BM];            // query timestamps of the block
   float win[2][C::WIN];          // rab_pos window for the tile
-  float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr]
+  float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr] (forward), rab_time[hr] (gradient)
 };
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
-__device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm, const WorkItem wi,
-                                         const SeqInfo si, const int head) {
-  using C = FwdCfg<T, D>;
+// GRAD (the dQ pass of the backward): the same walk over key tiles with
+// the same bias and mask, but per tile
+//   S^T  = K Q^T + bias,  dP^T = V dA'^T        (dA' = dO*U/L resident like Q)
+//   dS^T = dP^T * sigma(S)(1 + S(1 - sigma(S)))  (0 where masked)
+//   dQ^T += K^T dS^T                             (K^T by LDS transpose reads)
+// so dQ stays in registers and is written once, with no atomics.
+template <typename T, int D, bool WIDE, bool POS, bool TIME, bool GRAD>
+__device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD>& sm,
+                                         const WorkItem wi, const SeqInfo si, const int head) {
+  using C = FwdCfg<T, D, GRAD>;
   using F = typename Frag<T>::type;
   const int H = p.H;
   const int L = si.len, hist = si.hist;
@@ -98,7 +115,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 
   if constexpr (has_time)
     for (int x = tid; x < p.n_time_buckets; x += C::NT)
-      sm.ttab[x] = kNegLog2e * p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+      sm.ttab[x] = (GRAD ? 1.f : kNegLog2e) * p.rab_time[(int64_t)hr * p.n_time_buckets + x];
 
   // Q fragments of this lane's row (B operand of S^T = K Q^T).
   F qf[C::KC];
@@ -109,6 +126,20 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) qf[c][m] = from_f32<T>(0.f);
+    }
+  }
+  // dA' fragments of this lane's row (B operand of dP^T = V dA'^T).
+  F daf[GRAD ? C::KC : 1];
+  if constexpr (GRAD) {
+    const T* dag = reinterpret_cast<const T*>(p.d_a);
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      if (row_ok) {
+        daf[c] = ld_frag(dag + ((start + i) * H + head) * (int64_t)D + 16 * c + 8 * g);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) daf[c][m] = from_f32<T>(0.f);
+      }
     }
   }
   int64_t ts_i = 0;
@@ -210,7 +241,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
           thr = (int32_t)ts_i + 1 - (1 << b_hi);     // hi iff ts_j <= ts_i + 1 - 2^b_hi
         }
       }
-      auto s_block = [&](int kb, f32x16& acc) {
+      auto s_block = [&](int kb, f32x16& acc, f32x16& pacc) {
         if constexpr (has_pos) {
           const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
 #pragma unroll
@@ -219,10 +250,17 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = 0.f;
         }
+        if constexpr (GRAD)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
         for (int c = 0; c < C::KC; ++c) {
           const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
           mfma_32x32x16(acc, a, qf[c]);
+          if constexpr (GRAD) {
+            const F b = ld_frag(vs + (32 * kb + l32) * C::V_LD + 16 * c + 8 * g);
+            mfma_32x32x16(pacc, b, daf[c]);
+          }
         }
       };
       // TM: time-bias mode (3: 64-bit timestamps); MASK: causal / candidate
@@ -232,34 +270,48 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
         constexpr bool MASK = decltype(mk)::value;
         const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
-        f32x16 sacc[C::KB];
-        s_block(0, sacc[0]);
+        // The next 32-key block's MFMAs are issued before this block's
+        // elementwise work (PIPE) unless the gradient pass runs two waves
+        // per SIMD and lacks the registers.
+        constexpr bool PIPE = !GRAD || DQ_PIPE;
+        f32x16 sacc[C::KB], pacc[GRAD ? C::KB : 1];
+        if constexpr (PIPE) s_block(0, sacc[0], pacc[0]);
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
-          if (kb + 1 < C::KB) s_block(kb + 1, sacc[kb + 1]);
+          if constexpr (PIPE) {
+            if (kb + 1 < C::KB) s_block(kb + 1, sacc[kb + 1], pacc[GRAD ? kb + 1 : 0]);
+          } else {
+            s_block(kb, sacc[kb], pacc[GRAD ? kb : 0]);
+          }
           float pv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
             const float a = sacc[kb][r];
-            float s;
+            // time bias of this pair (pre-scaled by -log2(e) in the forward)
+            float tb = 0.f;
             if constexpr (has_time) {
               if constexpr (TM == 0) {
-                s = __builtin_fmaf(a, kNegLog2e, tb_lo);
+                tb = tb_lo;
               } else if constexpr (TM == 1) {
                 const bool hi = (int32_t)sm.ts[buf][jl] <= thr;
-                s = __builtin_fmaf(a, kNegLog2e, hi ? tb_hi : tb_lo);
+                tb = hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
-                const int bt = time_bucket_rel((uint32_t)ts_i, (uint32_t)sm.ts[buf][jl], t_last);
-                s = __builtin_fmaf(a, kNegLog2e, sm.ttab[bt]);
+                tb = sm.ttab[time_bucket_rel((uint32_t)ts_i, (uint32_t)sm.ts[buf][jl], t_last)];
               } else {
-                const int bt = time_bucket_wide(ts_i, sm.ts[buf][jl], t_last);
-                s = __builtin_fmaf(a, kNegLog2e, sm.ttab[bt]);
+                tb = sm.ttab[time_bucket_wide(ts_i, sm.ts[buf][jl], t_last)];
               }
-            } else {
-              s = a * kNegLog2e;
             }
-            float pr = s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s));
+            float pr;
+            if constexpr (GRAD) {
+              const float sv = a + tb;
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kNegLog2e));
+              const float sl = sv * sg;
+              pr = pacc[kb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
+            } else {
+              const float sv = __builtin_fmaf(a, kNegLog2e, tb);
+              pr = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv));
+            }
             if constexpr (MASK) {
               const int j = j0 + jl;
               const bool ok = j <= i && (j < hist || j == i);
@@ -273,7 +325,9 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
             const int kr = 32 * kb + 16 * h;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              const F a = ld_frag_kmajor(vs, C::V_LD, 32 * db, kr, kr + 8);
+              // forward: O^T += V^T P^T; gradient: dQ^T += K^T dS^T
+              const F a = GRAD ? ld_frag_kmajor(ks, C::K_LD, 32 * db, kr, kr + 8)
+                               : ld_frag_kmajor(vs, C::V_LD, 32 * db, kr, kr + 8);
               mfma_32x32x16(acc_o[db], a, pf);
             }
           }
@@ -304,6 +358,21 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 
   // ---------------------------------------------------------------- epilogue
   if (!row_ok) return;
+  if constexpr (GRAD) {
+    // dQ row of this lane: register 4 rq + m of block db is head dim
+    // 32 db + 8 rq + 4 g + m (1/L is already in dA').
+    T* dqg = reinterpret_cast<T*>(p.dq) + ((start + i) * H + head) * (int64_t)D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        f32x4 a;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = acc_o[db][4 * rq + m];
+        st4_from_f32(dqg + 32 * db + 8 * rq + 4 * g, a);
+      }
+    return;
+  }
   const float scale = kNegLn2 * si.inv_len;
   const int64_t orow = ((start + i) * H + head) * (int64_t)D;
   T* og = reinterpret_cast<T*>(p.o) + orow;
@@ -331,36 +400,67 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D>& sm,
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_kernel(AttnParams p) {
-  __shared__ FwdSmem<T, D> sm;
+  __shared__ FwdSmem<T, D, false> sm;
   const int item = blockIdx.x / p.H;
   const int head = blockIdx.x - item * p.H;
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
   const SeqInfo si = p.seq[wi.seq];
   if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  fwd_body<T, D, WIDE, POS, TIME>(p, sm, wi, si, head);
+  fwd_body<T, D, WIDE, POS, TIME, false>(p, sm, wi, si, head);
+}
+
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQ_WAVES, DQ_WAVES)))
+void hstu_dq_kernel(AttnParams p) {
+  __shared__ FwdSmem<T, D, true> sm;
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;
+  fwd_body<T, D, WIDE, POS, TIME, true>(p, sm, wi, si, head);
+}
+
+template <bool GRAD, typename T, int D, bool WIDE, bool POS, bool TIME>
+void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
+  if constexpr (GRAD)
+    hipLaunchKernelGGL((hstu_dq_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((hstu_fwd_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+}
+
+template <bool GRAD, typename T, int D>
+hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
+  const int64_t grid = p.max_items * p.H;
+  if (grid == 0) return hipSuccess;
+  const dim3 g((unsigned)grid);
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
+  prof_before(id, s);
+  if (pos && time) launch_one<GRAD, T, D, false, true, true>(p, g, s);
+  else if (pos) launch_one<GRAD, T, D, false, true, false>(p, g, s);
+  else if (time) launch_one<GRAD, T, D, false, false, true>(p, g, s);
+  else launch_one<GRAD, T, D, false, false, false>(p, g, s);
+  // Only a time bias can mark a sequence as needing 64-bit timestamps.
+  if (time) {
+    if (pos) launch_one<GRAD, T, D, true, true, true>(p, g, s);
+    else launch_one<GRAD, T, D, true, false, true>(p, g, s);
+  }
+  prof_after(id, s);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 template <typename T, int D>
 hipError_t launch_fwd(const AttnParams& p, hipStream_t s) {
-  const int64_t grid = p.max_items * p.H;
-  if (grid == 0) return hipSuccess;
-  const dim3 g((unsigned)grid), b(256);
-  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
-  prof_before(kKFwd, s);
-  if (pos && time) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, true, true>), g, b, 0, s, p);
-  else if (pos) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, true, false>), g, b, 0, s, p);
-  else if (time) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, false, true>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((hstu_fwd_kernel<T, D, false, false, false>), g, b, 0, s, p);
-  prof_after(kKFwd, s);
-  hipError_t e = hipGetLastError();
-  // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (e != hipSuccess || !time) return e;
-  if (pos) hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true, true, true>), g, b, 0, s, p);
-  else hipLaunchKernelGGL((hstu_fwd_kernel<T, D, true, false, true>), g, b, 0, s, p);
-  return hipGetLastError();
+  return launch_all<false, T, D>(p, kKFwd, s);
+}
+
+template <typename T, int D>
+hipError_t launch_dq(const AttnParams& p, hipStream_t s) {
+  return launch_all<true, T, D>(p, kKDq, s);
 }
 
 template hipError_t launch_fwd<bf16, 32>(const AttnParams&, hipStream_t);
@@ -368,5 +468,10 @@ template hipError_t launch_fwd<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<bf16, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<bf16, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<bf16, 128>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<float, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<float, 64>(const AttnParams&, hipStream_t);
 
 }  // namespace hstu

@@ -37,7 +37,6 @@ struct AttnParams {
   WorkItem* items;                   // [max_items]
   int32_t* n_items;                  // [1]
   int32_t* sched_scratch;            // schedule kernel scratch
-  float* dq_acc;                     // [T, H, D] fp32 (backward)
   float* dkv_part;                   // [2, T, H, D] fp32 partial dK, dV (split backward)
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
@@ -49,12 +48,15 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
 
 // bf16 at head dim 128 runs the backward as two launches (general tiles,
 // then fast tiles) that meet through fp32 dK / dV partials.
-constexpr bool bwd_split_shape(int elem_bytes, int D) { return elem_bytes == 2 && D == 128; }
+#ifndef BWD_SPLIT
+#define BWD_SPLIT 0
+#endif
+constexpr bool bwd_split_shape(int elem_bytes, int D) { return BWD_SPLIT && elem_bytes == 2 && D == 128; }
 inline bool bwd_split(const AttnParams& p) { return p.dkv_part != nullptr; }
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
-  kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKBwdPost, kKFill, kKLinear, kKLayerNorm,
+  kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
   kKBucketize, kNumKernelIds
 };
 // Records a HIP event on `s` before / after a launch when timing is enabled.
@@ -68,9 +70,11 @@ hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, ui
                             uint8_t* bt, hipStream_t s);
 
 template <typename T, int D> hipError_t launch_fwd(const AttnParams& p, hipStream_t s);
+// Backward: launch_bwd computes dK, dV and the rab gradients per key block;
+// launch_dq computes dQ per query block (schedule mode 0, like the forward).
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);
+template <typename T, int D> hipError_t launch_dq(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
-template <typename T> hipError_t launch_bwd_post(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 
 hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,

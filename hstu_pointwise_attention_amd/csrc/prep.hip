@@ -252,13 +252,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnParams p) {
   }
 }
 
-// dQ: fp32 accumulator -> output dtype.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_post_kernel(const float* acc, T* out, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = from_f32<T>(acc[i]);
-}
 
 int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
@@ -282,11 +275,9 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.items = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
   p.n_items = (int32_t*)take(sizeof(int32_t));
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 3 * NB));
-  p.dq_acc = nullptr;
   p.d_a = nullptr;
   p.dkv_part = nullptr;
   if (bwd) {
-    p.dq_acc = (float*)take(sizeof(float) * (size_t)p.T * p.H * p.D);
     p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
     if (bwd_split_shape(elem_bytes, p.D)) {
       float* part = (float*)take(2 * sizeof(float) * (size_t)p.T * p.H * p.D);
@@ -339,20 +330,7 @@ hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_bwd_post(const AttnParams& p, hipStream_t s) {
-  const int64_t n = p.T * p.H * p.D;
-  if (n == 0) return hipSuccess;
-  prof_before(kKBwdPost, s);
-  hipLaunchKernelGGL(bwd_post_kernel<T>, dim3(grid_for(n, 256)), dim3(256), 0, s, p.dq_acc,
-                     reinterpret_cast<T*>(p.dq), n);
-  prof_after(kKBwdPost, s);
-  return hipGetLastError();
-}
-
 template hipError_t launch_bwd_pre<bf16>(const AttnParams&, hipStream_t);
 template hipError_t launch_bwd_pre<float>(const AttnParams&, hipStream_t);
-template hipError_t launch_bwd_post<bf16>(const AttnParams&, hipStream_t);
-template hipError_t launch_bwd_post<float>(const AttnParams&, hipStream_t);
 
 }  // namespace hstu

@@ -35,7 +35,7 @@ hipEvent_t take_event() {
 }
 
 const char* const kNames[kNumKernelIds] = {"prep", "schedule", "fwd", "bwd_pre", "bwd",
-                                           "bwd_post", "fill", "linear", "layernorm_gate",
+                                           "dq", "fill", "linear", "layernorm_gate",
                                            "bucketize"};
 
 }  // namespace
