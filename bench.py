@@ -27,6 +27,15 @@ sys.path.insert(0, ROOT)
 METRIC = "HSTU jagged attn fwd+bwd TFLOP/s @ max_len 8192; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) scaled by the copy-kernel calibration; the
+# summaries are under profiles/. None when not measured for the kernel as it
+# stands.
+TRAFFIC = {
+    # hstu_bwd_kernel<bf16, 128>: 622.2 MiB fetched + 130.4 MiB written per launch
+    "bwd": {"fetch_bytes": 652_418_000, "write_bytes": 136_773_000, "total_bytes": 789_191_000,
+            "compulsory_bytes": 263_000_000, "unit": "B"},
+}
 
 
 def parse():
@@ -113,16 +122,21 @@ def main():
     tflops = fl["total"] / (ms_step * 1e-3) / 1e12
 
     kern = {name: round(kt.avg_ms(name), 5) for name in kt.results}
-    bwd_ms = kt.avg_ms("bwd")
     fwd_ms = kt.avg_ms("fwd")
+    # the backward: dA' / dU preprocessing, key-block kernel, dQ kernel
+    bwd_ms = sum(kt.avg_ms(k) for k in ("bwd_pre", "bwd", "dq"))
     bwd_tf = fl["bwd"] / (bwd_ms * 1e-3) / 1e12
     fwd_tf = fl["fwd"] / (fwd_ms * 1e-3) / 1e12
-    # the dominant kernel by time
-    dom, dom_ms, dom_flops = ("bwd", bwd_ms, fl["bwd"]) if bwd_ms >= fwd_ms else ("fwd", fwd_ms, fl["fwd"])
+    per_kernel = {k: {"ms": round(kt.avg_ms(k), 5), "algorithmic_flops": f,
+                      "tflops": round(f / (kt.avg_ms(k) * 1e-3) / 1e12, 2)}
+                  for k, f in fl["kernels"].items()}
+    # the dominant attention kernel by time
+    dom = max(fl["kernels"], key=lambda k: kt.avg_ms(k))
+    dom_ms, dom_flops = kt.avg_ms(dom), fl["kernels"][dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": TRAFFIC.get(dom),
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 5)}
 
     out = {
@@ -137,6 +151,7 @@ def main():
                    "tokens": int(inp["seq_offsets"][-1]), "pair_heads": fl["pair_heads"],
                    "flops_per_step": fl["total"], "rab": "position 16383 + time 128 buckets"},
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+        "attention_kernels": per_kernel,
         "kernels_avg_ms": kern,
         "roofline": roofline,
     }

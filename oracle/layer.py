@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attention_fwd, silu
+from .attention import attention_fwd, attention_fwd_rows, silu
 
 LN_EPS = 1e-5
 
@@ -53,3 +53,34 @@ def layer_fwd(x, w1, b1, w2, b2, seq_offsets, num_targets, heads, head_dim,
     y = (layernorm(a2) * u.reshape(T, heads * head_dim)) @ np.asarray(w2, np.float64) \
         + np.asarray(b2, np.float64)
     return dict(uvqk=uvqk, a=a2, y=y)
+
+
+def layer_fwd_rows(x, w1, b1, w2, b2, seq_offsets, num_targets, heads, head_dim, token_rows):
+    """uvqk, a and y of :func:`layer_fwd` at selected global rows only.
+
+    The projection is evaluated for the sequences that hold those rows (a
+    row's attention reads its whole sequence), the attention and the output
+    steps for the rows themselves.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    offs = np.asarray(seq_offsets, dtype=np.int64)
+    token_rows = np.asarray(token_rows, dtype=np.int64)
+    n, HD = len(token_rows), heads * head_dim
+    out = dict(uvqk=np.zeros((n, 4 * HD)), a=np.zeros((n, HD)), y=np.zeros((n, w2.shape[1])))
+    seqs = np.searchsorted(offs, token_rows, side="right") - 1
+    for b in np.unique(seqs):
+        s, e = int(offs[b]), int(offs[b + 1])
+        uvqk = silu(x[s:e] @ w1 + np.asarray(b1, np.float64))
+        u, v, q, k = split_uvqk(uvqk, heads, head_dim)
+        sel = np.nonzero(seqs == b)[0]
+        rows = token_rows[sel] - s
+        nt = None if num_targets is None else np.array([int(num_targets[b])])
+        _, a = attention_fwd_rows(q, k, v, None, np.array([0, e - s]), max(e - s, 1), rows, nt)
+        a2 = a.reshape(len(rows), HD)
+        out["uvqk"][sel] = uvqk[rows]
+        out["a"][sel] = a2
+        out["y"][sel] = (layernorm(a2) * u[rows].reshape(len(rows), HD)) @ w2 \
+            + np.asarray(b2, np.float64)
+    return out

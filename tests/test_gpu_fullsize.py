@@ -1,0 +1,139 @@
+"""Full-size parity of the HIP path on sampled outputs (needs a gfx950 GPU).
+
+The efficiency workload (8 sequences, lengths U[4096, 8192], 4 heads, head
+dim 128, bf16, both rab tables) runs through the C ABI exactly as the
+benchmark times it; the oracle then evaluates sampled outputs one by one
+(oracle/sampled.py): rows of O, A, dQ and dU, key rows of dK and dV, and
+d_rab_pos entries as diagonal sums of dS. d_rab_time is checked through a
+property that holds at any size: every unmasked pair adds its dS to exactly
+one position bucket and one time bucket, so both tables sum to the same
+total. The M-FALCON layer workload (4 users x (8192 + 1024 candidates),
+d_model 512) is checked on sampled rows of UVQK, A and Y.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle import sampled
+from oracle.layer import layer_fwd_rows
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hstu_pointwise_attention_amd import _lib
+    _lib.load()
+
+
+def _sample_rows(offs, rng, per_seq=6):
+    """Per sequence: first and last rows, rows at 64/128 tile edges, random rows."""
+    rows = []
+    for b in range(len(offs) - 1):
+        s, e = int(offs[b]), int(offs[b + 1])
+        L = e - s
+        picks = {0, L - 1, min(63, L - 1), min(64, L - 1), min(127, L - 1), min(128, L - 1)}
+        picks |= set(int(x) for x in rng.integers(0, L, size=per_seq))
+        rows += [s + i for i in sorted(picks)]
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.fixture(scope="module")
+def efficiency():
+    import torch
+    inp = W.make_attention_inputs(W.EFFICIENCY)
+    dev = P.to_dev(inp)
+    O, A = P.gpu_fwd(inp, dev)
+    g = P.gpu_bwd(inp, A, dev)
+    torch.cuda.synchronize()
+    got = {"O": P.host(O), "A": P.host(A)}
+    got.update({k: P.host(v) for k, v in g.items()})
+    print(f"efficiency workload: T={int(inp['seq_offsets'][-1])}", flush=True)
+    return inp, got
+
+
+def test_efficiency_forward_rows(efficiency):
+    inp, got = efficiency
+    rows = _sample_rows(inp["seq_offsets"], np.random.default_rng(7))
+    wO, wA = oracle.attention_fwd_rows(inp["q"], inp["k"], inp["v"], inp["u"], inp["seq_offsets"],
+                                       inp["max_len"], rows, inp["num_targets"], inp["timestamps"],
+                                       inp["rab_pos"], inp["rab_time"])
+    err = float(np.max(np.abs(got["O"][rows] - wO)))
+    assert err <= P.BF16_O_MAXABS, ("O max-abs", err)
+    assert P.rel_l2(got["O"][rows], wO) <= P.BF16_REL
+    assert P.rel_l2(got["A"][rows], wA) <= P.BF16_REL
+
+
+def test_efficiency_backward_rows_and_keys(efficiency):
+    inp, got = efficiency
+    rng = np.random.default_rng(8)
+    args = (inp["q"], inp["k"], inp["v"], inp["u"], inp["seq_offsets"], inp["max_len"], inp["d_o"])
+    rest = dict(num_targets=inp["num_targets"], timestamps=inp["timestamps"],
+                rab_pos=inp["rab_pos"], rab_time=inp["rab_time"])
+    rows = _sample_rows(inp["seq_offsets"], rng, per_seq=4)
+    dq, du = sampled.attention_bwd_rows(*args, rows, **rest)
+    assert P.rel_l2(got["dq"][rows], dq) <= P.BF16_REL, P.rel_l2(got["dq"][rows], dq)
+    assert P.rel_l2(got["du"][rows], du) <= P.BF16_REL, P.rel_l2(got["du"][rows], du)
+    keys = _sample_rows(inp["seq_offsets"], rng, per_seq=4)
+    dk, dv = sampled.attention_bwd_cols(*args, keys, **rest)
+    assert P.rel_l2(got["dk"][keys], dk) <= P.BF16_REL, P.rel_l2(got["dk"][keys], dk)
+    assert P.rel_l2(got["dv"][keys], dv) <= P.BF16_REL, P.rel_l2(got["dv"][keys], dv)
+
+
+def test_efficiency_rab_gradients(efficiency):
+    inp, got = efficiency
+    lengths = np.diff(inp["seq_offsets"])
+    assert inp["num_targets"] is None and int(lengths.max()) <= inp["max_len"]
+    # diagonals near the main one (the largest entries), tile edges, and far ones
+    deltas = np.array([0, -1, -2, -3, -31, -32, -63, -64, -65, -127, -128, -129, -500,
+                       -2047, -4095, -4096, -6000, -8000])
+    want = sampled.diagonal_ds_sums(inp["q"], inp["k"], inp["v"], inp["u"], inp["seq_offsets"],
+                                    inp["max_len"], inp["d_o"], deltas, inp["timestamps"],
+                                    inp["rab_pos"], inp["rab_time"])
+    g = got["d_rab_pos"][0, deltas + inp["max_len"] - 1]
+    assert P.rel_l2(g, want) <= P.BF16_REL, (P.rel_l2(g, want), g, want)
+    # positive offsets are never read by causal pairs
+    assert np.all(got["d_rab_pos"][0, inp["max_len"]:] == 0)
+    # both tables hold the same total of dS
+    tp, tt = float(np.sum(got["d_rab_pos"])), float(np.sum(got["d_rab_time"]))
+    scale = float(np.sum(np.abs(got["d_rab_pos"])))
+    assert abs(tp - tt) <= 1e-3 * scale, (tp, tt, scale)
+
+
+@pytest.fixture(scope="module")
+def layer():
+    import torch
+    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd
+    li = W.make_layer_inputs(W.MFALCON_LAYER)
+    dev = "cuda"
+    t = {k: torch.from_numpy(li[k]).to(dev, torch.bfloat16) for k in ("x", "w1", "w2")}
+    t.update({k: torch.from_numpy(li[k]).to(dev) for k in ("b1", "b2", "seq_offsets", "num_targets")})
+    y, a, uvqk = hstu_layer_fwd(t["x"], t["w1"], t["b1"], t["w2"], t["b2"], t["seq_offsets"],
+                                t["num_targets"], li["heads"], li["head_dim"])
+    torch.cuda.synchronize()
+    print(f"layer workload: T={li['x'].shape[0]}", flush=True)
+    return li, {"y": P.host(y), "a": P.host(a), "uvqk": P.host(uvqk)}
+
+
+def test_layer_rows(layer):
+    li, got = layer
+    offs = li["seq_offsets"]
+    rng = np.random.default_rng(9)
+    # two users: history rows, the last history row, candidates
+    rows = []
+    for b in (0, 3):
+        s = int(offs[b])
+        hist = int(offs[b + 1] - offs[b]) - int(li["num_targets"][b])
+        rows += [s, s + 1, s + 4095, s + hist - 1, s + hist, s + hist + 511,
+                 int(offs[b + 1]) - 1] + [s + int(x) for x in rng.integers(0, hist, size=3)]
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    want = layer_fwd_rows(li["x"], li["w1"], li["b1"], li["w2"], li["b2"], offs,
+                          li["num_targets"], li["heads"], li["head_dim"], rows)
+    for key in ("uvqk", "a", "y"):
+        e = P.rel_l2(got[key][rows], want[key])
+        assert e <= P.BF16_REL, (key, e)

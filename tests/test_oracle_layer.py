@@ -2,7 +2,7 @@
 import numpy as np
 
 import oracle
-from oracle.layer import split_uvqk
+from oracle.layer import layer_fwd_rows, split_uvqk
 
 
 def test_layernorm_moments():
@@ -50,3 +50,23 @@ def test_layer_bruteforce_tiny():
         for n in range(dm):
             y[t, n] = b2[n] + sum(g[c] * w2[c, n] for c in range(H * D))
     assert np.max(np.abs(y - r["y"])) < 1e-12
+
+
+def test_layer_rows_match_full():
+    """The sampled-rows form used by the full-size layer check agrees with the full layer."""
+    rng = np.random.default_rng(2)
+    H, D, dm = 2, 4, 6
+    offs = np.array([0, 9, 9, 16])
+    nt = np.array([3, 0, 2])
+    T = 16
+    x = rng.standard_normal((T, dm))
+    w1 = 0.5 * rng.standard_normal((dm, 4 * H * D))
+    b1 = 0.1 * rng.standard_normal(4 * H * D)
+    w2 = 0.5 * rng.standard_normal((H * D, dm))
+    b2 = 0.1 * rng.standard_normal(dm)
+    full = oracle.layer_fwd(x, w1, b1, w2, b2, offs, nt, H, D)
+    rows = np.array([0, 5, 8, 9, 15, 12])
+    part = layer_fwd_rows(x, w1, b1, w2, b2, offs, nt, H, D, rows)
+    for key in ("uvqk", "a", "y"):
+        want = full[key][rows]
+        assert np.max(np.abs(part[key] - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
