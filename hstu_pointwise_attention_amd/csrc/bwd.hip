@@ -24,6 +24,16 @@
 // window instead.
 #include "internal.h"
 
+#ifndef BWD_SPLIT_PIN
+#define BWD_SPLIT_PIN 0
+#endif
+#ifndef BWD_DK_PIPE
+#define BWD_DK_PIPE 0
+#endif
+#ifndef BWD_KV_WAVES
+#define BWD_KV_WAVES 2
+#endif
+
 #ifndef BWD_PIPE
 #define BWD_PIPE true
 #endif
@@ -63,7 +73,6 @@ struct BwdCfg {
   static constexpr int WIN = BN + BM;            // >= BN + BM - 1
   static constexpr int CH = BM * CPR / NT;       // 16-byte chunks per thread per tile
   static constexpr int MAX_TIME = 1024;
-  static constexpr int MAX_QT = 2048;            // tiles whose fast/general flag is kept in LDS
   // Time-gradient histogram: with up to HREP_NT buckets, HREP copies (lane
   // l adds into copy l % HREP, HREP_LD floats apart so a bucket's copies sit
   // in different banks) keep the per-element adds of one instruction from
@@ -88,7 +97,6 @@ struct BwdSmem {
   int64_t tsk[C::BN];            // timestamps of the key block
   float ttab[C::MAX_TIME];
   float thist[C::THIST];
-  uint8_t tflag[C::MAX_QT];      // 1: the tile takes the fast body (see tile_fast)
 };
 
 __device__ __forceinline__ float sum8(const bf16x8& v) {
@@ -106,14 +114,16 @@ __device__ __forceinline__ float sum8(const f32x8& v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
-// PART 0: every tile of the key block; 1: only the tiles the fast body does
-// not take, dK / dV partials to the workspace; 2: only the fast tiles,
-// starting from those partials.
-template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
+// KV 0: dK, dV and the rab gradients in one pass; 1: dV only (S, SiLU,
+// s^T dA'); 2: dK and the rab gradients only (S, dP, dS, dS^T Q). The split
+// form spends one more GEMM (S twice) to fit two waves per SIMD.
+template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
   using F = typename Frag<T>::type;
+  constexpr bool DV = KV != 2;                   // this pass computes dV
+  constexpr bool DK = KV != 1;                   // this pass computes dK and d_rab
   const int H = p.H;
   const int L = si.len, hist = si.hist;
   const int64_t start = si.start;
@@ -130,6 +140,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   // straight-line code the scheduler can interleave.
   constexpr bool has_pos = POS;
   constexpr bool has_time = TIME;
+  constexpr bool pos_grad = has_pos && DK;       // this pass sums d_rab_pos
+  constexpr bool time_grad = has_time && DK;     // this pass sums d_rab_time
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
   // timestamps and run in the second instantiation of the kernel.
@@ -149,21 +161,21 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   float* const thist_lane = sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
   for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
   // Diagonal-copy entries that no element maps to stay zero for the whole loop.
-  if (has_pos)
+  if (pos_grad)
     for (int x = tid; x < C::NDIAG * C::DG_LD; x += C::NT) sm.dsd[x] = from_f32<T>(0.f);
 
   // Resident K, V fragments of this lane's key (B operands of Q K^T, dA' V^T).
-  F kf[C::KC], vf[C::KC];
+  F kf[C::KC], vf[DK ? C::KC : 1];
 #pragma unroll
   for (int c = 0; c < C::KC; ++c) {
     if (key_ok) {
       kf[c] = ld_frag(kg + (start + j) * p.sk + (int64_t)head * D + 16 * c + 8 * g);
-      vf[c] = ld_frag(vg + (start + j) * p.sv + (int64_t)head * D + 16 * c + 8 * g);
+      if constexpr (DK) vf[c] = ld_frag(vg + (start + j) * p.sv + (int64_t)head * D + 16 * c + 8 * g);
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         kf[c][m] = from_f32<T>(0.f);
-        vf[c][m] = from_f32<T>(0.f);
+        if constexpr (DK) vf[c][m] = from_f32<T>(0.f);
       }
     }
   }
@@ -223,101 +235,46 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
   };
 
-  // Partial dK / dV of this lane: register r of block db is key
-  // jw + 8(r/4) + 4g + r%4, head dim 32 db + l32.
-  const int64_t THD = p.T * HD;
-  auto part_off = [&](int db, int r) {
-    return ((start + jw + 8 * (r >> 2) + 4 * g + (r & 3)) * H + head) * (int64_t)D + 32 * db + l32;
-  };
-  f32x16 acc_dk[C::DB], acc_dv[C::DB];
+  f32x16 acc_dk[DK ? C::DB : 1], acc_dv[DV ? C::DB : 1];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool in = PART == 2 && jw + 8 * (r >> 2) + 4 * g + (r & 3) < L;
-      acc_dk[db][r] = in ? p.dkv_part[part_off(db, r)] : 0.f;
-      acc_dv[db][r] = in ? p.dkv_part[THD + part_off(db, r)] : 0.f;
+      if constexpr (DK) acc_dk[db][r] = 0.f;
+      if constexpr (DV) acc_dv[db][r] = 0.f;
     }
-
-  // Wave w of tile n takes the fast body when none of its pairs is masked,
-  // the rows it sees are history rows (or there is no position bias) and,
-  // with sorted timestamps, its time buckets span at most two adjacent
-  // values. Every wave evaluates the test for all four, from global memory,
-  // so both parts of a split launch agree on each (tile, wave).
-  auto wave_skip = [&](int n, int w) -> bool {
-    const int q0 = (qt_first + n) * C::BM, jv = k0 + 32 * w;
-    return jv >= L || q0 + C::BM - 1 < jv || (jv >= hist && (q0 > jv + 31 || q0 + C::BM - 1 < jv));
-  };
-  auto wave_fast = [&](int n, int w) -> bool {
-    if (WIDE) return false;
-    const int q0 = (qt_first + n) * C::BM, jv = k0 + 32 * w;
-    if (q0 < jv + 31 || jv + 31 >= hist || q0 + C::BM - 1 >= (has_pos ? hist : L)) return false;
-    if (has_time) {
-      if (!sorted_ts) return false;
-      const uint32_t* tr = p.ts_rel + start;
-      const int bh = time_bucket_rel(tr[q0 + C::BM - 1], tr[jv], t_last);
-      const int bl = time_bucket_rel(tr[q0], tr[jv + 31], t_last);
-      if (bh > bl + 1) return false;
-    }
-    return true;
-  };
-  // Bit w: wave w takes the fast body in tile n.
-  auto fast_mask = [&](int n) -> int {
-    int m = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) m |= wave_fast(n, w) ? 1 << w : 0;
-    return m;
-  };
-  if (PART != 0) {
-    for (int t = tid; t < min(n_qt, C::MAX_QT); t += C::NT) sm.tflag[t] = (uint8_t)fast_mask(t);
-    __syncthreads();
-  }
-  auto tile_mask = [&](int n) -> int { return n < C::MAX_QT ? sm.tflag[n] : fast_mask(n); };
-  // Part 2 visits the tiles with a fast wave, part 1 those with a wave that
-  // computes but is not fast.
-  auto selected = [&](int n) -> bool {
-    if constexpr (PART == 0) {
-      return true;
-    } else {
-      const int m = tile_mask(n);
-      if constexpr (PART == 2) return m != 0;
-      bool any = false;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) any |= !((m >> w) & 1) && !wave_skip(n, w);
-      return any;
-    }
-  };
-  auto next_sel = [&](int n) {
-    while (n < n_qt && !selected(n)) ++n;
-    return n;
-  };
 
   // Per-lane base of this lane's entries in the diagonal copy.
   T* const dsd_lane = sm.dsd + (C::BN - 1 - jl) * C::DG_LD + 4 * g * (C::DG_LD + 1);
 
-  int n = next_sel(0);
-  if (n < n_qt) {
-    load_tile((qt_first + n) * C::BM);
-    store_tile();
-  }
+  load_tile(qt_first * C::BM);
+  store_tile();
   // Nothing loaded before the loop is still in flight when it starts: the
   // memory counters inside the loop then only ever wait for the loop's own
   // loads, never behind the dQ atomics of the previous tile.
   __builtin_amdgcn_s_waitcnt(0);
 
-  while (n < n_qt) {
+  for (int n = 0; n < n_qt; ++n) {
     const int q0 = (qt_first + n) * C::BM;
-    const int n_next = next_sel(n + 1);
-    const bool more = n_next < n_qt;
+    const bool more = n + 1 < n_qt;
     __syncthreads();                               // tile n staged; previous dQ done
     // Keep the loop-carried MFMA operands and accumulators in the
     // accumulation registers: left to itself the allocator parks them in
     // VGPRs between tiles and copies them back and forth every iteration.
+    if constexpr (KV == 0 || BWD_SPLIT_PIN) {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(acc_dk[db]), "+a"(acc_dv[db]));
+      for (int db = 0; db < C::DB; ++db) {
+        if constexpr (DK) asm volatile("" : "+a"(acc_dk[db]));
+        if constexpr (DV) asm volatile("" : "+a"(acc_dv[db]));
+      }
+    }
+    // (the split passes leave K and V to the allocator: their VGPR and AGPR
+    // budgets are half as large)
+    if constexpr (KV == 0) {
 #pragma unroll
-    for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
-    if (more) load_tile((qt_first + n_next) * C::BM);
+      for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
+    }
+    if (more) load_tile(q0 + C::BM);
 
     // Tiles of history rows only sum the position gradient along diagonals of
     // the dS tile after it is complete; tiles with candidate rows (whose
@@ -325,11 +282,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     const bool pos_diag = has_pos && q0 + C::BM - 1 < hist;
     const bool skip = jw >= L || q0 + C::BM - 1 < jw ||
                       (jw >= hist && (q0 > jw + 31 || q0 + C::BM - 1 < jw));
-    // In a split launch each (tile, wave) is computed by one part only; in
-    // the other it contributes zeros like a wave without pairs.
-    bool mine = true;
-    if constexpr (PART != 0) mine = (((tile_mask(n) >> wave) & 1) != 0) == (PART == 2);
-    if (!skip && mine) {
+    if (!skip) {
       const bool need_mask = !(q0 >= jw + 31 && jw + 31 < hist && q0 + C::BM - 1 < L);
       const int p_min = min(q0, hist);
       // Time-bias mode of this wave's sub-tile (its 32 keys x the 64 queries).
@@ -358,8 +311,9 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // below stays branch-free).
       auto sp_block = [&](auto pd, int qb, f32x16& acc_s, f32x16& acc_p) {
         constexpr bool PD = decltype(pd)::value;
+        if constexpr (DK)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
+          for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
         if constexpr (PD) {
           // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
           const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
@@ -379,8 +333,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         for (int c = 0; c < C::KC; ++c) {
           const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
           mfma_32x32x16(acc_s, a, kf[c]);
-          const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
-          mfma_32x32x16(acc_p, b, vf[c]);
+          if constexpr (DK) {
+            const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
+            mfma_32x32x16(acc_p, b, vf[c]);
+          }
         }
       };
       // Per 32-query block: elementwise (SiLU and dS), dV += s^T dA' and
@@ -402,7 +358,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         // with the query, so nearly all elements land in the window.
         float gw[4] = {0.f, 0.f, 0.f, 0.f};
         int b_top = 0;
-        if constexpr (has_time && TM >= 2) {
+        if constexpr (time_grad && TM >= 2) {
           const int q_hi = min(q0 + C::BM - 1, L - 1) - q0;
           b_top = TM == 2 ? time_bucket_rel((uint32_t)sm.tsq[q_hi], (uint32_t)ts_j, t_last)
                           : time_bucket_wide(sm.tsq[q_hi], ts_j, t_last);
@@ -410,7 +366,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         // PIPE: the next block's S and dP MFMAs are issued before this
         // block's elementwise work so the two overlap.
         f32x16 acc_sb[C::QB], acc_pb[C::QB];
-        constexpr bool PIPE = C::PIPE && PART != 1;   // the general part keeps registers instead
+        // (the dK pass at two waves per SIMD lacks the registers)
+        constexpr bool PIPE = C::PIPE && (KV != 2 || BWD_DK_PIPE);
         if constexpr (PIPE) sp_block(pd, 0, acc_sb[0], acc_pb[0]);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
@@ -422,12 +379,17 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           f32x16& acc_s = acc_sb[qb];
           f32x16& acc_p = acc_pb[qb];
           // B operands of the first 16-query chunk's dV / dK products, read
-          // now so the elementwise work below covers the LDS latency.
-          F bv0[C::DB], bk0[C::DB];
+          // now so the elementwise work below covers the LDS latency (one
+          // wave per SIMD); with two, the other wave covers it and the
+          // registers are short.
+          constexpr bool PREFETCH = KV == 0;
+          F bv0[DV ? C::DB : 1], bk0[DK ? C::DB : 1];
+          if constexpr (PREFETCH) {
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
-            bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+            for (int db = 0; db < C::DB; ++db) {
+              if constexpr (DV) bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+              if constexpr (DK) bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+            }
           }
           int bts[16];
 #pragma unroll
@@ -451,16 +413,16 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             }
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
             float sl = s * sg;
-            float ds = acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl));
+            float ds = DK ? acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl)) : 0.f;
             if constexpr (MASK) {
               const bool ok = j <= i && (j < hist || j == i) && i < L;
               sl = ok ? sl : 0.f;
               ds = ok ? ds : 0.f;
             }
             acc_s[r] = sl;
-            acc_p[r] = ds;
+            if constexpr (DK) acc_p[r] = ds;
             bts[r] = bt;
-            if constexpr (TM == 1 && has_time) {
+            if constexpr (TM == 1 && time_grad) {
               g_all += ds;
               g_hi += hi ? ds : 0.f;
             }
@@ -471,17 +433,17 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           // The position gradient goes through the diagonal copy in history
           // tiles (plain stores) and through window adds only in tiles with
           // candidate rows; LDS float atomics cost far more than stores.
-          const bool to_copy = has_pos && (PD || pos_diag);
+          const bool to_copy = pos_grad && (PD || pos_diag);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < 16 && DK; ++r) {
             const float ds = acc_p[r];
-            if constexpr (has_pos && !PD) {
+            if constexpr (pos_grad && !PD) {
               if (!pos_diag) {
                 const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
                 atomicAdd(&sm.wing[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
               }
             }
-            if constexpr (has_time && TM >= 2) {
+            if constexpr (time_grad && TM >= 2) {
               const int k = b_top - bts[r];
 #pragma unroll
               for (int w = 0; w < 4; ++w) gw[w] += k == w ? ds : 0.f;
@@ -493,34 +455,45 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           F sf[2], df[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
-            df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
+            if constexpr (DV) sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
+            if constexpr (DK) df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
           }
-          // second chunk's operands in flight while the first chunk's MFMAs run
-          F bv1[C::DB], bk1[C::DB];
+          if constexpr (PREFETCH) {
+            // second chunk's operands in flight while the first chunk's MFMAs run
+            F bv1[DV ? C::DB : 1], bk1[DK ? C::DB : 1];
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            bv1[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
-            bk1[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
-          }
+            for (int db = 0; db < C::DB; ++db) {
+              if constexpr (DV) bv1[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+              if constexpr (DK) bk1[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+            }
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            mfma_32x32x16(acc_dv[db], sf[0], bv0[db]);
-            mfma_32x32x16(acc_dk[db], df[0], bk0[db]);
-          }
+            for (int db = 0; db < C::DB; ++db) {
+              if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[0], bv0[db]);
+              if constexpr (DK) mfma_32x32x16(acc_dk[db], df[0], bk0[db]);
+            }
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
-            mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
+            for (int db = 0; db < C::DB; ++db) {
+              if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
+              if constexpr (DK) mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int db = 0; db < C::DB; ++db) {
+                const int kr = 32 * qb + 16 * h;
+                if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[h], ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8));
+                if constexpr (DK) mfma_32x32x16(acc_dk[db], df[h], ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8));
+              }
           }
         }
-        if constexpr (has_time && TM >= 2) {
+        if constexpr (time_grad && TM >= 2) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             if (gw[w] != 0.f) atomicAdd(thist_lane + (b_top - w), gw[w]);
         }
         if constexpr (TM < 2) {
-          if constexpr (has_time) {
+          if constexpr (time_grad) {
             g_all = wave_sum(g_all);
             if constexpr (TM == 1) g_hi = wave_sum(g_hi);
             if (lane == 0) {
@@ -535,28 +508,21 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
       using NoMask = std::integral_constant<bool, false>;
       using Mask = std::integral_constant<bool, true>;
-      // Every body of this size in the loop raises the register pressure of
-      // the whole loop, so a split launch compiles one per kernel: the fast
-      // body (no mask, at most two time buckets, history rows, position
-      // gradient through the diagonal copy) in part 2, the general one
-      // (masks, per-element buckets, position gradient through the window)
-      // in part 1; part 0 holds both.
+      // Two bodies, no more: every body of this size in the loop raises the
+      // register pressure of the whole loop. The fast one (no mask, at most
+      // two time buckets, history rows, position gradient through the
+      // diagonal copy) takes the bulk; the general one (masks, per-element
+      // buckets, position gradient through the diagonal copy in history
+      // tiles and through the window in tiles with candidate rows) the rest.
       using IG = std::conditional_t<WIDE, I3, I2>;
       using PosDiag = std::integral_constant<bool, has_pos>;
-      auto general = [&]() { tile_math(IG(), Mask(), std::false_type()); };
-      if constexpr (PART == 2) {
+      if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
         tile_math(I1(), NoMask(), PosDiag());
-      } else if constexpr (PART == 1) {
-        general();
-      } else {
-        if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
-          tile_math(I1(), NoMask(), PosDiag());
-        else
-          general();
-      }
+      else
+        tile_math(IG(), Mask(), std::false_type());
     } else {
       // This wave's entries of the diagonal copy are zero.
-      if (pos_diag) {
+      if (pos_grad && pos_diag) {
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
@@ -568,7 +534,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     // Every read of this tile's Q and dA' is done: stage the next tile.
     if (more) store_tile();
 
-    if (pos_diag) {
+    if (pos_grad && pos_diag) {
       // Diagonal sums: diagonal dd (query - key + BN - 1 within the tile)
       // gathers the elements whose position bucket is that of offset
       // k0 - q0 + (BN - 1) - dd.
@@ -584,7 +550,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
                     sum);
       }
     }
-    if (has_pos && !pos_diag && tid < C::WIN) {
+    if (pos_grad && !pos_diag && tid < C::WIN) {
       // Flush the position-gradient window of this tile.
       const float gsum = sm.wing[tid];
       if (gsum != 0.f) {
@@ -595,11 +561,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         sm.wing[tid] = 0.f;
       }
     }
-    n = n_next;
   }
 
   // Time-gradient histogram of this workgroup.
-  if constexpr (has_time) {
+  if constexpr (time_grad) {
     __syncthreads();
     for (int x = tid; x < p.n_time_buckets; x += C::NT) {
       float gsum = 0.f;
@@ -608,52 +573,56 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     }
   }
 
-  // dK, dV of this lane's keys (partials in fp32 for part 1): register r
-  // holds key 8(r/4) + 4g + r%4 of the wave, column d = 32 db + l32.
+  // dK, dV of this lane's keys: register r holds key 8(r/4) + 4g + r%4 of
+  // the wave, column d = 32 db + l32.
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jj = jw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (jj < L) {
-        const int64_t o = part_off(db, r);
-        if constexpr (PART == 1) {
-          p.dkv_part[o] = acc_dk[db][r];
-          p.dkv_part[THD + o] = acc_dv[db][r];
-        } else {
-          reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
-          reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
-        }
+        const int64_t o = ((start + jj) * H + head) * (int64_t)D + 32 * db + l32;
+        if constexpr (DK) reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
+        if constexpr (DV) reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
       }
     }
   }
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void hstu_bwd_kernel(AttnParams p) {
-  __shared__ BwdSmem<T, D> sm;
-  const int item = blockIdx.x / p.H;
-  const int head = blockIdx.x - item * p.H;
-  if (item >= *p.n_items) return;
-  const WorkItem wi = p.items[item];
-  const SeqInfo si = p.seq[wi.seq];
-  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  bwd_body<T, D, WIDE, POS, TIME, PART>(p, sm, wi, si, head);
-}
+#define HSTU_BWD_KERNEL(NAME, WAVES)                                                           \
+  template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>                         \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))         \
+  void NAME(AttnParams p) {                                                                    \
+    __shared__ BwdSmem<T, D> sm;                                                               \
+    const int item = blockIdx.x / p.H;                                                         \
+    const int head = blockIdx.x - item * p.H;                                                  \
+    if (item >= *p.n_items) return;                                                            \
+    const WorkItem wi = p.items[item];                                                         \
+    const SeqInfo si = p.seq[wi.seq];                                                          \
+    if (((si.flags & kSeqWideTs) != 0) != WIDE) return; /* the other instantiation takes it */ \
+    bwd_body<T, D, WIDE, POS, TIME, KV>(p, sm, wi, si, head);                                  \
+  }
+// The one-pass form holds dK, dV, K and V in registers: one wave per SIMD.
+// The dV-only and dK-only passes fit two.
+HSTU_BWD_KERNEL(hstu_bwd_kernel, 1)
+HSTU_BWD_KERNEL(hstu_bwd_split_kernel, BWD_KV_WAVES)
+#undef HSTU_BWD_KERNEL
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME, int PART>
+template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>
 void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
-  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME, PART>), g, dim3(256), 0, s, p);
+  if constexpr (KV == 0)
+    hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME, 0>), g, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((hstu_bwd_split_kernel<T, D, WIDE, POS, TIME, KV>), g, dim3(256), 0, s, p);
 }
 
-template <typename T, int D, bool WIDE, int PART>
+template <typename T, int D, bool WIDE, int KV>
 void launch_rab(const AttnParams& p, dim3 g, hipStream_t s) {
   const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
-  if (pos && time) launch_one<T, D, WIDE, true, true, PART>(p, g, s);
-  else if (pos) launch_one<T, D, WIDE, true, false, PART>(p, g, s);
-  else if (time) launch_one<T, D, WIDE, false, true, PART>(p, g, s);
-  else launch_one<T, D, WIDE, false, false, PART>(p, g, s);
+  if (pos && time) launch_one<T, D, WIDE, true, true, KV>(p, g, s);
+  else if (pos) launch_one<T, D, WIDE, true, false, KV>(p, g, s);
+  else if (time) launch_one<T, D, WIDE, false, true, KV>(p, g, s);
+  else launch_one<T, D, WIDE, false, false, KV>(p, g, s);
 }
 
 }  // namespace
@@ -663,10 +632,8 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
   const dim3 g((unsigned)grid);
-  constexpr bool split = bwd_split_shape((int)sizeof(T), D);
-  if (split != bwd_split(p)) return hipErrorInvalidValue;   // workspace carved for the other form
   prof_before(kKBwd, s);
-  if constexpr (split) {
+  if constexpr (bwd_kv_split((int)sizeof(T), D)) {
     launch_rab<T, D, false, 1>(p, g, s);
     launch_rab<T, D, false, 2>(p, g, s);
   } else {

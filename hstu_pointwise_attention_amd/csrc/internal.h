@@ -37,7 +37,6 @@ struct AttnParams {
   WorkItem* items;                   // [max_items]
   int32_t* n_items;                  // [1]
   int32_t* sched_scratch;            // schedule kernel scratch
-  float* dkv_part;                   // [2, T, H, D] fp32 partial dK, dV (split backward)
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
 };
@@ -46,13 +45,13 @@ struct AttnParams {
 // base != nullptr).
 size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
 
-// bf16 at head dim 128 runs the backward as two launches (general tiles,
-// then fast tiles) that meet through fp32 dK / dV partials.
-#ifndef BWD_SPLIT
-#define BWD_SPLIT 0
+// Shapes whose backward computes dV and dK (with the rab gradients) in two
+// key-block passes instead of one: the one-pass kernel then holds too many
+// registers for two waves per SIMD.
+#ifndef BWD_KVSPLIT
+#define BWD_KVSPLIT 0
 #endif
-constexpr bool bwd_split_shape(int elem_bytes, int D) { return BWD_SPLIT && elem_bytes == 2 && D == 128; }
-inline bool bwd_split(const AttnParams& p) { return p.dkv_part != nullptr; }
+constexpr bool bwd_kv_split(int elem_bytes, int D) { return BWD_KVSPLIT && elem_bytes == 2 && D == 128; }
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {

@@ -276,14 +276,7 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.n_items = (int32_t*)take(sizeof(int32_t));
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 3 * NB));
   p.d_a = nullptr;
-  p.dkv_part = nullptr;
-  if (bwd) {
-    p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
-    if (bwd_split_shape(elem_bytes, p.D)) {
-      float* part = (float*)take(2 * sizeof(float) * (size_t)p.T * p.H * p.D);
-      p.dkv_part = part;
-    }
-  }
+  if (bwd) p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
   return off;
 }
 
