@@ -313,6 +313,10 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
               pr = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv));
             }
             if constexpr (MASK) {
+              // pr opaque first: left alone the compiler turns the select
+              // into a branch around the whole element (bias lookups
+              // included), and the elements then run one at a time
+              asm volatile("" : "+v"(pr));
               const int j = j0 + jl;
               const bool ok = j <= i && (j < hist || j == i);
               pr = ok ? pr : 0.f;
