@@ -120,10 +120,29 @@ __device__ __forceinline__ void st4_from_f32(bf16* p, f32x4 v) {
 }
 __device__ __forceinline__ void st4_from_f32(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
+// Sum over the 64 lanes, returned to every lane. DPP adds within each 16-lane
+// row (quad swaps, then half-row and row mirrors) stay in the VALU; the four
+// row sums then come out through readlane. A shuffle ladder would instead make
+// six LDS round trips, each waited on alone.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int x = __builtin_bit_cast(int, v), y;
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: y = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: y = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return v + __builtin_bit_cast(float, y);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  for (int c = 0; c < 4; ++c) v = dpp_add(v, c);
+  const int x = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 48)));
 }
 
 // ---------------------------------------------------------------------------
