@@ -176,8 +176,9 @@ template <typename T>
 hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
   hipError_t e = launch_bwd_pre<T>(p, s);
   if (e == hipSuccess) e = dispatch_bwd<T>(p, s);
-  if (e == hipSuccess) e = launch_schedule(p, 0, s);
-  if (e == hipSuccess) e = dispatch_dq<T>(p, s);
+  AttnParams pq = p;                             // the dQ pass walks query blocks
+  pq.items = p.items_q;
+  if (e == hipSuccess) e = dispatch_dq<T>(pq, s);
   return e;
 }
 
@@ -276,15 +277,17 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   carve_workspace(p, workspace, true, eb);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (p.d_rab_pos)
-    e = launch_fill_f32(p.d_rab_pos, (int64_t)desc->rab_heads * (2 * (int64_t)desc->max_len - 1), 0.f, s);
-  if (e == hipSuccess && p.d_rab_time)
-    e = launch_fill_f32(p.d_rab_time, (int64_t)desc->rab_heads * desc->n_time_buckets, 0.f, s);
-  if (e == hipSuccess && p.T > 0 && p.B > 0) {
-    e = launch_prep(p, s);
-    if (e == hipSuccess) e = launch_schedule(p, 1, s);
+  if (p.T > 0 && p.B > 0) {
+    e = launch_prep(p, s);                       // also clears d_rab_pos / d_rab_time
+    if (e == hipSuccess) e = launch_schedule(p, 2, s);
     if (e == hipSuccess)
       e = desc->dtype == HSTU_DTYPE_BF16 ? run_bwd_main<bf16>(p, s) : run_bwd_main<float>(p, s);
+  } else {
+    // nothing to attend over: the rab gradients are still overwritten
+    if (p.d_rab_pos)
+      e = launch_fill_f32(p.d_rab_pos, (int64_t)desc->rab_heads * (2 * (int64_t)desc->max_len - 1), 0.f, s);
+    if (e == hipSuccess && p.d_rab_time)
+      e = launch_fill_f32(p.d_rab_time, (int64_t)desc->rab_heads * desc->n_time_buckets, 0.f, s);
   }
   if (e != hipSuccess) return hip_fail(e, "hstu_attn_bwd launch");
   return ok();

@@ -35,6 +35,7 @@ struct AttnParams {
   SeqInfo* seq;
   uint32_t* ts_rel;                  // [T] rebased timestamps
   WorkItem* items;                   // [max_items]
+  WorkItem* items_q;                 // [max_items] query-block order (backward only)
   int32_t* n_items;                  // [1]
   int32_t* sched_scratch;            // schedule kernel scratch
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
@@ -63,7 +64,9 @@ void prof_before(int id, hipStream_t s);
 void prof_after(int id, hipStream_t s);
 
 hipError_t launch_prep(const AttnParams& p, hipStream_t s);
-// mode 0: forward order (query block index descending); 1: backward order.
+// mode 0: forward order (query block index descending) into items; 1:
+// backward order into items; 2: backward order into items and forward order
+// into items_q.
 hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s);
 hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, uint16_t* bp,
                             uint8_t* bt, hipStream_t s);

@@ -8,6 +8,7 @@ namespace hstu {
 namespace {
 
 constexpr int kPrepThreads = 256;
+constexpr int kSeqPrepThreads = 1024;
 constexpr int kSchedThreads = 1024;
 
 template <typename V, typename Op>
@@ -34,11 +35,24 @@ struct TsStats { int64_t lo, hi; int32_t sorted; };
 __device__ TsStats ts_stats(const int64_t* ts, int64_t s, int64_t e, int64_t* lds64, int32_t* lds32) {
   int64_t lo = INT64_MAX, hi = INT64_MIN;
   int32_t sorted = 1;
-  for (int64_t t = s + threadIdx.x; t < e; t += blockDim.x) {
-    const int64_t x = ts[t];
-    lo = x < lo ? x : lo;
-    hi = x > hi ? x : hi;
-    if (t > s && ts[t - 1] > x) sorted = 0;
+  // four rounds of loads in flight per step: the loop is latency-bound
+  constexpr int U = 4;
+  for (int64_t t0 = s + threadIdx.x; t0 < e; t0 += U * (int64_t)blockDim.x) {
+    int64_t x[U], y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u * (int64_t)blockDim.x;
+      x[u] = t < e ? ts[t] : 0;
+      y[u] = (t < e && t > s) ? ts[t - 1] : INT64_MIN;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u * (int64_t)blockDim.x < e) {
+        lo = x[u] < lo ? x[u] : lo;
+        hi = x[u] > hi ? x[u] : hi;
+        if (y[u] > x[u]) sorted = 0;
+      }
+    }
   }
   TsStats r;
   r.lo = block_reduce(lo, lds64, MinOp());
@@ -52,10 +66,23 @@ __device__ __forceinline__ bool span_is_wide(int64_t lo, int64_t hi) {
   return (uint64_t)hi - (uint64_t)lo >= 0x7fffffffull;
 }
 
-// One workgroup per sequence: metadata + rebased timestamps.
-__global__ __launch_bounds__(kPrepThreads) void seq_prep_kernel(AttnParams p) {
-  __shared__ int64_t lds64[kPrepThreads / kWave];
-  __shared__ int32_t lds32[kPrepThreads / kWave];
+// One workgroup per sequence: metadata + rebased timestamps. In the backward
+// the workgroups also clear the rab gradient tables (overwritten outputs).
+__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p) {
+  __shared__ int64_t lds64[kSeqPrepThreads / kWave];
+  __shared__ int32_t lds32[kSeqPrepThreads / kWave];
+  {
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if (p.d_rab_pos) {
+      const int64_t n = (int64_t)p.rab_heads * (2 * (int64_t)p.max_len - 1);
+      for (int64_t i = i0; i < n; i += stride) p.d_rab_pos[i] = 0.f;
+    }
+    if (p.d_rab_time) {
+      const int64_t n = (int64_t)p.rab_heads * p.n_time_buckets;
+      for (int64_t i = i0; i < n; i += stride) p.d_rab_time[i] = 0.f;
+    }
+  }
   const int b = blockIdx.x;
   const int64_t s = p.seq_offsets[b];
   const int64_t e = p.seq_offsets[b + 1];
@@ -69,9 +96,22 @@ __global__ __launch_bounds__(kPrepThreads) void seq_prep_kernel(AttnParams p) {
     lo = st.lo;
     if (span_is_wide(st.lo, st.hi)) flags |= kSeqWideTs;
     if (st.sorted) flags |= kSeqSortedTs;
-    if (!(flags & kSeqWideTs))
-      for (int64_t t = s + threadIdx.x; t < e; t += blockDim.x)
-        p.ts_rel[t] = (uint32_t)(p.timestamps[t] - lo);
+    if (!(flags & kSeqWideTs)) {
+      constexpr int U = 4;
+      for (int64_t t0 = s + threadIdx.x; t0 < e; t0 += U * (int64_t)blockDim.x) {
+        int64_t x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t t = t0 + u * (int64_t)blockDim.x;
+          x[u] = t < e ? p.timestamps[t] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t t = t0 + u * (int64_t)blockDim.x;
+          if (t < e) p.ts_rel[t] = (uint32_t)(x[u] - lo);
+        }
+      }
+    }
   }
   if (threadIdx.x == 0) {
     SeqInfo si;
@@ -115,7 +155,8 @@ __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
 // x = 0..n-1 whose cost grows with x (forward: x is the query block index,
 // the causal row block that sees the most keys; backward: x = n-1-key block,
 // the key block that sees the most queries). Items are placed by x
-// descending: start[x] = number of items with a larger x.
+// descending: start[x] = number of items with a larger x. Both orders hold
+// the same multiset of x, so mode 2 places every item in both lists.
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
   __shared__ int lds[kSchedThreads];
   const int B = p.B;
@@ -124,7 +165,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
   int* hist = seq_base + (B + 1);               // [NB]: sequences with n blocks
   int* cnt = hist + NB;                         // [NB]: sequences with more than x blocks
   int* fill = cnt + NB;                         // [NB]
-  for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; }
+  int* fill_q = fill + NB;                      // [NB] (mode 2: forward-order list)
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; fill_q[i] = 0; }
   __syncthreads();
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int n = p.seq[b].nblk;
@@ -159,6 +201,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     w.seq = b;
     w.blk = blk;
     p.items[pos] = w;
+    if (mode == 2) p.items_q[hist[blk] + atomicAdd(&fill_q[blk], 1)] = w;
   }
   if (threadIdx.x == 0) *p.n_items = total;
 }
@@ -220,35 +263,61 @@ __device__ __forceinline__ int seq_of_token(const int64_t* offs, int B, int64_t 
   return lo;
 }
 
-// dA' = dO * U / L (or dO / L without gate), dU = dO * A. Four elements per thread.
+// dA' = dO * U / L (or dO / L without gate), dU = dO * A. Eight elements per
+// thread, so every access is 16 bytes (bf16) or two of them (fp32).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float* f) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) f[m] = (float)v[m];
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float* f) {
+    bf16x8 v;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) v[m] = (bf16)f[m];
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* f) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { f[m] = a[m]; f[4 + m] = b[m]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* f) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnParams p) {
-  const int HD = p.H * p.D;
-  const int64_t n4 = p.T * HD / 4;
-  for (int64_t q4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q4 < n4;
-       q4 += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = q4 * 4;
+  const int HD = p.H * p.D;                      // a multiple of 32
+  const int64_t n8 = p.T * HD / 8;
+  for (int64_t q8 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q8 < n8;
+       q8 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = q8 * 8;
     const int64_t t = e0 / HD;
     const int hd = (int)(e0 - t * HD);
     const float inv = p.seq[seq_of_token(p.seq_offsets, p.B, t)].inv_len;
-    const T* dop = reinterpret_cast<const T*>(p.d_o) + e0;
-    T* dap = reinterpret_cast<T*>(p.d_a) + e0;
-    float go[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) go[m] = to_f32(dop[m]);
+    float go[8], da[8];
+    Vec8<T>::load(reinterpret_cast<const T*>(p.d_o) + e0, go);
     if (p.u != nullptr) {
-      const T* up = reinterpret_cast<const T*>(p.u) + t * p.su + hd;
-      const float* ap = p.a_in + e0;
-      T* dup = reinterpret_cast<T*>(p.du) + e0;
+      float uv[8], av[8], du[8];
+      Vec8<T>::load(reinterpret_cast<const T*>(p.u) + t * p.su + hd, uv);
+      Vec8<float>::load(p.a_in + e0, av);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        dap[m] = from_f32<T>(go[m] * to_f32(up[m]) * inv);
-        dup[m] = from_f32<T>(go[m] * ap[m]);
+      for (int m = 0; m < 8; ++m) {
+        da[m] = go[m] * uv[m] * inv;
+        du[m] = go[m] * av[m];
       }
+      Vec8<T>::store(reinterpret_cast<T*>(p.du) + e0, du);
     } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) dap[m] = from_f32<T>(go[m] * inv);
+      for (int m = 0; m < 8; ++m) da[m] = go[m] * inv;
     }
+    Vec8<T>::store(reinterpret_cast<T*>(p.d_a) + e0, da);
   }
 }
 
@@ -274,16 +343,20 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.ts_rel = (uint32_t*)take(sizeof(uint32_t) * (size_t)(p.T > 0 ? p.T : 1));
   p.items = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
   p.n_items = (int32_t*)take(sizeof(int32_t));
-  p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 3 * NB));
+  p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 4 * NB));
+  p.items_q = nullptr;
   p.d_a = nullptr;
-  if (bwd) p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
+  if (bwd) {
+    p.items_q = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
+    p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
+  }
   return off;
 }
 
 hipError_t launch_prep(const AttnParams& p, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   prof_before(kKPrep, s);
-  hipLaunchKernelGGL(seq_prep_kernel, dim3(p.B), dim3(kPrepThreads), 0, s, p);
+  hipLaunchKernelGGL(seq_prep_kernel, dim3(p.B), dim3(kSeqPrepThreads), 0, s, p);
   prof_after(kKPrep, s);
   return hipGetLastError();
 }
@@ -315,10 +388,10 @@ hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s) {
-  const int64_t n4 = p.T * p.H * p.D / 4;
-  if (n4 == 0) return hipSuccess;
+  const int64_t n8 = p.T * p.H * p.D / 8;
+  if (n8 == 0) return hipSuccess;
   prof_before(kKBwdPre, s);
-  hipLaunchKernelGGL(bwd_pre_kernel<T>, dim3(grid_for(n4, 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_pre_kernel<T>, dim3(grid_for(n8, 256)), dim3(256), 0, s, p);
   prof_after(kKBwdPre, s);
   return hipGetLastError();
 }
