@@ -598,13 +598,28 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))         \
   void NAME(AttnParams p) {                                                                    \
     __shared__ BwdSmem<T, D> sm;                                                               \
-    const int item = blockIdx.x / p.H;                                                         \
-    const int head = blockIdx.x - item * p.H;                                                  \
-    if (item >= *p.n_items) return;                                                            \
-    const WorkItem wi = p.items[item];                                                         \
-    const SeqInfo si = p.seq[wi.seq];                                                          \
-    if (((si.flags & kSeqWideTs) != 0) != WIDE) return; /* the other instantiation takes it */ \
-    bwd_body<T, D, WIDE, POS, TIME, KV>(p, sm, wi, si, head);                                  \
+    if constexpr (WIDE) {                                                                      \
+      /* rare sequences needing 64-bit timestamps: a small grid walks the work slots */        \
+      if (p.n_items[1] == 0) return;                                                           \
+      const int64_t slots = (int64_t)*p.n_items * p.H;                                         \
+      for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {                                \
+        const int item = (int)(w / p.H);                                                       \
+        const int head = (int)(w - (int64_t)item * p.H);                                       \
+        const WorkItem wi = p.items[item];                                                     \
+        const SeqInfo si = p.seq[wi.seq];                                                      \
+        if ((si.flags & kSeqWideTs) == 0) continue;                                            \
+        bwd_body<T, D, true, POS, TIME, KV>(p, sm, wi, si, head);                              \
+        __syncthreads(); /* the next slot reuses the LDS */                                    \
+      }                                                                                        \
+    } else {                                                                                   \
+      const int item = blockIdx.x / p.H;                                                       \
+      const int head = blockIdx.x - item * p.H;                                                \
+      if (item >= *p.n_items) return;                                                          \
+      const WorkItem wi = p.items[item];                                                       \
+      const SeqInfo si = p.seq[wi.seq];                                                        \
+      if ((si.flags & kSeqWideTs) != 0) return; /* the other instantiation takes it */         \
+      bwd_body<T, D, false, POS, TIME, KV>(p, sm, wi, si, head);                               \
+    }                                                                                          \
   }
 // The one-pass form holds dK, dV, K and V in registers: one wave per SIMD.
 // The dV-only and dK-only passes fit two.
@@ -645,8 +660,9 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   }
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
   if (p.rab_time != nullptr) {
-    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true, 0>(p, g, s);
-    else launch_one<T, D, true, false, true, 0>(p, g, s);
+    const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
+    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true, 0>(p, gw, s);
+    else launch_one<T, D, true, false, true, 0>(p, gw, s);
   }
   prof_after(kKBwd, s);
   return hipGetLastError();

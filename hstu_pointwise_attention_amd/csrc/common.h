@@ -156,7 +156,7 @@ __device__ __forceinline__ int pos_bucket(int rel, int max_len) {
   return rel + lim;
 }
 
-// Rebased timestamps (offsets from the sequence minimum) below 2^31 - 1:
+// Rebased timestamps (offsets from a per-sequence origin) in [0, 2^31 - 1):
 // |a - b| + 1 <= 2^31 - 1 cannot overflow.
 __device__ __forceinline__ int time_bucket_rel(uint32_t a, uint32_t b, int last) {
   const uint32_t d = (a > b ? a - b : b - a) + 1u;
@@ -184,7 +184,7 @@ struct SeqInfo {
   int32_t flags;    // kSeqWideTs | kSeqSortedTs
   float inv_len;    // 1 / L (0 for L == 0)
   int32_t nblk;     // ceil(L / 128): query blocks (forward) = key blocks (backward)
-  int64_t ts_min;   // smallest timestamp (rebasing origin)
+  int64_t ts_origin;  // rebasing origin of the 32-bit timestamps
 };
 static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
 

@@ -405,26 +405,58 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
-  const int item = blockIdx.x / p.H;
-  const int head = blockIdx.x - item * p.H;
-  if (item >= *p.n_items) return;
-  const WorkItem wi = p.items[item];
-  const SeqInfo si = p.seq[wi.seq];
-  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;   // the other instantiation takes it
-  fwd_body<T, D, WIDE, POS, TIME, false>(p, sm, wi, si, head);
+  if constexpr (WIDE) {
+    // sequences needing 64-bit timestamps are rare: a small grid walks the
+    // work slots and takes only theirs
+    if (p.n_items[1] == 0) return;
+    const int64_t slots = (int64_t)*p.n_items * p.H;
+    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
+      const int item = (int)(w / p.H);
+      const int head = (int)(w - (int64_t)item * p.H);
+      const WorkItem wi = p.items[item];
+      const SeqInfo si = p.seq[wi.seq];
+      if ((si.flags & kSeqWideTs) == 0) continue;
+      fwd_body<T, D, true, POS, TIME, false>(p, sm, wi, si, head);
+      __syncthreads();                             // the next slot reuses the LDS
+    }
+  } else {
+    const int item = blockIdx.x / p.H;
+    const int head = blockIdx.x - item * p.H;
+    if (item >= *p.n_items) return;
+    const WorkItem wi = p.items[item];
+    const SeqInfo si = p.seq[wi.seq];
+    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+    fwd_body<T, D, false, POS, TIME, false>(p, sm, wi, si, head);
+  }
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQ_WAVES, DQ_WAVES)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
-  const int item = blockIdx.x / p.H;
-  const int head = blockIdx.x - item * p.H;
-  if (item >= *p.n_items) return;
-  const WorkItem wi = p.items[item];
-  const SeqInfo si = p.seq[wi.seq];
-  if (((si.flags & kSeqWideTs) != 0) != WIDE) return;
-  fwd_body<T, D, WIDE, POS, TIME, true>(p, sm, wi, si, head);
+  if constexpr (WIDE) {
+    // sequences needing 64-bit timestamps are rare: a small grid walks the
+    // work slots and takes only theirs
+    if (p.n_items[1] == 0) return;
+    const int64_t slots = (int64_t)*p.n_items * p.H;
+    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
+      const int item = (int)(w / p.H);
+      const int head = (int)(w - (int64_t)item * p.H);
+      const WorkItem wi = p.items[item];
+      const SeqInfo si = p.seq[wi.seq];
+      if ((si.flags & kSeqWideTs) == 0) continue;
+      fwd_body<T, D, true, POS, TIME, true>(p, sm, wi, si, head);
+      __syncthreads();                             // the next slot reuses the LDS
+    }
+  } else {
+    const int item = blockIdx.x / p.H;
+    const int head = blockIdx.x - item * p.H;
+    if (item >= *p.n_items) return;
+    const WorkItem wi = p.items[item];
+    const SeqInfo si = p.seq[wi.seq];
+    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+    fwd_body<T, D, false, POS, TIME, true>(p, sm, wi, si, head);
+  }
 }
 
 template <bool GRAD, typename T, int D, bool WIDE, bool POS, bool TIME>
@@ -448,8 +480,9 @@ hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
   else launch_one<GRAD, T, D, false, false, false>(p, g, s);
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
   if (time) {
-    if (pos) launch_one<GRAD, T, D, true, true, true>(p, g, s);
-    else launch_one<GRAD, T, D, true, false, true>(p, g, s);
+    const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
+    if (pos) launch_one<GRAD, T, D, true, true, true>(p, gw, s);
+    else launch_one<GRAD, T, D, true, false, true>(p, gw, s);
   }
   prof_after(id, s);
   return hipGetLastError();

@@ -36,7 +36,7 @@ struct AttnParams {
   uint32_t* ts_rel;                  // [T] rebased timestamps
   WorkItem* items;                   // [max_items]
   WorkItem* items_q;                 // [max_items] query-block order (backward only)
-  int32_t* n_items;                  // [1]
+  int32_t* n_items;                  // [2]: items, sequences that need 64-bit timestamps
   int32_t* sched_scratch;            // schedule kernel scratch
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
@@ -53,6 +53,10 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
 #define BWD_KVSPLIT 0
 #endif
 constexpr bool bwd_kv_split(int elem_bytes, int D) { return BWD_KVSPLIT && elem_bytes == 2 && D == 128; }
+
+// Grid of the attention kernels' 64-bit-timestamp instantiations, which walk
+// the work slots of the (rare) sequences that need them.
+constexpr int kWideGrid = 512;
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {

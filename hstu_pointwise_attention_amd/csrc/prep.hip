@@ -90,28 +90,43 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p)
   int nt = p.num_targets ? (int)p.num_targets[b] : 0;
   nt = nt < 0 ? 0 : (nt > L ? L : nt);
   int flags = 0;
-  int64_t lo = 0;
+  int64_t origin = 0;
   if (p.timestamps != nullptr && L > 0) {
-    TsStats st = ts_stats(p.timestamps, s, e, lds64, lds32);
-    lo = st.lo;
-    if (span_is_wide(st.lo, st.hi)) flags |= kSeqWideTs;
-    if (st.sorted) flags |= kSeqSortedTs;
-    if (!(flags & kSeqWideTs)) {
-      constexpr int U = 4;
-      for (int64_t t0 = s + threadIdx.x; t0 < e; t0 += U * (int64_t)blockDim.x) {
-        int64_t x[U];
+    // One pass: the timestamps relative to origin = first - 2^30 (known
+    // before the pass, unlike the minimum), then min, max and sortedness.
+    // The 32-bit form is exact when every relative value lies in
+    // [0, 2^31 - 1), i.e. the sequence stays within 2^30 s before its first
+    // timestamp and spans less than that range; otherwise the sequence is
+    // flagged wide and the kernels use the 64-bit timestamps.
+    origin = p.timestamps[s] - ((int64_t)1 << 30);
+    int64_t lo = INT64_MAX, hi = INT64_MIN;
+    int32_t sorted = 1;
+    constexpr int U = 4;                         // loads in flight per step
+    for (int64_t t0 = s + threadIdx.x; t0 < e; t0 += U * (int64_t)blockDim.x) {
+      int64_t x[U], y[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t t = t0 + u * (int64_t)blockDim.x;
-          x[u] = t < e ? p.timestamps[t] : 0;
-        }
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        x[u] = t < e ? p.timestamps[t] : 0;
+        y[u] = (t < e && t > s) ? p.timestamps[t - 1] : INT64_MIN;
+      }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t t = t0 + u * (int64_t)blockDim.x;
-          if (t < e) p.ts_rel[t] = (uint32_t)(x[u] - lo);
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + u * (int64_t)blockDim.x;
+        if (t < e) {
+          lo = x[u] < lo ? x[u] : lo;
+          hi = x[u] > hi ? x[u] : hi;
+          if (y[u] > x[u]) sorted = 0;
+          p.ts_rel[t] = (uint32_t)(x[u] - origin);
         }
       }
     }
+    lo = block_reduce(lo, lds64, MinOp());
+    hi = block_reduce(hi, lds64, MaxOp());
+    sorted = block_reduce(sorted, lds32, AndOp());
+    const bool narrow = lo >= origin && (uint64_t)hi - (uint64_t)origin < 0x7fffffffull;
+    if (!narrow) flags |= kSeqWideTs;
+    if (sorted) flags |= kSeqSortedTs;
   }
   if (threadIdx.x == 0) {
     SeqInfo si;
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p)
     si.flags = flags;
     si.inv_len = L > 0 ? 1.0f / (float)L : 0.0f;
     si.nblk = (L + kBlk - 1) / kBlk;
-    si.ts_min = lo;
+    si.ts_origin = origin;
     p.seq[b] = si;
   }
 }
@@ -157,22 +172,33 @@ __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
 // the key block that sees the most queries). Items are placed by x
 // descending: start[x] = number of items with a larger x. Both orders hold
 // the same multiset of x, so mode 2 places every item in both lists.
+// Its arrays live in LDS when they fit (every access is then a short LDS
+// round trip instead of a global one), else in the workspace scratch.
+constexpr int kSchedLds = 6144;
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
   __shared__ int lds[kSchedThreads];
+  __shared__ int small[kSchedLds];
   const int B = p.B;
   const int NB = (int)(p.T / kBlk) + 2;       // x ranges over [0, NB)
-  int* seq_base = p.sched_scratch;              // [B + 1]
+  int* seq_base = (B + 1 + 4 * NB <= kSchedLds) ? small : p.sched_scratch;   // [B + 1]
   int* hist = seq_base + (B + 1);               // [NB]: sequences with n blocks
   int* cnt = hist + NB;                         // [NB]: sequences with more than x blocks
   int* fill = cnt + NB;                         // [NB]
   int* fill_q = fill + NB;                      // [NB] (mode 2: forward-order list)
   for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; fill_q[i] = 0; }
   __syncthreads();
+  if (threadIdx.x == 0) lds[0] = 0;
+  __syncthreads();
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int n = p.seq[b].nblk;
+    const SeqInfo si = p.seq[b];
+    const int n = si.nblk;
     seq_base[b] = n;
     atomicAdd(&hist[n < NB ? n : NB - 1], 1);
+    if (si.flags & kSeqWideTs) atomicAdd(&lds[0], 1);
   }
+  __syncthreads();
+  if (threadIdx.x == 0) p.n_items[1] = lds[0];
   __syncthreads();
   const int total = block_scan_excl(seq_base, B, false, lds);
   if (threadIdx.x == 0) seq_base[B] = total;
@@ -342,7 +368,7 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.seq = (SeqInfo*)take(sizeof(SeqInfo) * (size_t)(p.B > 0 ? p.B : 1));
   p.ts_rel = (uint32_t*)take(sizeof(uint32_t) * (size_t)(p.T > 0 ? p.T : 1));
   p.items = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
-  p.n_items = (int32_t*)take(sizeof(int32_t));
+  p.n_items = (int32_t*)take(2 * sizeof(int32_t));
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 4 * NB));
   p.items_q = nullptr;
   p.d_a = nullptr;

@@ -117,6 +117,45 @@ def test_random_small_sweep(dtype, seed):
     _run_parity(inp, tag=f"{dtype} seed {seed} H{H} D{D} L{list(lengths)}")
 
 
+def _timestamps(kind, offs, rng):
+    """Per-sequence timestamps of one kind (int64 seconds)."""
+    T = int(offs[-1])
+    i64 = np.iinfo(np.int64)
+    if kind == "unsorted":
+        return rng.integers(-10 ** 6, 10 ** 6, size=T)
+    if kind == "wide":                                   # spans wider than 2^31: 64-bit buckets
+        return np.sort(rng.integers(0, 1 << 40, size=T))
+    if kind == "extreme":
+        return np.array(([i64.min, i64.max] * T)[:T], dtype=np.int64)
+    if kind == "ties":
+        return np.full(T, 1_700_000_000, dtype=np.int64)
+    out = np.zeros(T, dtype=np.int64)
+    for b in range(len(offs) - 1):
+        s, e = int(offs[b]), int(offs[b + 1])
+        seq = 1_700_000_000 + np.cumsum(rng.integers(0, 4000, size=e - s))
+        if kind == "before_first" and e - s > 2:      # one value 2^30 + 5 s before the first
+            seq[(e - s) // 2] = seq[0] - (1 << 30) - 5
+        if kind == "mixed" and b % 2 == 1:             # every other sequence needs 64 bits
+            seq = seq + np.arange(e - s, dtype=np.int64) * (1 << 28)
+        out[s:e] = seq
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("kind", ["unsorted", "wide", "extreme", "ties", "before_first", "mixed"])
+def test_timestamp_kinds(dtype, kind):
+    """Timestamps off the sorted 32-bit fast paths, through forward and backward: unsorted and
+    negative, spans past 2^31 (the 64-bit bucket kernels), extreme int64 values, all ties, a
+    value more than 2^30 s before the first one, and a batch mixing both kernel kinds."""
+    lengths = (5, 0, 70, 1, 130, 200)
+    D = 64 if dtype == "fp32" else 128
+    w = W.AttnWorkload("tskinds", 31, len(lengths), 2, D, D, 256, 128, True, dtype, "fixed",
+                       lengths)
+    inp = W.make_attention_inputs(w)
+    inp["timestamps"] = _timestamps(kind, inp["seq_offsets"], np.random.default_rng(77)).astype(np.int64)
+    _run_parity(inp, tag=f"{dtype} {kind}")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_edge_lengths(dtype):
     """Empty sequences, L=1, exactly one tile, one past a tile, all-candidate sequences."""
