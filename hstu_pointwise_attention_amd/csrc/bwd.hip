@@ -291,7 +291,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // bound it: at most two adjacent buckets, split by a per-key threshold
       // (mode 1; a single bucket is the case of a threshold no query
       // reaches). Everything else takes per-element buckets (mode 2).
-      int tmode = 2, b_lo = 0, b_hi = 0;
+      int tmode = has_time ? 2 : 1, b_lo = 0, b_hi = 0;   // no time bias: one "bucket"
       uint32_t thr = 0;
       if (has_time && !wide && !need_mask && sorted_ts) {
         const int qi_hi = min(q0 + C::BM - 1, L - 1) - q0;
@@ -346,9 +346,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         constexpr int TM = decltype(tm)::value;
         constexpr bool MASK = decltype(mk)::value;
         constexpr bool PD = decltype(pd)::value;
-        // TM 1: two buckets split at a per-key threshold; 2: per-element
-        // buckets of rebased timestamps; 3: of raw 64-bit timestamps.
-        const float tb_lo = (TM == 1 && has_time) ? sm.ttab[b_lo] : 0.f;
+        // TM 0: one bucket for the whole sub-tile; 1: two buckets split at a
+        // per-key threshold; 2: per-element buckets of rebased timestamps; 3:
+        // of raw 64-bit timestamps.
+        const float tb_lo = (TM <= 1 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1 && has_time) ? sm.ttab[b_hi] : 0.f;
         float g_all = 0.f, g_hi = 0.f;
         // Per-element buckets: the gradient of the lane's four largest
@@ -400,7 +401,9 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             int bt = 0;
             bool hi = false;
             if constexpr (has_time) {
-              if constexpr (TM == 1) {
+              if constexpr (TM == 0) {
+                s += tb_lo;
+              } else if constexpr (TM == 1) {
                 hi = (uint32_t)sm.tsq[ql] >= thr;
                 s += hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
@@ -422,10 +425,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             acc_s[r] = sl;
             if constexpr (DK) acc_p[r] = ds;
             bts[r] = bt;
-            if constexpr (TM == 1 && time_grad) {
-              g_all += ds;
-              g_hi += hi ? ds : 0.f;
-            }
+            if constexpr (TM <= 1 && time_grad) g_all += ds;
+            if constexpr (TM == 1 && time_grad) g_hi += hi ? ds : 0.f;
           }
           // Side effects after all the block's LDS reads: the compiler cannot
           // move a table read above an LDS write it cannot disambiguate, so
@@ -508,15 +509,21 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       using I3 = std::integral_constant<int, 3>;   // 64-bit timestamps
       using NoMask = std::integral_constant<bool, false>;
       using Mask = std::integral_constant<bool, true>;
-      // Two bodies, no more: every body of this size in the loop raises the
-      // register pressure of the whole loop. The fast one (no mask, at most
-      // two time buckets, history rows, position gradient through the
-      // diagonal copy) takes the bulk; the general one (masks, per-element
-      // buckets, position gradient through the diagonal copy in history
-      // tiles and through the window in tiles with candidate rows) the rest.
+      // Three bodies: every body of this size in the loop raises the register
+      // pressure of the whole loop, so only shapes that pay for themselves
+      // get one. The fast ones (no mask, history rows, position gradient
+      // through the diagonal copy) take the bulk: one time bucket (most
+      // tiles away from the diagonal: a constant bias, one gradient sum) or
+      // two. The general one (masks, per-element buckets, position gradient
+      // through the diagonal copy in history tiles and through the window in
+      // tiles with candidate rows) takes the rest.
+      using I0 = std::integral_constant<int, 0>;
       using IG = std::conditional_t<WIDE, I3, I2>;
       using PosDiag = std::integral_constant<bool, has_pos>;
-      if (!WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag))
+      const bool fast = !WIDE && !need_mask && tmode == 1 && (!has_pos || pos_diag);
+      if (fast && b_hi == b_lo)
+        tile_math(I0(), NoMask(), PosDiag());
+      else if (fast)
         tile_math(I1(), NoMask(), PosDiag());
       else
         tile_math(IG(), Mask(), std::false_type());
