@@ -145,9 +145,9 @@ hipError_t dispatch_bwd(const AttnParams& p, hipStream_t s) {
 template <>
 hipError_t dispatch_bwd<bf16>(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
-    case 32: return launch_bwd<bf16, 32>(p, s);
-    case 64: return launch_bwd<bf16, 64>(p, s);
-    case 128: return launch_bwd<bf16, 128>(p, s);
+    case 32: return BWD_K16 ? launch_bwd_k16<32>(p, s) : launch_bwd<bf16, 32>(p, s);
+    case 64: return BWD_K16 ? launch_bwd_k16<64>(p, s) : launch_bwd<bf16, 64>(p, s);
+    case 128: return BWD_K16 ? launch_bwd_k16<128>(p, s) : launch_bwd<bf16, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

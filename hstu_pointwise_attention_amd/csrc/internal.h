@@ -79,6 +79,12 @@ template <typename T, int D> hipError_t launch_fwd(const AttnParams& p, hipStrea
 // Backward: launch_bwd computes dK, dV and the rab gradients per key block;
 // launch_dq computes dQ per query block (schedule mode 0, like the forward).
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);
+// The same for bf16 with eight waves of 16 keys, two per SIMD
+// (bwd_k16.hip); BWD_K16 = 0 selects launch_bwd<bf16, D> instead.
+template <int D> hipError_t launch_bwd_k16(const AttnParams& p, hipStream_t s);
+#ifndef BWD_K16
+#define BWD_K16 1
+#endif
 template <typename T, int D> hipError_t launch_dq(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
