@@ -21,10 +21,11 @@ namespace hstu {
 
 namespace {
 
-template <int D> struct K16Ld;
-template <> struct K16Ld<32> { static constexpr int Q = 56; };
-template <> struct K16Ld<64> { static constexpr int Q = 72; };
-template <> struct K16Ld<128> { static constexpr int Q = 152; };
+// Row stride (elements) of the staged Q and dA' tiles: D + 16 keeps both
+// read patterns (16-row fragments of 16 bytes, and transposed reads of
+// 4-row x 32-byte blocks per 16 lanes) free of bank conflicts; measured,
+// strides of D + 8 or D + 24 take about 1.7x as long per byte.
+template <int D> struct K16Ld { static constexpr int Q = D + 16; };
 
 template <int D>
 struct K16Cfg {
@@ -245,36 +246,39 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
                           : time_bucket_wide(sm.tsq[q_hi], ts_j, t_last);
         }
         const bool to_copy = has_pos && (PD || pos_diag);
+        // per 32-query chunk: S, dP (sp), the elementwise step and the rab
+        // gradient side effects (ew), dV, dK (kv)
+        f32x4 acc_s[2][2], acc_p[2][2];              // [chunk][16-query block]
+        auto sp = [&](const int kc) {
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {             // 32-query chunks
-          f32x4 acc_s[2], acc_p[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {               // 16-query blocks
+          for (int h = 0; h < 2; ++h) {
             const int qb = 2 * kc + h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc_p[h][r] = 0.f;
+            for (int r = 0; r < 4; ++r) acc_p[kc][h][r] = 0.f;
             if constexpr (PD) {
               const float* w = sm.win + (C::BN - 1 - jl) + 16 * qb + 4 * q4;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc_s[h][r] = w[r];
+              for (int r = 0; r < 4; ++r) acc_s[kc][h][r] = w[r];
             } else if constexpr (has_pos) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int ql = 16 * qb + 4 * q4 + r;
-                acc_s[h][r] = sm.win[(C::BN - 1 - jl) + min(q0 + ql, hist) - p_min];
+                acc_s[kc][h][r] = sm.win[(C::BN - 1 - jl) + min(q0 + ql, hist) - p_min];
               }
             } else {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc_s[h][r] = 0.f;
+              for (int r = 0; r < 4; ++r) acc_s[kc][h][r] = 0.f;
             }
 #pragma unroll
             for (int c = 0; c < C::DK; ++c) {
               const F a = ld_frag(sm.qs + (16 * qb + l16) * C::Q_LD + 32 * c + 8 * q4);
-              mfma16(acc_s[h], a, kf[c]);
+              mfma16(acc_s[kc][h], a, kf[c]);
               const F b = ld_frag(sm.das + (16 * qb + l16) * C::Q_LD + 32 * c + 8 * q4);
-              mfma16(acc_p[h], b, vf[c]);
+              mfma16(acc_p[kc][h], b, vf[c]);
             }
           }
+        };
+        auto ew = [&](const int kc, F& sf, F& df) {
           int bts[8];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -282,7 +286,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
             for (int r = 0; r < 4; ++r) {
               const int ql = 32 * kc + 16 * h + 4 * q4 + r;
               const int i = q0 + ql;
-              float s = acc_s[h][r];
+              float s = acc_s[kc][h][r];
               int bt = 0;
               bool hi = false;
               if constexpr (has_time) {
@@ -301,14 +305,14 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
               }
               const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
               float sl = s * sg;
-              float ds = acc_p[h][r] * (sg + __builtin_fmaf(-sl, sg, sl));
+              float ds = acc_p[kc][h][r] * (sg + __builtin_fmaf(-sl, sg, sl));
               if constexpr (MASK) {
                 const bool ok = j <= i && (j < hist || j == i) && i < L;
                 sl = ok ? sl : 0.f;
                 ds = ok ? ds : 0.f;
               }
-              acc_s[h][r] = sl;
-              acc_p[h][r] = ds;
+              acc_s[kc][h][r] = sl;
+              acc_p[kc][h][r] = ds;
               bts[4 * h + r] = bt;
               if constexpr (TM <= 1 && has_time) g_all += ds;
               if constexpr (TM == 1 && has_time) g_hi += hi ? ds : 0.f;
@@ -318,7 +322,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float ds = acc_p[h][r];
+              const float ds = acc_p[kc][h][r];
               if constexpr (has_pos && !PD) {
                 if (!pos_diag) {
                   const int i = q0 + 32 * kc + 16 * h + 4 * q4 + r;
@@ -336,20 +340,28 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
             }
           // s^T and dS^T as A operands: slots 0..3 the first block's
           // queries, 4..7 the second's (the k-major reads pair them alike)
-          F sf, df;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sf[r] = (bf16)acc_s[0][r];
-            sf[4 + r] = (bf16)acc_s[1][r];
-            df[r] = (bf16)acc_p[0][r];
-            df[4 + r] = (bf16)acc_p[1][r];
+            sf[r] = (bf16)acc_s[kc][0][r];
+            sf[4 + r] = (bf16)acc_s[kc][1][r];
+            df[r] = (bf16)acc_p[kc][0][r];
+            df[4 + r] = (bf16)acc_p[kc][1][r];
           }
+        };
+        auto kv = [&](const int kc, const F& sf, const F& df) {
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
             mfma16(acc_dv[db], sf, ld_frag_kmajor16(sm.das, C::Q_LD, 16 * db, 32 * kc, 32 * kc + 16));
             mfma16(acc_dk[db], df, ld_frag_kmajor16(sm.qs, C::Q_LD, 16 * db, 32 * kc, 32 * kc + 16));
           }
-        }
+        };
+        F sf0, df0, sf1, df1;
+        sp(0);
+        ew(0, sf0, df0);
+        kv(0, sf0, df0);
+        sp(1);
+        ew(1, sf1, df1);
+        kv(1, sf1, df1);
         if constexpr (has_time && TM >= 2) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)

@@ -31,16 +31,37 @@ namespace hstu {
 
 namespace {
 
-// Row strides (elements) of the LDS tiles. K is read with 16-byte row
-// fragments (conflict-free when the stride is an odd multiple of 16 bytes);
-// V is read with transpose reads, four consecutive rows of 32 bytes per
-// 16-lane group, conflict-free when consecutive rows start >= 8 banks apart.
+// Row strides (elements) of the LDS tiles. The tile read by 16-byte row
+// fragments (K forward, V gradient) runs at full LDS rate with a stride of
+// D + 8. The tile read by transpose reads (V forward, K gradient, which
+// also takes row fragments) does not at any plain stride near D (measured:
+// about 110 B/clk per CU against 170-200 for the other patterns), so for
+// D = 128 its rows are stored permuted (P) at stride D + 8, which serves
+// both read patterns at 170-200 B/clk.
 template <typename T, int D> struct FwdLd;
-template <> struct FwdLd<bf16, 32> { static constexpr int K = 40, V = 56; };
-template <> struct FwdLd<bf16, 64> { static constexpr int K = 72, V = 72; };
-template <> struct FwdLd<bf16, 128> { static constexpr int K = 136, V = 152; };
-template <> struct FwdLd<float, 32> { static constexpr int K = 36, V = 36; };
-template <> struct FwdLd<float, 64> { static constexpr int K = 68, V = 68; };
+template <> struct FwdLd<bf16, 32> { static constexpr int K = 40, V = 56; static constexpr bool P = false; };
+template <> struct FwdLd<bf16, 64> { static constexpr int K = 72, V = 72; static constexpr bool P = false; };
+template <> struct FwdLd<bf16, 128> { static constexpr int K = 136, V = 136; static constexpr bool P = true; };
+template <> struct FwdLd<float, 32> { static constexpr int K = 36, V = 36; static constexpr bool P = false; };
+template <> struct FwdLd<float, 64> { static constexpr int K = 68, V = 68; static constexpr bool P = false; };
+
+// P: the tile read by transposed reads (V forward, K gradient) stores row r
+// at row_perm(r), which swaps the two 2-bit fields of r's low four bits.
+__device__ __forceinline__ int row_perm(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// ld_frag_kmajor of rows kr..kr+15 (kr a multiple of 16) stored permuted by
+// row_perm: row kr + 4 g + s' sits at kr + 4 s' + g, row kr + 8 + 4 g + s'
+// at kr + 4 s' + g + 2.
+__device__ __forceinline__ bf16x8 ld_frag_kmajor_perm(const bf16* X, int ld, int n0, int kr) {
+  const int l = threadIdx.x & 63, s = l & 15, g = l >> 5;
+  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+  const bf16* p0 = X + (kr + 4 * (s >> 2) + g) * ld + col;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 2 * ld));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
 
 // GRAD: the query-block pass of the backward, which computes dQ with the
 // same tiling (see the comment of fwd_body).
@@ -59,6 +80,8 @@ struct FwdCfg {
   // K^T dS^T) and V only by rows, so the two strides swap.
   static constexpr int K_LD = GRAD ? FwdLd<T, D>::V : FwdLd<T, D>::K;
   static constexpr int V_LD = GRAD ? FwdLd<T, D>::K : FwdLd<T, D>::V;
+  static constexpr bool K_PERM = GRAD && FwdLd<T, D>::P;   // K rows stored permuted
+  static constexpr bool V_PERM = !GRAD && FwdLd<T, D>::P;  // V rows stored permuted
   static constexpr int WIN = BN + BM;            // position-bias window (>= BN + BM - 1)
   static constexpr int CH = BN * CPR / NT;       // 16-byte chunks per thread per tile (K or V)
   static constexpr int MAX_TIME = 1024;
@@ -192,8 +215,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     for (int m = 0; m < C::CH; ++m) {
       const int ch = tid + C::NT * m;
       const int row = ch / C::CPR, cc = ch % C::CPR;
-      st16(sm.k[buf] + row * C::K_LD + cc * C::VPC, kreg[m]);
-      st16(sm.v[buf] + row * C::V_LD + cc * C::VPC, vreg[m]);
+      st16(sm.k[buf] + (C::K_PERM ? row_perm(row) : row) * C::K_LD + cc * C::VPC, kreg[m]);
+      st16(sm.v[buf] + (C::V_PERM ? row_perm(row) : row) * C::V_LD + cc * C::VPC, vreg[m]);
     }
     if (has_time && tid < C::BN) sm.ts[buf][tid] = tsreg;
     if (has_pos && tid < C::WIN) sm.win[buf][tid] = winreg;
@@ -255,7 +278,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
         for (int c = 0; c < C::KC; ++c) {
-          const F a = ld_frag(ks + (32 * kb + l32) * C::K_LD + 16 * c + 8 * g);
+          const F a = ld_frag(ks + (32 * kb + (C::K_PERM ? row_perm(l32) : l32)) * C::K_LD + 16 * c + 8 * g);
           mfma_32x32x16(acc, a, qf[c]);
           if constexpr (GRAD) {
             const F b = ld_frag(vs + (32 * kb + l32) * C::V_LD + 16 * c + 8 * g);
@@ -330,8 +353,15 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
               // forward: O^T += V^T P^T; gradient: dQ^T += K^T dS^T
-              const F a = GRAD ? ld_frag_kmajor(ks, C::K_LD, 32 * db, kr, kr + 8)
-                               : ld_frag_kmajor(vs, C::V_LD, 32 * db, kr, kr + 8);
+              F a;
+              if constexpr (C::K_PERM)
+                a = ld_frag_kmajor_perm(ks, C::K_LD, 32 * db, kr);
+              else if constexpr (GRAD)
+                a = ld_frag_kmajor(ks, C::K_LD, 32 * db, kr, kr + 8);
+              else if constexpr (C::V_PERM)
+                a = ld_frag_kmajor_perm(vs, C::V_LD, 32 * db, kr);
+              else
+                a = ld_frag_kmajor(vs, C::V_LD, 32 * db, kr, kr + 8);
               mfma_32x32x16(acc_o[db], a, pf);
             }
           }
