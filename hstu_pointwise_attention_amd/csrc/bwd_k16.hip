@@ -317,7 +317,19 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
               if constexpr (TM <= 1 && has_time) g_all += ds;
               if constexpr (TM == 1 && has_time) g_hi += hi ? ds : 0.f;
             }
-          // side effects after the chunk's LDS reads
+          // s^T and dS^T as A operands: slots 0..3 the first block's
+          // queries, 4..7 the second's (the k-major reads pair them alike)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sf[r] = (bf16)acc_s[kc][0][r];
+            sf[4 + r] = (bf16)acc_s[kc][1][r];
+            df[r] = (bf16)acc_p[kc][0][r];
+            df[4 + r] = (bf16)acc_p[kc][1][r];
+          }
+          // side effects after the chunk's LDS reads; the dS copy stores the
+          // halves of df's words (opaque, so that they are not converted again)
+          asm volatile("" : "+v"(df));
+          const u32x4 dfw = __builtin_bit_cast(u32x4, df);
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -335,18 +347,12 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
                 for (int w = 0; w < 4; ++w) gw[w] += k == w ? ds : 0.f;
                 if ((unsigned)k >= 4u && ds != 0.f) atomicAdd(thist_lane + bts[4 * h + r], ds);
               }
-              if (to_copy)
-                dsd_lane[(32 * kc + 16 * h + r) * (C::DG_LD + 1)] = (bf16)ds;
+              if (to_copy) {
+                const uint32_t w = dfw[2 * h + (r >> 1)];
+                reinterpret_cast<uint16_t*>(dsd_lane)[(32 * kc + 16 * h + r) * (C::DG_LD + 1)] =
+                    (uint16_t)((r & 1) ? (w >> 16) : w);
+              }
             }
-          // s^T and dS^T as A operands: slots 0..3 the first block's
-          // queries, 4..7 the second's (the k-major reads pair them alike)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sf[r] = (bf16)acc_s[kc][0][r];
-            sf[4 + r] = (bf16)acc_s[kc][1][r];
-            df[r] = (bf16)acc_p[kc][0][r];
-            df[4 + r] = (bf16)acc_p[kc][1][r];
-          }
         };
         auto kv = [&](const int kc, const F& sf, const F& df) {
 #pragma unroll
