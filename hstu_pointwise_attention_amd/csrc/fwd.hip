@@ -306,12 +306,9 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           } else {
             s_block(kb, sacc[kb], pacc[GRAD ? kb : 0]);
           }
-          float pv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          // time bias of element r (pre-scaled by -log2(e) in the forward)
+          auto tbias = [&](const int r) {
             const int jl = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            const float a = sacc[kb][r];
-            // time bias of this pair (pre-scaled by -log2(e) in the forward)
             float tb = 0.f;
             if constexpr (has_time) {
               if constexpr (TM == 0) {
@@ -325,26 +322,44 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
                 tb = sm.ttab[time_bucket_wide(ts_i, sm.ts[buf][jl], t_last)];
               }
             }
-            float pr;
-            if constexpr (GRAD) {
-              const float sv = a + tb;
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kNegLog2e));
-              const float sl = sv * sg;
-              pr = pacc[kb][r] * (sg + __builtin_fmaf(-sl, sg, sl));
-            } else {
-              const float sv = __builtin_fmaf(a, kNegLog2e, tb);
-              pr = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv));
-            }
+            return tb;
+          };
+          auto mask = [&](const int r, float pr) {
             if constexpr (MASK) {
               // pr opaque first: left alone the compiler turns the select
               // into a branch around the whole element (bias lookups
               // included), and the elements then run one at a time
               asm volatile("" : "+v"(pr));
-              const int j = j0 + jl;
+              const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
               const bool ok = j <= i && (j < hist || j == i);
               pr = ok ? pr : 0.f;
             }
-            pv[r] = pr;
+            return pr;
+          };
+          float pv[16];
+          if constexpr (!GRAD) {
+            // in stages over the block's 16 elements, so that independent
+            // elements interleave (one element's chain of bias, exp,
+            // reciprocal and product at a time leaves the SIMD waiting)
+            float sv[16], sg[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = __builtin_fmaf(sacc[kb][r], kNegLog2e, tbias(r));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sg[r] = __builtin_amdgcn_exp2f(sv[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sg[r] = __builtin_amdgcn_rcpf(1.0f + sg[r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pv[r] = mask(r, sv[r] * sg[r]);
+          } else {
+            // element by element (staging all 16 needs registers this pass
+            // does not have)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float sv = sacc[kb][r] + tbias(r);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kNegLog2e));
+              const float sl = sv * sg;
+              pv[r] = mask(r, pacc[kb][r] * (sg + __builtin_fmaf(-sl, sg, sl)));
+            }
           }
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
