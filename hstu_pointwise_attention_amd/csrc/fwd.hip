@@ -351,14 +351,21 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
 #pragma unroll
             for (int r = 0; r < 16; ++r) pv[r] = mask(r, sv[r] * sg[r]);
           } else {
-            // element by element (staging all 16 needs registers this pass
-            // does not have)
+            // the same in two groups of 8 (all 16 at once spills here)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float sv = sacc[kb][r] + tbias(r);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kNegLog2e));
-              const float sl = sv * sg;
-              pv[r] = mask(r, pacc[kb][r] * (sg + __builtin_fmaf(-sl, sg, sl)));
+            for (int r0 = 0; r0 < 16; r0 += 8) {
+              float sv[8], sg[8];
+#pragma unroll
+              for (int r = 0; r < 8; ++r) sv[r] = sacc[kb][r0 + r] + tbias(r0 + r);
+#pragma unroll
+              for (int r = 0; r < 8; ++r) sg[r] = __builtin_amdgcn_exp2f(sv[r] * kNegLog2e);
+#pragma unroll
+              for (int r = 0; r < 8; ++r) sg[r] = __builtin_amdgcn_rcpf(1.0f + sg[r]);
+#pragma unroll
+              for (int r = 0; r < 8; ++r) {
+                const float sl = sv[r] * sg[r];
+                pv[r0 + r] = mask(r0 + r, pacc[kb][r0 + r] * (sg[r] + __builtin_fmaf(-sl, sg[r], sl)));
+              }
             }
           }
 #pragma unroll
