@@ -279,44 +279,55 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           }
         };
         auto ew = [&](const int kc, F& sf, F& df) {
+          // in stages over the chunk's 8 elements (e = 4 h + r), so that
+          // independent elements interleave
           int bts[8];
+          bool his[8];
+          float sv[8], sg[8];
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int ql = 32 * kc + 16 * h + 4 * q4 + r;
-              const int i = q0 + ql;
-              float s = acc_s[kc][h][r];
-              int bt = 0;
-              bool hi = false;
-              if constexpr (has_time) {
-                if constexpr (TM == 0) {
-                  s += tb_lo;
-                } else if constexpr (TM == 1) {
-                  hi = (uint32_t)sm.tsq[ql] >= thr;
-                  s += hi ? tb_hi : tb_lo;
-                } else if constexpr (TM == 2) {
-                  bt = time_bucket_rel((uint32_t)sm.tsq[ql], (uint32_t)ts_j, t_last);
-                  s += sm.ttab[bt];
-                } else {
-                  bt = time_bucket_wide(sm.tsq[ql], ts_j, t_last);
-                  s += sm.ttab[bt];
-                }
+          for (int e = 0; e < 8; ++e) {
+            const int ql = 32 * kc + 16 * (e >> 2) + 4 * q4 + (e & 3);
+            float s = acc_s[kc][e >> 2][e & 3];
+            int bt = 0;
+            bool hi = false;
+            if constexpr (has_time) {
+              if constexpr (TM == 0) {
+                s += tb_lo;
+              } else if constexpr (TM == 1) {
+                hi = (uint32_t)sm.tsq[ql] >= thr;
+                s += hi ? tb_hi : tb_lo;
+              } else if constexpr (TM == 2) {
+                bt = time_bucket_rel((uint32_t)sm.tsq[ql], (uint32_t)ts_j, t_last);
+                s += sm.ttab[bt];
+              } else {
+                bt = time_bucket_wide(sm.tsq[ql], ts_j, t_last);
+                s += sm.ttab[bt];
               }
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
-              float sl = s * sg;
-              float ds = acc_p[kc][h][r] * (sg + __builtin_fmaf(-sl, sg, sl));
-              if constexpr (MASK) {
-                const bool ok = j <= i && (j < hist || j == i) && i < L;
-                sl = ok ? sl : 0.f;
-                ds = ok ? ds : 0.f;
-              }
-              acc_s[kc][h][r] = sl;
-              acc_p[kc][h][r] = ds;
-              bts[4 * h + r] = bt;
-              if constexpr (TM <= 1 && has_time) g_all += ds;
-              if constexpr (TM == 1 && has_time) g_hi += hi ? ds : 0.f;
             }
+            sv[e] = s;
+            bts[e] = bt;
+            his[e] = hi;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_exp2f(sv[e] * kNegLog2e);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_rcpf(1.0f + sg[e]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int h = e >> 2, r = e & 3;
+            const int i = q0 + 32 * kc + 16 * h + 4 * q4 + r;
+            float sl = sv[e] * sg[e];
+            float ds = acc_p[kc][h][r] * (sg[e] + __builtin_fmaf(-sl, sg[e], sl));
+            if constexpr (MASK) {
+              const bool ok = j <= i && (j < hist || j == i) && i < L;
+              sl = ok ? sl : 0.f;
+              ds = ok ? ds : 0.f;
+            }
+            acc_s[kc][h][r] = sl;
+            acc_p[kc][h][r] = ds;
+            if constexpr (TM <= 1 && has_time) g_all += ds;
+            if constexpr (TM == 1 && has_time) g_hi += his[e] ? ds : 0.f;
+          }
           // s^T and dS^T as A operands: slots 0..3 the first block's
           // queries, 4..7 the second's (the k-major reads pair them alike)
 #pragma unroll
