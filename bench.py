@@ -197,7 +197,8 @@ def bench_layer(torch, W, hstu_layer_fwd, iters=10):
 
 
 def cpu_baseline(inp, wl):
-    """The oracle (numpy fp64) on a bounded sample: the first sequence of the batch, head 0."""
+    """The oracle (numpy fp64) on a bounded sample: the first sequence of the batch, heads 0 and 1
+    (about 10 s on 16 host threads)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -207,7 +208,8 @@ def cpu_baseline(inp, wl):
     from hstu_pointwise_attention_amd.flops import attention_flops
     s, e = int(inp["seq_offsets"][0]), int(inp["seq_offsets"][1])
     sl = slice(s, e)
-    sub = {k: inp[k][sl, :1] for k in ("q", "k", "v", "u", "d_o")}      # head 0 only
+    nh = 2 if wl.rab_heads == 1 else 1                                    # heads 0 and 1
+    sub = {k: inp[k][sl, :nh] for k in ("q", "k", "v", "u", "d_o")}
     sub["timestamps"] = inp["timestamps"][sl]
     offs = np.array([0, e - s])
     t0 = time.perf_counter()
@@ -215,10 +217,10 @@ def cpu_baseline(inp, wl):
                          None, sub["timestamps"], inp["rab_pos"], inp["rab_time"])
     sec = time.perf_counter() - t0
     # attention_bwd evaluates the forward once inside; count fwd + bwd work
-    f = attention_flops([e - s], 1, wl.d_qk, wl.d_v)
+    f = attention_flops([e - s], nh, wl.d_qk, wl.d_v)
     return {"value": round(f["total"] / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"sequence 0 of the batch (L={e - s}), head 0, fwd+bwd, fp64 numpy"}
+            "sample": f"sequence 0 of the batch (L={e - s}), {nh} head(s), fwd+bwd, fp64 numpy"}
 
 
 if __name__ == "__main__":
