@@ -415,9 +415,6 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
         for (int r = 0; r < 4; ++r)
           dsd_lane[(16 * qb + r) * (C::DG_LD + 1)] = (bf16)0.f;
     }
-    // this wave's staging loads complete before the barrier, so the stores
-    // after it run back to back
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();                               // dS copy and window complete
     if (more) store_tile();
     if (has_pos && pos_diag) {
