@@ -373,9 +373,18 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           }
         };
         F sf0, df0, sf1, df1;
-        sp(0);
-        ew(0, sf0, df0);
-        kv(0, sf0, df0);
+        if (MASK && q0 + 31 < jw) {
+          // the first 32 queries lie before this wave's keys: all masked
+          if (to_copy) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              dsd_lane[(16 * (e >> 2) + (e & 3)) * (C::DG_LD + 1)] = (bf16)0.f;
+          }
+        } else {
+          sp(0);
+          ew(0, sf0, df0);
+          kv(0, sf0, df0);
+        }
         sp(1);
         ew(1, sf1, df1);
         kv(1, sf1, df1);
