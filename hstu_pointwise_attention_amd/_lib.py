@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_EINVAL", -2: "HSTU_EUNSUPPORTED",
 
 # Every symbol the header declares.
 EXPORTS = ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size", "hstu_attn_fwd",
+           "hstu_attn_fwd_cached_workspace_size", "hstu_attn_fwd_cached",
            "hstu_attn_bwd", "hstu_rab_bucketize", "hstu_linear", "hstu_layernorm_gate",
            "hstu_profile_begin", "hstu_profile_end", "hstu_kernel_name", "hstu_kernel_count",
            "hstu_last_error")
@@ -60,6 +61,10 @@ _SIGS = {
     "hstu_attn_bwd_workspace_size": [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)],
     "hstu_attn_fwd": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       ctypes.c_size_t, _P],
+    "hstu_attn_fwd_cached_workspace_size": [ctypes.POINTER(AttnDesc), _I64,
+                                            ctypes.POINTER(ctypes.c_size_t)],
+    "hstu_attn_fwd_cached": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _I64, _P, _P, _P, _P,
+                             _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P],
     "hstu_attn_bwd": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "hstu_rab_bucketize": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P],

@@ -135,6 +135,35 @@ hipError_t dispatch_fwd<bf16>(const AttnParams& p, hipStream_t s) {
 }
 
 template <typename T>
+hipError_t dispatch_fwd_cand(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd_cand<T, 32>(p, s);
+    case 64: return launch_fwd_cand<T, 64>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <>
+hipError_t dispatch_fwd_cand<bf16>(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_fwd_cand<bf16, 32>(p, s);
+    case 64: return launch_fwd_cand<bf16, 64>(p, s);
+    case 128: return launch_fwd_cand<bf16, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Joined row count of a cached-history call (candidates + history rows).
+hstu_status check_hist_tokens(const hstu_attn_desc* d, int64_t hist_tokens) {
+  if (hist_tokens < 0) return fail(HSTU_EINVAL, "hist_tokens %lld < 0", (long long)hist_tokens);
+  if (d->total_tokens + hist_tokens >= ((int64_t)1 << 31))
+    return fail(HSTU_EINVAL, "total_tokens + hist_tokens = %lld outside [0, 2^31)",
+                (long long)(d->total_tokens + hist_tokens));
+  if ((double)(d->total_tokens + hist_tokens) * d->heads * d->d_qk >= 4.0e18)
+    return fail(HSTU_EINVAL, "(total_tokens + hist_tokens) * heads * d overflows the index range");
+  return HSTU_OK;
+}
+
+template <typename T>
 hipError_t dispatch_bwd(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_bwd<T, 32>(p, s);
@@ -236,6 +265,87 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   if (e == hipSuccess)
     e = desc->dtype == HSTU_DTYPE_BF16 ? dispatch_fwd<bf16>(p, s) : dispatch_fwd<float>(p, s);
   if (e != hipSuccess) return hip_fail(e, "hstu_attn_fwd launch");
+  return ok();
+}
+
+hstu_status hstu_attn_fwd_cached_workspace_size(const hstu_attn_desc* desc, int64_t hist_tokens,
+                                                 size_t* bytes) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  st = check_hist_tokens(desc, hist_tokens);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr);
+  p.T = desc->total_tokens + hist_tokens;
+  CandArgs c = {};
+  *bytes = carve_workspace_cand(p, c, nullptr);
+  return ok();
+}
+
+hstu_status hstu_attn_fwd_cached(const hstu_attn_desc* desc, const int64_t* cand_offsets,
+                                 const int64_t* cand_first, const int64_t* n_cands,
+                                 const int64_t* hist_offsets, int64_t hist_tokens,
+                                 const int64_t* ts_hist, const int64_t* ts_cand,
+                                 const float* rab_pos, const float* rab_time, const void* q,
+                                 const void* k, const void* v, const void* u, const void* k_hist,
+                                 const void* v_hist, int64_t stride_kh, int64_t stride_vh, void* o,
+                                 float* a_saved, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  st = check_hist_tokens(desc, hist_tokens);
+  if (st != HSTU_OK) return st;
+  if (desc->batch > 0 && (!cand_offsets || !cand_first || !n_cands || !hist_offsets))
+    return fail(HSTU_EINVAL, "cand_offsets, cand_first, n_cands and hist_offsets are required");
+  if (rab_time && desc->n_time_buckets < 1)
+    return fail(HSTU_EINVAL, "rab_time given but n_time_buckets is %d", desc->n_time_buckets);
+  // a call without candidate rows computes nothing, so needs no tensors
+  if (desc->total_tokens > 0) {
+    if (rab_time && (!ts_cand || (hist_tokens > 0 && !ts_hist)))
+      return fail(HSTU_EINVAL, "rab_time given without ts_cand / ts_hist");
+    // the candidate tensors as the forward's inputs
+    st = check_inputs(desc, cand_offsets, ts_cand, rab_time, q, k, v, u);
+    if (st != HSTU_OK) return st;
+  }
+  if (hist_tokens > 0 && desc->total_tokens > 0) {
+    if (!k_hist || !v_hist) return fail(HSTU_EINVAL, "k_hist and v_hist are required");
+    if (!aligned(k_hist, 16) || !aligned(v_hist, 16))
+      return fail(HSTU_EINVAL, "k_hist and v_hist must be 16-byte aligned");
+    const int64_t hd = (int64_t)desc->heads * desc->d_qk;
+    const int vec = 16 / elem_bytes(desc->dtype);
+    if (stride_kh < hd || stride_vh < hd || stride_kh % vec || stride_vh % vec)
+      return fail(HSTU_EINVAL, "stride_kh %lld / stride_vh %lld must be >= heads*d (%lld) and multiples of %d",
+                  (long long)stride_kh, (long long)stride_vh, (long long)hd, vec);
+  }
+  if (desc->total_tokens > 0) {
+    if (!o) return fail(HSTU_EINVAL, "o is NULL");
+    if (!aligned(o, 16) || (a_saved && !aligned(a_saved, 16)))
+      return fail(HSTU_EINVAL, "o and a_saved must be 16-byte aligned");
+  }
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, rab_pos, rab_time, q, k, v, u);
+  p.T = desc->total_tokens + hist_tokens;
+  p.o = o;
+  p.a_saved = a_saved;
+  p.k_hist = k_hist;
+  p.v_hist = v_hist;
+  p.skh = stride_kh;
+  p.svh = stride_vh;
+  CandArgs c = {cand_offsets, cand_first, n_cands, hist_offsets, ts_hist, ts_cand, nullptr, nullptr};
+  const size_t need = carve_workspace_cand(p, c, nullptr);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  carve_workspace_cand(p, c, workspace);
+  p.cand = c.cand;
+  p.timestamps = rab_time ? c.ts_joined : nullptr;   // the joined numbering's timestamps
+  if (desc->total_tokens == 0 || p.B == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prep_cand(p, c, s);
+  if (e == hipSuccess) e = launch_schedule(p, 0, s);
+  if (e == hipSuccess)
+    e = desc->dtype == HSTU_DTYPE_BF16 ? dispatch_fwd_cand<bf16>(p, s) : dispatch_fwd_cand<float>(p, s);
+  if (e != hipSuccess) return hip_fail(e, "hstu_attn_fwd_cached launch");
   return ok();
 }
 

@@ -188,6 +188,18 @@ struct SeqInfo {
 };
 static_assert(sizeof(SeqInfo) == 32, "SeqInfo layout");
 
+// Candidate scoring against a cached history: where sequence b's rows live.
+// Its rows are numbered as in the single-shot layout, history first
+// (0..h-1, in k_hist / v_hist from hist_start) and then this call's
+// candidates (h..h+m-1, in q / k / v / u from cand_start); pos_shift is the
+// index of the first of them among all the sequence's candidates.
+struct SeqCand {
+  int32_t hist_start;
+  int32_t cand_start;
+  int32_t pos_shift;
+  int32_t pad;
+};
+
 struct WorkItem {
   int32_t seq;
   int32_t blk;

@@ -105,7 +105,13 @@ struct FwdSmem {
 //   dS^T = dP^T * sigma(S)(1 + S(1 - sigma(S)))  (0 where masked)
 //   dQ^T += K^T dS^T                             (K^T by LDS transpose reads)
 // so dQ stays in registers and is written once, with no atomics.
-template <typename T, int D, bool WIDE, bool POS, bool TIME, bool GRAD>
+// CAND (forward only): candidate scoring against a cached history. Rows are
+// numbered as in the single-shot layout (history 0..hist-1, then this
+// call's candidates); history keys and values come from p.k_hist /
+// p.v_hist, candidate rows from q, k, v, u, and only candidate rows are
+// queries. The self term's position bucket is shifted by the index of the
+// call's first candidate among all of the sequence's candidates.
+template <typename T, int D, bool WIDE, bool POS, bool TIME, bool GRAD, bool CAND = false>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD>& sm,
                                          const WorkItem wi, const SeqInfo si, const int head) {
   using C = FwdCfg<T, D, GRAD>;
@@ -113,14 +119,17 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
   const int H = p.H;
   const int L = si.len, hist = si.hist;
   const int64_t start = si.start;
-  const int i0 = wi.blk * C::BM;
+  const SeqCand sc = CAND ? p.cand[wi.seq] : SeqCand{0, 0, 0, 0};
+  const int i0 = (wi.blk + (CAND ? hist / C::BM : 0)) * C::BM;
   const int i_last = min(i0 + C::BM, L) - 1;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int l32 = lane & 31, g = lane >> 5;
   const int iw = i0 + 32 * wave;                 // first row of this wave
   const int i = iw + l32;                        // this lane's query row
-  const bool row_ok = i < L;
+  const bool row_ok = i < L && (!CAND || i >= hist);
+  // row of this lane's query in q, u, o, a
+  const int64_t qrow = CAND ? (int64_t)sc.cand_start + (i - hist) : start + i;
   const int hr = p.rab_heads == 1 ? 0 : head;
   // Which bias terms exist is a compile-time choice so the tile loop is
   // straight-line code the scheduler can interleave.
@@ -145,7 +154,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
 #pragma unroll
   for (int c = 0; c < C::KC; ++c) {
     if (row_ok) {
-      qf[c] = ld_frag(qg + (start + i) * p.sq + (int64_t)head * D + 16 * c + 8 * g);
+      qf[c] = ld_frag(qg + qrow * p.sq + (int64_t)head * D + 16 * c + 8 * g);
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) qf[c][m] = from_f32<T>(0.f);
@@ -165,8 +174,10 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
       }
     }
   }
+  // every row of the sequence has a timestamp (CAND: history rows too, which
+  // are no queries but bound the wave's time-bucket range)
   int64_t ts_i = 0;
-  if (has_time && row_ok)
+  if (has_time && i < L)
     ts_i = wide ? p.timestamps[start + i] : (int64_t)p.ts_rel[start + i];
   if constexpr (has_time) sm.tsq[32 * wave + l32] = ts_i;     // both lane halves hold the same row
 
@@ -197,8 +208,17 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
       const int row = ch / C::CPR, cc = ch % C::CPR;
       const int j = j0 + row;
       const int64_t off = (int64_t)head * D + cc * C::VPC;
-      kreg[m] = j < L ? ld16(kg + (start + j) * p.sk + off) : u32x4{0, 0, 0, 0};
-      vreg[m] = j < L ? ld16(vg + (start + j) * p.sv + off) : u32x4{0, 0, 0, 0};
+      if constexpr (CAND) {
+        const bool hj = j < hist;
+        const int64_t r = hj ? (int64_t)sc.hist_start + j : (int64_t)sc.cand_start + (j - hist);
+        const T* kr = hj ? reinterpret_cast<const T*>(p.k_hist) + r * p.skh : kg + r * p.sk;
+        const T* vr = hj ? reinterpret_cast<const T*>(p.v_hist) + r * p.svh : vg + r * p.sv;
+        kreg[m] = j < L ? ld16(kr + off) : u32x4{0, 0, 0, 0};
+        vreg[m] = j < L ? ld16(vr + off) : u32x4{0, 0, 0, 0};
+      } else {
+        kreg[m] = j < L ? ld16(kg + (start + j) * p.sk + off) : u32x4{0, 0, 0, 0};
+        vreg[m] = j < L ? ld16(vg + (start + j) * p.sv + off) : u32x4{0, 0, 0, 0};
+      }
     }
     if (has_time && tid < C::BN) {
       const int j = j0 + tid;
@@ -206,7 +226,9 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     }
     if (has_pos && tid < C::WIN) {
       const int rel = j0 - p_max + tid;
-      winreg = p.rab_pos[(int64_t)hr * (2 * p.max_len - 1) + pos_bucket(rel, p.max_len)];
+      // CAND: offsets >= 0 are the self terms (candidates see no other candidate)
+      const int relp = CAND && rel >= 0 ? rel + sc.pos_shift : rel;
+      winreg = p.rab_pos[(int64_t)hr * (2 * p.max_len - 1) + pos_bucket(relp, p.max_len)];
     }
   };
 
@@ -241,7 +263,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     if (more) load_tile(tile_j0(n + 1));
 
     // Does this wave have any unmasked pair in the tile?
-    const bool skip = iw >= L || j0 > iw + 31 || (j0 >= hist && j0 + C::BN - 1 < iw);
+    const bool skip = iw >= L || j0 > iw + 31 || (j0 >= hist && j0 + C::BN - 1 < iw) ||
+                      (CAND && iw + 31 < hist);   // CAND: no candidate row in this wave
     if (!skip) {
       const bool need_mask = j0 + C::BN - 1 > min(iw, hist - 1);
       const T* ks = sm.k[buf];
@@ -430,9 +453,9 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     return;
   }
   const float scale = kNegLn2 * si.inv_len;
-  const int64_t orow = ((start + i) * H + head) * (int64_t)D;
+  const int64_t orow = (qrow * H + head) * (int64_t)D;
   T* og = reinterpret_cast<T*>(p.o) + orow;
-  const T* ug = p.u ? reinterpret_cast<const T*>(p.u) + (start + i) * p.su + (int64_t)head * D
+  const T* ug = p.u ? reinterpret_cast<const T*>(p.u) + qrow * p.su + (int64_t)head * D
                     : nullptr;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
@@ -483,6 +506,33 @@ void hstu_fwd_kernel(AttnParams p) {
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void hstu_fwd_cand_kernel(AttnParams p) {
+  __shared__ FwdSmem<T, D, false> sm;
+  if constexpr (WIDE) {
+    if (p.n_items[1] == 0) return;
+    const int64_t slots = (int64_t)*p.n_items * p.H;
+    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
+      const int item = (int)(w / p.H);
+      const int head = (int)(w - (int64_t)item * p.H);
+      const WorkItem wi = p.items[item];
+      const SeqInfo si = p.seq[wi.seq];
+      if ((si.flags & kSeqWideTs) == 0) continue;
+      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, wi, si, head);
+      __syncthreads();                             // the next slot reuses the LDS
+    }
+  } else {
+    const int item = blockIdx.x / p.H;
+    const int head = blockIdx.x - item * p.H;
+    if (item >= *p.n_items) return;
+    const WorkItem wi = p.items[item];
+    const SeqInfo si = p.seq[wi.seq];
+    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+    fwd_body<T, D, false, POS, TIME, false, true>(p, sm, wi, si, head);
+  }
+}
+
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQ_WAVES, DQ_WAVES)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
@@ -511,30 +561,33 @@ void hstu_dq_kernel(AttnParams p) {
   }
 }
 
-template <bool GRAD, typename T, int D, bool WIDE, bool POS, bool TIME>
+// KIND: 0 forward, 1 dQ pass, 2 candidate scoring against a cached history
+template <int KIND, typename T, int D, bool WIDE, bool POS, bool TIME>
 void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
-  if constexpr (GRAD)
+  if constexpr (KIND == 1)
     hipLaunchKernelGGL((hstu_dq_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+  else if constexpr (KIND == 2)
+    hipLaunchKernelGGL((hstu_fwd_cand_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((hstu_fwd_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
 }
 
-template <bool GRAD, typename T, int D>
+template <int KIND, typename T, int D>
 hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
   const dim3 g((unsigned)grid);
   const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(id, s);
-  if (pos && time) launch_one<GRAD, T, D, false, true, true>(p, g, s);
-  else if (pos) launch_one<GRAD, T, D, false, true, false>(p, g, s);
-  else if (time) launch_one<GRAD, T, D, false, false, true>(p, g, s);
-  else launch_one<GRAD, T, D, false, false, false>(p, g, s);
+  if (pos && time) launch_one<KIND, T, D, false, true, true>(p, g, s);
+  else if (pos) launch_one<KIND, T, D, false, true, false>(p, g, s);
+  else if (time) launch_one<KIND, T, D, false, false, true>(p, g, s);
+  else launch_one<KIND, T, D, false, false, false>(p, g, s);
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
   if (time) {
     const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
-    if (pos) launch_one<GRAD, T, D, true, true, true>(p, gw, s);
-    else launch_one<GRAD, T, D, true, false, true>(p, gw, s);
+    if (pos) launch_one<KIND, T, D, true, true, true>(p, gw, s);
+    else launch_one<KIND, T, D, true, false, true>(p, gw, s);
   }
   prof_after(id, s);
   return hipGetLastError();
@@ -544,12 +597,17 @@ hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_fwd(const AttnParams& p, hipStream_t s) {
-  return launch_all<false, T, D>(p, kKFwd, s);
+  return launch_all<0, T, D>(p, kKFwd, s);
 }
 
 template <typename T, int D>
 hipError_t launch_dq(const AttnParams& p, hipStream_t s) {
-  return launch_all<true, T, D>(p, kKDq, s);
+  return launch_all<1, T, D>(p, kKDq, s);
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_cand(const AttnParams& p, hipStream_t s) {
+  return launch_all<2, T, D>(p, kKFwd, s);
 }
 
 template hipError_t launch_fwd<bf16, 32>(const AttnParams&, hipStream_t);
@@ -557,6 +615,11 @@ template hipError_t launch_fwd<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<bf16, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<bf16, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<bf16, 128>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<float, 32>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<float, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 128>(const AttnParams&, hipStream_t);

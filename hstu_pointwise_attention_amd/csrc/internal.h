@@ -40,6 +40,13 @@ struct AttnParams {
   int32_t* sched_scratch;            // schedule kernel scratch
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
+  // candidate scoring against a cached history (null otherwise): T counts
+  // history + candidate rows, seq_offsets / num_targets / timestamps are
+  // unused by the kernels, which read the arrays below
+  const SeqCand* cand;               // [B]
+  const void* k_hist;
+  const void* v_hist;
+  int64_t skh, svh;                  // row strides of k_hist / v_hist
 };
 
 // Workspace layout: returns total bytes and fills the pointers in p (when
@@ -76,6 +83,22 @@ hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, ui
                             uint8_t* bt, hipStream_t s);
 
 template <typename T, int D> hipError_t launch_fwd(const AttnParams& p, hipStream_t s);
+// Candidate scoring against a cached history (p.cand set): query blocks
+// hold only candidate rows; launch_prep_cand builds p.seq, p.cand and the
+// timestamp arrays of the joined row numbering first.
+template <typename T, int D> hipError_t launch_fwd_cand(const AttnParams& p, hipStream_t s);
+struct CandArgs {
+  const int64_t* cand_offsets;
+  const int64_t* cand_first;
+  const int64_t* n_cands;
+  const int64_t* hist_offsets;
+  const int64_t* ts_hist;
+  const int64_t* ts_cand;
+  int64_t* ts_joined;                // [T] workspace (when timestamps are used)
+  SeqCand* cand;                     // [B] workspace
+};
+hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t s);
+size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base);
 // Backward: launch_bwd computes dK, dV and the rab gradients per key block;
 // launch_dq computes dQ per query block (schedule mode 0, like the forward).
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);

@@ -141,6 +141,68 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p)
   }
 }
 
+// Candidate scoring against a cached history: one workgroup per sequence.
+// The sequence's rows are numbered as in the single-shot layout (history,
+// then this call's candidates); the joined timestamps of that numbering go
+// to c.ts_joined (64-bit) and p.ts_rel (rebased, as in seq_prep_kernel).
+// Normalisation is 1 / (h + n) over all n candidates of the sequence, and
+// only query blocks holding candidates are scheduled (nblk counts blocks
+// from the one holding row h).
+__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_cand_kernel(AttnParams p, CandArgs c) {
+  __shared__ int64_t lds64[kSeqPrepThreads / kWave];
+  __shared__ int32_t lds32[kSeqPrepThreads / kWave];
+  const int b = blockIdx.x;
+  const int64_t hs = c.hist_offsets[b], cs = c.cand_offsets[b];
+  const int h = (int)(c.hist_offsets[b + 1] - hs);
+  const int m = (int)(c.cand_offsets[b + 1] - cs);
+  const int L = h + m;
+  const int64_t vs = (hs - c.hist_offsets[0]) + (cs - c.cand_offsets[0]);
+  int64_t first = c.cand_first[b];
+  first = first < 0 ? 0 : first;
+  int64_t n_all = c.n_cands[b];
+  n_all = n_all < first + m ? first + m : n_all;   // at least the candidates given
+  auto ts_at = [&](int64_t j) { return j < h ? c.ts_hist[hs + j] : c.ts_cand[cs + (j - h)]; };
+  int flags = 0;
+  int64_t origin = 0;
+  if (p.timestamps != nullptr && L > 0) {
+    origin = ts_at(0) - ((int64_t)1 << 30);
+    int64_t lo = INT64_MAX, hi = INT64_MIN;
+    int32_t sorted = 1;
+    for (int64_t j = threadIdx.x; j < L; j += blockDim.x) {
+      const int64_t x = ts_at(j);
+      lo = x < lo ? x : lo;
+      hi = x > hi ? x : hi;
+      if (j > 0 && ts_at(j - 1) > x) sorted = 0;
+      c.ts_joined[vs + j] = x;
+      p.ts_rel[vs + j] = (uint32_t)(x - origin);
+    }
+    lo = block_reduce(lo, lds64, MinOp());
+    hi = block_reduce(hi, lds64, MaxOp());
+    sorted = block_reduce(sorted, lds32, AndOp());
+    const bool narrow = lo >= origin && (uint64_t)hi - (uint64_t)origin < 0x7fffffffull;
+    if (!narrow) flags |= kSeqWideTs;
+    if (sorted) flags |= kSeqSortedTs;
+  }
+  if (threadIdx.x == 0) {
+    SeqInfo si;
+    si.start = (int32_t)vs;
+    si.len = L;
+    si.hist = h;
+    si.flags = flags;
+    const int64_t n_norm = (int64_t)h + n_all;
+    si.inv_len = n_norm > 0 ? 1.0f / (float)n_norm : 0.0f;
+    si.nblk = m > 0 ? (L + kBlk - 1) / kBlk - h / kBlk : 0;
+    si.ts_origin = origin;
+    p.seq[b] = si;
+    SeqCand sc;
+    sc.hist_start = (int32_t)hs;
+    sc.cand_start = (int32_t)cs;
+    sc.pos_shift = first > (int64_t)1 << 30 ? 1 << 30 : (int32_t)first;
+    sc.pad = 0;
+    c.cand[b] = sc;
+  }
+}
+
 // Exclusive prefix sum over n ints in place (forward or from the end), one
 // workgroup, chunks of blockDim.x with a running carry. Returns the total.
 __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
@@ -377,6 +439,28 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
     p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
   }
   return off;
+}
+
+// The forward's carve-up for the joined row count p.T, plus the per-sequence
+// candidate records and, with a time bias, the joined 64-bit timestamps.
+size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base) {
+  size_t off = carve_workspace(p, base, false, 2);
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return base ? (void*)((char*)base + at) : nullptr;
+  };
+  c.cand = (SeqCand*)take(sizeof(SeqCand) * (size_t)(p.B > 0 ? p.B : 1));
+  c.ts_joined = (int64_t*)take(sizeof(int64_t) * (size_t)(p.T > 0 ? p.T : 1));
+  return off;
+}
+
+hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t s) {
+  if (p.B == 0) return hipSuccess;
+  prof_before(kKPrep, s);
+  hipLaunchKernelGGL(seq_prep_cand_kernel, dim3(p.B), dim3(kSeqPrepThreads), 0, s, p, c);
+  prof_after(kKPrep, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_prep(const AttnParams& p, hipStream_t s) {

@@ -26,6 +26,8 @@ def _stream():
 def _token_stride(t: torch.Tensor, name: str, H: int, D: int) -> int:
     if t.dim() != 3 or t.shape[1] != H or t.shape[2] != D:
         raise ValueError(f"{name} must be [T, {H}, {D}], got {tuple(t.shape)}")
+    if t.numel() == 0:
+        return H * D                                  # no rows: any valid stride
     if t.stride(2) != 1 or t.stride(1) != D:
         raise ValueError(f"{name} must have contiguous heads and head dim (strides {t.stride()})")
     return t.stride(0)
@@ -89,6 +91,46 @@ def attn_fwd(q, k, v, u, seq_offsets, max_len, *, num_targets=None, timestamps=N
                                  _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(u), _ptr(o), _ptr(a), _ptr(ws), nbytes.value,
                                  _stream()))
+    return o, a
+
+
+def attn_fwd_cached(q, k, v, u, cand_offsets, cand_first, n_cands, k_hist, v_hist,
+                    hist_offsets, max_len, *, ts_hist=None, ts_cand=None, rab_pos=None,
+                    rab_time=None, save_a: bool = True):
+    """Candidate scoring against a cached history (hstu_attn_fwd_cached).
+
+    q, k, v, u: this call's candidate rows [M, H, D] (cand_offsets [B+1]);
+    k_hist, v_hist: the history rows [Th, H, D] (hist_offsets [B+1]);
+    cand_first [B], n_cands [B]: position of the call's candidates among each
+    sequence's candidates. Returns (O [M,H,Dv], A [M,H,Dv] fp32 or None).
+    """
+    lib = _lib.load()
+    cand_offsets, cand_first, n_cands = _i64(cand_offsets), _i64(cand_first), _i64(n_cands)
+    hist_offsets, ts_hist, ts_cand = _i64(hist_offsets), _i64(ts_hist), _i64(ts_cand)
+    rab_pos, rab_time = _f32c(rab_pos), _f32c(rab_time)
+    nt, hr = _rab_meta(rab_pos, rab_time)
+    desc = make_desc(q, k, v, u, cand_offsets, max_len, nt, hr)
+    M, H, D = q.shape
+    Dv = v.shape[2]
+    for name, t in (("k_hist", k_hist), ("v_hist", v_hist)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    skh = _token_stride(k_hist, "k_hist", H, D)
+    svh = _token_stride(v_hist, "v_hist", H, Dv)
+    Th = k_hist.shape[0]
+    if v_hist.shape[0] != Th:
+        raise ValueError("k_hist and v_hist must have the same rows")
+    o = torch.empty((M, H, Dv), dtype=q.dtype, device=q.device)
+    a = torch.empty((M, H, Dv), dtype=torch.float32, device=q.device) if save_a else None
+    nbytes = ctypes.c_size_t()
+    _lib.check(lib.hstu_attn_fwd_cached_workspace_size(ctypes.byref(desc), Th, ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.hstu_attn_fwd_cached(ctypes.byref(desc), _ptr(cand_offsets), _ptr(cand_first),
+                                        _ptr(n_cands), _ptr(hist_offsets), Th, _ptr(ts_hist),
+                                        _ptr(ts_cand), _ptr(rab_pos), _ptr(rab_time), _ptr(q),
+                                        _ptr(k), _ptr(v), _ptr(u), _ptr(k_hist), _ptr(v_hist),
+                                        skh, svh, _ptr(o), _ptr(a), _ptr(ws), nbytes.value,
+                                        _stream()))
     return o, a
 
 

@@ -109,6 +109,60 @@ HSTU_API hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* se
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Candidate scoring against a cached history (M-FALCON-style micro-batched
+ * inference; the pages name M-FALCON for inference in the abstract of
+ * "Actions Speak Louder than Words" and in the Generative Recommenders
+ * README, whose "HSTU Ultra attention benchmark" defines the target-aware
+ * mask used here and notes that cached incremental decoding is not yet
+ * included there).
+ *
+ * Sequence b has h_b history rows, whose keys and values were computed once
+ * (k_hist, v_hist), and n_b candidates, scored here in micro-batches: this
+ * call takes m_b of them, the candidates cand_first[b] .. cand_first[b] +
+ * m_b - 1. Each candidate attends to every history row and to itself. The
+ * outputs equal those candidates' rows of hstu_attn_fwd on the whole
+ * sequence [history, all n_b candidates] with num_targets = n_b: the same
+ * normalisation 1 / (h_b + n_b), position buckets and time buckets.
+ *
+ *  desc          batch B; total_tokens = candidate rows of this call (sum of
+ *                m_b); stride_q, stride_k, stride_v, stride_u as in
+ *                hstu_attn_fwd, for q, k, v, u
+ *  cand_offsets  (device) int64 [B+1]: sequence b's candidate rows of this
+ *                call are cand_offsets[b] .. cand_offsets[b+1] - 1
+ *  cand_first    (device) int64 [B]: index of the first of them among the
+ *                sequence's n_b candidates (values < 0 count as 0)
+ *  n_cands       (device) int64 [B]: n_b (at least cand_first[b] + m_b; a
+ *                smaller value counts as cand_first[b] + m_b)
+ *  hist_offsets  (device) int64 [B+1]: sequence b's history rows in
+ *                k_hist / v_hist
+ *  hist_tokens   rows of k_hist / v_hist; total_tokens + hist_tokens < 2^31
+ *  ts_hist, ts_cand (device) int64 timestamps of the history rows and of
+ *                this call's candidate rows; required when rab_time != NULL
+ *  rab_pos, rab_time as in hstu_attn_fwd
+ *  q, k, v, u    (device) dtype [total_tokens, H, d]: the candidates' rows
+ *  k_hist, v_hist (device) dtype [hist_tokens, H, d], row strides
+ *                stride_kh, stride_vh (>= H * d, multiples of 16 bytes)
+ *  o, a_saved    (device) [total_tokens, H, d_v]: the candidates' O (dtype)
+ *                and A (fp32, or NULL), written
+ *  workspace     (device) >= hstu_attn_fwd_cached_workspace_size bytes,
+ *                256-aligned
+ * Errors as in hstu_attn_fwd. Offsets that index outside the given tensors
+ * are the caller's error and are not checked on the device.
+ */
+HSTU_API hstu_status hstu_attn_fwd_cached_workspace_size(const hstu_attn_desc* desc,
+                                                          int64_t hist_tokens, size_t* bytes);
+HSTU_API hstu_status hstu_attn_fwd_cached(const hstu_attn_desc* desc, const int64_t* cand_offsets,
+                                          const int64_t* cand_first, const int64_t* n_cands,
+                                          const int64_t* hist_offsets, int64_t hist_tokens,
+                                          const int64_t* ts_hist, const int64_t* ts_cand,
+                                          const float* rab_pos, const float* rab_time,
+                                          const void* q, const void* k, const void* v,
+                                          const void* u, const void* k_hist, const void* v_hist,
+                                          int64_t stride_kh, int64_t stride_vh, void* o,
+                                          float* a_saved, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * Backward. Inputs as in hstu_attn_fwd, plus
  *  a_saved      (device) fp32 [T, H, d_v] from the forward; required if u != NULL
  *  d_o          (device) dtype [T, H, d_v] dense
