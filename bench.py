@@ -158,6 +158,7 @@ def main():
 
     if not args.no_layer:
         out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd)
+        out["cached_scoring"] = bench_cached(torch)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl)
@@ -194,6 +195,47 @@ def bench_layer(torch, W, hstu_layer_fwd, iters=10):
     gemm = 2 * T * w.model_dim * (4 * w.heads * w.head_dim) + 2 * T * (w.heads * w.head_dim) * w.model_dim
     return {"ms": round(ms, 4), "tflops": round((attn + gemm) / (ms * 1e-3) / 1e12, 2),
             "attn_flops": attn, "gemm_flops": gemm, "tokens": T}
+
+
+def bench_cached(torch, users=4, hist=8192, n_cand=1024, micro=128, heads=4, d=128, iters=5):
+    """Candidate scoring against a cached history (hstu_attn_fwd_cached) at the
+    M-FALCON layer's attention shape: 4 users x 8192 history rows, 1024
+    candidates each, scored in micro-batches of 128 per user; H 4, D 128,
+    bf16, no bias or gate (the layer's attention). Seeded synthetic inputs."""
+    from hstu_pointwise_attention_amd import ops
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(1006)
+    rnd = lambda *shape: (0.5 * torch.randn(*shape, generator=g, device=dev)).to(torch.bfloat16)
+    k_hist, v_hist = rnd(users * hist, heads, d), rnd(users * hist, heads, d)
+    hist_offsets = torch.arange(users + 1, device=dev, dtype=torch.int64) * hist
+    cand_offsets = torch.arange(users + 1, device=dev, dtype=torch.int64) * micro
+    n_cands = torch.full((users,), n_cand, device=dev, dtype=torch.int64)
+    n_micro = n_cand // micro
+    batches = [(rnd(users * micro, heads, d), rnd(users * micro, heads, d), rnd(users * micro, heads, d),
+                torch.full((users,), mb * micro, device=dev, dtype=torch.int64)) for mb in range(n_micro)]
+
+    def score_all():
+        for q, k, v, first in batches:
+            ops.attn_fwd_cached(q, k, v, None, cand_offsets, first, n_cands, k_hist, v_hist,
+                                hist_offsets, hist + n_cand, save_a=False)
+
+    score_all()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        score_all()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters                 # all candidates of all users
+    pairs = users * heads * n_cand * (hist + 1)
+    flops = pairs * 4 * d
+    return {"ms_all_candidates": round(ms, 4), "ms_per_micro_batch": round(ms / n_micro, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "candidates_per_s": round(users * n_cand / (ms * 1e-3)),
+            "shape": f"{users} users x {hist} history rows, {n_cand} candidates in micro-batches "
+                     f"of {micro}, H {heads}, D {d}, bf16, no bias",
+            "pair_heads": pairs, "flops": flops}
 
 
 def cpu_baseline(inp, wl):

@@ -278,6 +278,8 @@ hstu_status hstu_attn_fwd_cached_workspace_size(const hstu_attn_desc* desc, int6
   AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                              nullptr, nullptr);
   p.T = desc->total_tokens + hist_tokens;
+  p.m_rows = desc->total_tokens;
+  p.kv_splits = cand_kv_splits(p.m_rows, hist_tokens, p.B, p.H);
   CandArgs c = {};
   *bytes = carve_workspace_cand(p, c, nullptr);
   return ok();
@@ -325,6 +327,8 @@ hstu_status hstu_attn_fwd_cached(const hstu_attn_desc* desc, const int64_t* cand
   }
   AttnParams p = base_params(desc, nullptr, nullptr, nullptr, rab_pos, rab_time, q, k, v, u);
   p.T = desc->total_tokens + hist_tokens;
+  p.m_rows = desc->total_tokens;
+  p.kv_splits = cand_kv_splits(p.m_rows, hist_tokens, p.B, p.H);
   p.o = o;
   p.a_saved = a_saved;
   p.k_hist = k_hist;

@@ -113,7 +113,8 @@ struct FwdSmem {
 // call's first candidate among all of the sequence's candidates.
 template <typename T, int D, bool WIDE, bool POS, bool TIME, bool GRAD, bool CAND = false>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD>& sm,
-                                         const WorkItem wi, const SeqInfo si, const int head) {
+                                         const WorkItem wi, const SeqInfo si, const int head,
+                                         const int split = 0) {
   using C = FwdCfg<T, D, GRAD>;
   using F = typename Frag<T>::type;
   const int H = p.H;
@@ -192,14 +193,25 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
   const int skip_hi = max(i0, hist) / C::BN;
   const int n_a = min(skip_lo, t_end);
   const int b_start = max(skip_hi, n_a);
-  const int n_tiles = n_a + max(0, t_end - b_start);
+  // CAND with p.kv_splits > 1: this workgroup's share of the history tiles;
+  // the last split also takes the candidate (diagonal) tiles
+  int h_lo = 0, h_n = n_a, d_n = max(0, t_end - b_start);
+  if constexpr (CAND) {
+    const int S = p.kv_splits;
+    if (S > 1) {
+      h_lo = (int)((int64_t)n_a * split / S);
+      h_n = (int)((int64_t)n_a * (split + 1) / S) - h_lo;
+      if (split != S - 1) d_n = 0;
+    }
+  }
+  const int n_tiles = h_n + d_n;
 
   // ---------------------------------------------------------------- staging
   u32x4 kreg[C::CH], vreg[C::CH];
   int64_t tsreg = 0;
   float winreg = 0.f;
 
-  auto tile_j0 = [&](int n) { return (n < n_a ? n : b_start + (n - n_a)) * C::BN; };
+  auto tile_j0 = [&](int n) { return (n < h_n ? h_lo + n : b_start + (n - h_n)) * C::BN; };
 
   auto load_tile = [&](int j0) {
 #pragma unroll
@@ -453,6 +465,21 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     return;
   }
   const float scale = kNegLn2 * si.inv_len;
+  if constexpr (CAND) {
+    if (p.kv_splits > 1) {                         // partial A of this split
+      float* pg = p.part + (((int64_t)split * p.m_rows + qrow) * H + head) * (int64_t)D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          f32x4 a;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) a[m] = acc_o[db][4 * rq + m] * scale;
+          *reinterpret_cast<f32x4*>(pg + 32 * db + 8 * rq + 4 * g) = a;
+        }
+      return;
+    }
+  }
   const int64_t orow = (qrow * H + head) * (int64_t)D;
   T* og = reinterpret_cast<T*>(p.o) + orow;
   const T* ug = p.u ? reinterpret_cast<const T*>(p.u) + qrow * p.su + (int64_t)head * D
@@ -509,26 +536,55 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_cand_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
+  const int S = p.kv_splits;                       // workgroups per (item, head)
   if constexpr (WIDE) {
     if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H;
+    const int64_t slots = (int64_t)*p.n_items * p.H * S;
     for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / p.H);
-      const int head = (int)(w - (int64_t)item * p.H);
+      const int item = (int)(w / ((int64_t)p.H * S));
+      const int rem = (int)(w - (int64_t)item * p.H * S);
+      const int head = rem / S, split = rem - head * S;
       const WorkItem wi = p.items[item];
       const SeqInfo si = p.seq[wi.seq];
       if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, wi, si, head);
+      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, wi, si, head, split);
       __syncthreads();                             // the next slot reuses the LDS
     }
   } else {
-    const int item = blockIdx.x / p.H;
-    const int head = blockIdx.x - item * p.H;
+    const int item = blockIdx.x / (p.H * S);
+    const int rem = blockIdx.x - item * p.H * S;
+    const int head = rem / S, split = rem - head * S;
     if (item >= *p.n_items) return;
     const WorkItem wi = p.items[item];
     const SeqInfo si = p.seq[wi.seq];
     if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
-    fwd_body<T, D, false, POS, TIME, false, true>(p, sm, wi, si, head);
+    fwd_body<T, D, false, POS, TIME, false, true>(p, sm, wi, si, head, split);
+  }
+}
+
+// Sum of the splits' partial A (candidate calls with p.kv_splits > 1), then
+// A and O = A * U (or A), 4 elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void cand_finish_kernel(AttnParams p) {
+  const int64_t n4 = p.m_rows * p.H * p.D / 4;
+  const int64_t plane = p.m_rows * p.H * p.D;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n4;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = 4 * x;
+    f32x4 a = *reinterpret_cast<const f32x4*>(p.part + e);
+    for (int sp = 1; sp < p.kv_splits; ++sp) {
+      const f32x4 b = *reinterpret_cast<const f32x4*>(p.part + sp * plane + e);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] += b[m];
+    }
+    if (p.a_saved) *reinterpret_cast<f32x4*>(p.a_saved + e) = a;
+    const int64_t row = e / ((int64_t)p.H * p.D), col = e - row * p.H * p.D;
+    if (p.u) {
+      const f32x4 uv = ld4_f32(reinterpret_cast<const T*>(p.u) + row * p.su + col);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] *= uv[m];
+    }
+    st4_from_f32(reinterpret_cast<T*>(p.o) + e, a);
   }
 }
 
@@ -574,7 +630,7 @@ void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
 
 template <int KIND, typename T, int D>
 hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
-  const int64_t grid = p.max_items * p.H;
+  const int64_t grid = p.max_items * p.H * (KIND == 2 ? p.kv_splits : 1);
   if (grid == 0) return hipSuccess;
   const dim3 g((unsigned)grid);
   const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
@@ -607,7 +663,12 @@ hipError_t launch_dq(const AttnParams& p, hipStream_t s) {
 
 template <typename T, int D>
 hipError_t launch_fwd_cand(const AttnParams& p, hipStream_t s) {
-  return launch_all<2, T, D>(p, kKFwd, s);
+  hipError_t e = launch_all<2, T, D>(p, kKFwd, s);
+  if (e != hipSuccess || p.kv_splits <= 1 || p.m_rows == 0) return e;
+  const int64_t n4 = p.m_rows * p.H * p.D / 4;
+  const int64_t blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL(cand_finish_kernel<T>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 template hipError_t launch_fwd<bf16, 32>(const AttnParams&, hipStream_t);

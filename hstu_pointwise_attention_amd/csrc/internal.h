@@ -47,6 +47,13 @@ struct AttnParams {
   const void* k_hist;
   const void* v_hist;
   int64_t skh, svh;                  // row strides of k_hist / v_hist
+  // the history tiles of a candidate query block split over kv_splits
+  // workgroups; with more than one, each writes its partial A to
+  // part[split][row][head][d] (fp32, rows of q) and a finishing kernel sums
+  // them into A and O
+  int32_t kv_splits;
+  int64_t m_rows;                    // candidate rows (rows of q)
+  float* part;
 };
 
 // Workspace layout: returns total bytes and fills the pointers in p (when
@@ -98,7 +105,11 @@ struct CandArgs {
   SeqCand* cand;                     // [B] workspace
 };
 hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t s);
+// p.T, p.B, p.H, p.D, p.m_rows and p.kv_splits set
 size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base);
+// Splits of the history for a candidate call: enough workgroups to fill the
+// chip, at least 8 history tiles (512 keys) per split on average.
+int cand_kv_splits(int64_t m_rows, int64_t hist_rows, int B, int H);
 // Backward: launch_bwd computes dK, dV and the rab gradients per key block;
 // launch_dq computes dQ per query block (schedule mode 0, like the forward).
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);

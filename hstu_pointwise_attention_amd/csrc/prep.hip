@@ -452,7 +452,20 @@ size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base) {
   };
   c.cand = (SeqCand*)take(sizeof(SeqCand) * (size_t)(p.B > 0 ? p.B : 1));
   c.ts_joined = (int64_t*)take(sizeof(int64_t) * (size_t)(p.T > 0 ? p.T : 1));
+  p.part = nullptr;
+  if (p.kv_splits > 1)
+    p.part = (float*)take(sizeof(float) * (size_t)p.kv_splits * (size_t)p.m_rows * p.H * p.D);
   return off;
+}
+
+int cand_kv_splits(int64_t m_rows, int64_t hist_rows, int B, int H) {
+  if (B <= 0 || m_rows <= 0) return 1;
+  const int64_t blocks = (m_rows / kBlk + B) * H;          // query-block workgroups, at most
+  const int64_t want = (2 * 256 + blocks - 1) / blocks;   // two workgroups per compute unit
+  const int64_t by_len = hist_rows / ((int64_t)B * 512);  // >= 8 tiles of 64 keys per split
+  int64_t s = want < by_len ? want : by_len;
+  s = s < 1 ? 1 : (s > 16 ? 16 : s);
+  return (int)s;
 }
 
 hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t s) {

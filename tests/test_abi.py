@@ -116,6 +116,37 @@ def test_bwd_requires_gradients(lib):
     assert st == _lib.HSTU_EINVAL
 
 
+def cached_call(lib, d, hist_tokens=20, ts_hist=FAKE, ts_cand=FAKE, rab_time=FAKE, k_hist=FAKE,
+                stride_kh=128, hist_offsets=FAKE, ws_bytes=1 << 30, ws=ctypes.c_void_p(1 << 20)):
+    return lib.hstu_attn_fwd_cached(ctypes.byref(d), FAKE, FAKE, FAKE, hist_offsets, hist_tokens,
+                                    ts_hist, ts_cand, None, rab_time, FAKE, FAKE, FAKE, FAKE,
+                                    k_hist, FAKE, stride_kh, 128, FAKE, None, ws, ws_bytes, None)
+
+
+def test_cached_validation(lib):
+    d = good_desc()
+    need = ctypes.c_size_t()
+    assert lib.hstu_attn_fwd_cached_workspace_size(ctypes.byref(d), 20, ctypes.byref(need)) == 0
+    fneed = ctypes.c_size_t()
+    assert lib.hstu_attn_fwd_workspace_size(ctypes.byref(d), ctypes.byref(fneed)) == 0
+    assert need.value > fneed.value                       # joined rows + per-sequence records
+    assert lib.hstu_attn_fwd_cached_workspace_size(ctypes.byref(d), -1, ctypes.byref(need)) \
+        == _lib.HSTU_EINVAL
+    assert lib.hstu_attn_fwd_cached_workspace_size(ctypes.byref(d), 1 << 31, ctypes.byref(need)) \
+        == _lib.HSTU_EINVAL                               # joined rows beyond 2^31
+    assert cached_call(lib, d, ts_hist=None) == _lib.HSTU_EINVAL        # time bias, no history ts
+    assert cached_call(lib, d, ts_cand=None) == _lib.HSTU_EINVAL        # time bias, no candidate ts
+    assert cached_call(lib, d, k_hist=None) == _lib.HSTU_EINVAL         # history rows, no keys
+    assert cached_call(lib, d, stride_kh=64) == _lib.HSTU_EINVAL        # stride below heads*d
+    assert cached_call(lib, d, stride_kh=130) == _lib.HSTU_EINVAL       # not 16-byte rows
+    assert cached_call(lib, d, hist_offsets=None) == _lib.HSTU_EINVAL
+    assert cached_call(lib, d, ws_bytes=16) == _lib.HSTU_EWORKSPACE
+    assert cached_call(lib, good_desc(d_qk=48, d_v=48)) == _lib.HSTU_EUNSUPPORTED
+    # no candidate rows: nothing to compute, no tensors needed
+    assert cached_call(lib, good_desc(total_tokens=0), ts_hist=None, ts_cand=None,
+                       k_hist=None) == _lib.HSTU_OK
+
+
 def test_layer_validation(lib):
     assert lib.hstu_linear(10, 48, 128, FAKE, 48, FAKE, None, FAKE, 1, None) == _lib.HSTU_EUNSUPPORTED
     assert lib.hstu_linear(10, 64, 100, FAKE, 64, FAKE, None, FAKE, 1, None) == _lib.HSTU_EUNSUPPORTED

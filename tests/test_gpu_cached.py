@@ -128,6 +128,13 @@ def test_cached_edges(dtype):
           H=2, D=32, max_len=300, nb=16, pos=True, rab_heads=1, gated=True, n_micro=3, seed=11)
 
 
+def test_cached_split_history_fp32():
+    """History long enough that each candidate block's history is split over
+    several workgroups whose partial A are summed (fp32: exact to 1e-5)."""
+    _case("fp32", [1200, 700, 1500], [40, 9, 70], H=2, D=64, max_len=1600, nb=128, pos=True,
+          rab_heads=2, gated=True, n_micro=2, seed=16)
+
+
 def test_cached_long_history_bf16():
     """Several history tiles and query blocks of candidates, head dim 128."""
     _case("bf16", [1500, 2100], [200, 70], H=2, D=128, max_len=2400, nb=128, pos=True,
