@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--workload", default="efficiency_8192_bf16")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--cached-only", action="store_true",
+                    help="only time candidate scoring against a cached history")
     return ap.parse_args()
 
 
@@ -76,6 +78,12 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.cached_only:
+        from hstu_pointwise_attention_amd import _lib as _l
+        _l.load()
+        print(json.dumps({"cached_scoring": bench_cached(torch)}), flush=True)
+        return
 
     import workloads as W
     from hstu_pointwise_attention_amd import _lib, ops
