@@ -70,3 +70,55 @@ def test_layer_rows_match_full():
     for key in ("uvqk", "a", "y"):
         want = full[key][rows]
         assert np.max(np.abs(part[key] - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_layer_bwd_finite_differences():
+    """Every gradient of the layer oracle against central differences of its
+    forward (directional derivatives along random directions, plus single
+    entries), so a dropped term, a transposed operand or a wrong sign in the
+    chain rule fails here."""
+    from oracle.layer import layer_bwd, layer_fwd
+    rng = np.random.default_rng(3)
+    H, D, dm = 2, 3, 5
+    offs = np.array([0, 5, 9])
+    nt = np.array([2, 1])
+    T = 9
+    x = 0.7 * rng.standard_normal((T, dm))
+    w1 = 0.6 * rng.standard_normal((dm, 4 * H * D))
+    b1 = 0.2 * rng.standard_normal(4 * H * D)
+    w2 = 0.6 * rng.standard_normal((H * D, dm))
+    b2 = 0.2 * rng.standard_normal(dm)
+    dy = rng.standard_normal((T, dm))
+    g = layer_bwd(x, w1, b1, w2, b2, offs, nt, H, D, dy)
+    params = dict(x=x, w1=w1, b1=b1, w2=w2, b2=b2)
+
+    def loss(**kw):
+        p = dict(params, **kw)
+        return float(np.sum(layer_fwd(p["x"], p["w1"], p["b1"], p["w2"], p["b2"], offs, nt, H, D)["y"] * dy))
+
+    h = 1e-5
+    for name, grad in (("x", "dx"), ("w1", "dw1"), ("b1", "db1"), ("w2", "dw2"), ("b2", "db2")):
+        base = params[name]
+        for trial in range(3):
+            d = rng.standard_normal(base.shape)
+            num = (loss(**{name: base + h * d}) - loss(**{name: base - h * d})) / (2 * h)
+            ana = float(np.sum(g[grad] * d))
+            assert abs(num - ana) <= 1e-6 * max(1.0, abs(num)), (name, trial, num, ana)
+        idx = tuple(int(rng.integers(n)) for n in base.shape)
+        e = np.zeros_like(base)
+        e[idx] = 1.0
+        num = (loss(**{name: base + h * e}) - loss(**{name: base - h * e})) / (2 * h)
+        assert abs(num - g[grad][idx]) <= 1e-6 * max(1.0, abs(num)), (name, idx, num, g[grad][idx])
+
+
+def test_layernorm_bwd_finite_differences():
+    from oracle.layer import layernorm_bwd
+    rng = np.random.default_rng(4)
+    a = 2.0 + rng.standard_normal((3, 16))
+    d_ln = rng.standard_normal((3, 16))
+    got = layernorm_bwd(a, d_ln)
+    h = 1e-6
+    for trial in range(4):
+        d = rng.standard_normal(a.shape)
+        num = (np.sum(oracle.layernorm(a + h * d) * d_ln) - np.sum(oracle.layernorm(a - h * d) * d_ln)) / (2 * h)
+        assert abs(num - np.sum(got * d)) <= 1e-7 * max(1.0, abs(num))
