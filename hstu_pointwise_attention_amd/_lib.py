@@ -26,6 +26,7 @@ STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_EINVAL", -2: "HSTU_EUNSUPPORTED",
 EXPORTS = ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size", "hstu_attn_fwd",
            "hstu_attn_fwd_cached_workspace_size", "hstu_attn_fwd_cached",
            "hstu_attn_bwd", "hstu_rab_bucketize", "hstu_linear", "hstu_layernorm_gate",
+           "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
            "hstu_profile_begin", "hstu_profile_end", "hstu_kernel_name", "hstu_kernel_count",
            "hstu_last_error")
 
@@ -70,6 +71,11 @@ _SIGS = {
     "hstu_rab_bucketize": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P],
     "hstu_linear": [_I64, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_int32, _P],
     "hstu_layernorm_gate": [_I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P],
+    "hstu_layer_bwd_workspace_size": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "hstu_layer_bwd": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                       _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
+                       ctypes.c_size_t, _P],
     "hstu_profile_begin": [],
     "hstu_profile_end": [ctypes.c_int32, _P, _P],
     "hstu_kernel_count": [],

@@ -54,3 +54,11 @@ def hstu_layer_fwd(x, w1, b1, w2, b2, seq_offsets, num_targets, heads: int, head
     g = ops.layernorm_gate(a2, uvqk[:, 0:HD], eps)
     y = ops.linear(g, w2, b2, silu=False)
     return y, a2, uvqk
+
+
+def hstu_layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a,
+                   dy, eps: float = 1e-5):
+    """Gradients of :func:`hstu_layer_fwd` from dY: dict dx, dw1, db1, dw2, db2
+    (uvqk and a as the forward returned them)."""
+    return ops.layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads, head_dim, uvqk, a, dy,
+                         eps)

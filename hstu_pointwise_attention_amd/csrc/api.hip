@@ -455,6 +455,148 @@ hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, const void
   return ok();
 }
 
+// ---------------------------------------------------------------- layer backward
+namespace {
+
+struct LayerBwdWs {
+  void *pre, *z, *zt, *dyp, *w2t, *dz, *da, *du, *dq, *dk, *dv, *d_pre, *xt, *w1t, *attn;
+  size_t attn_bytes;
+};
+
+// Carve-up of the layer backward's workspace (base == nullptr: sizes only).
+hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
+                            int32_t head_dim, void* base, LayerBwdWs* w, size_t* bytes) {
+  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD, Mp = (M + 31) / 32 * 32;
+  hstu_attn_desc ad = {};
+  ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim; ad.max_len = 1;
+  ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
+  ad.stride_q = ad.stride_k = ad.stride_v = W; ad.stride_u = 0;
+  size_t attn = 0;
+  hstu_status st = hstu_attn_bwd_workspace_size(&ad, &attn);
+  if (st != HSTU_OK) return st;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t at = off;
+    off += (b + 255) & ~(size_t)255;
+    return base ? (void*)((char*)base + at) : nullptr;
+  };
+  const size_t e = 2;                            // bf16
+  w->pre = take(e * M * W);
+  w->z = take(e * M * HD);
+  w->zt = take(e * HD * Mp);
+  w->dyp = take(e * Mp * d_model);
+  w->w2t = take(e * d_model * HD);
+  w->dz = take(e * M * HD);
+  w->da = take(e * M * HD);
+  w->du = take(e * M * HD);
+  w->dq = take(e * M * HD);
+  w->dk = take(e * M * HD);
+  w->dv = take(e * M * HD);
+  w->d_pre = take(e * Mp * W);
+  w->xt = take(e * d_model * Mp);
+  w->w1t = take(e * W * d_model);
+  w->attn = take(attn);
+  w->attn_bytes = attn;
+  *bytes = off;
+  return HSTU_OK;
+}
+
+hstu_status layer_bwd_check(int64_t M, int32_t batch, int32_t d_model, int32_t heads, int32_t head_dim) {
+  if (M < 0 || M >= ((int64_t)1 << 31) || batch < 0 || heads < 1)
+    return fail(HSTU_EINVAL, "bad sizes M=%lld batch=%d heads=%d", (long long)M, batch, heads);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(HSTU_EUNSUPPORTED, "head_dim %d is not supported", head_dim);
+  if (d_model <= 0 || d_model % 128 || ((int64_t)heads * head_dim) % 128)
+    return fail(HSTU_EUNSUPPORTED, "d_model (%d) and heads*head_dim (%d) must be multiples of 128",
+                d_model, heads * head_dim);
+  return HSTU_OK;
+}
+
+}  // namespace
+
+hstu_status hstu_layer_bwd_workspace_size(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
+                                          int32_t head_dim, size_t* bytes) {
+  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
+  LayerBwdWs w;
+  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, nullptr, &w, bytes);
+  if (st != HSTU_OK) return st;
+  return ok();
+}
+
+hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
+                           int32_t head_dim, const int64_t* seq_offsets, const int64_t* num_targets,
+                           const void* x, const void* w1, const float* b1, const void* w2,
+                           const void* uvqk, const float* a, float eps, const void* dy, void* dx,
+                           float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim);
+  if (st != HSTU_OK) return st;
+  if (!(eps >= 0.f)) return fail(HSTU_EINVAL, "eps must be >= 0");
+  if (batch > 0 && !seq_offsets) return fail(HSTU_EINVAL, "seq_offsets is NULL");
+  if (!dw1 || !db1 || !dw2 || !db2 || !w1 || !w2)
+    return fail(HSTU_EINVAL, "w1, w2, dw1, db1, dw2 and db2 are required");
+  if (M > 0 && (!x || !uvqk || !a || !dy || !dx))
+    return fail(HSTU_EINVAL, "x, uvqk, a, dy and dx are required");
+  const void* al[] = {x, w1, w2, uvqk, a, dy, dx, dw1, dw2};
+  for (const void* q : al)
+    if (!aligned(q, 16)) return fail(HSTU_EINVAL, "layer backward buffers must be 16-byte aligned");
+  LayerBwdWs w;
+  size_t need = 0;
+  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, nullptr, &w, &need);
+  if (st != HSTU_OK) return st;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  layer_bwd_carve(M, batch, d_model, heads, head_dim, workspace, &w, &need);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD, Mp = (M + 31) / 32 * 32;
+  if (M == 0) {                                  // no tokens: every gradient is 0
+    hipError_t z = launch_fill_f32(dw1, (int64_t)d_model * W, 0.f, s);
+    if (z == hipSuccess) z = launch_fill_f32(db1, W, 0.f, s);
+    if (z == hipSuccess) z = launch_fill_f32(dw2, HD * d_model, 0.f, s);
+    if (z == hipSuccess) z = launch_fill_f32(db2, d_model, 0.f, s);
+    if (z != hipSuccess) return hip_fail(z, "hstu_layer_bwd launch");
+    return ok();
+  }
+  const bf16* uv = reinterpret_cast<const bf16*>(uvqk);
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  // Z = LayerNorm(A) * U; dW2 = Z^T dY, db2 = colsum dY; dZ = dY W2^T
+  run(launch_linear(M, d_model, W, x, d_model, w1, b1, w.pre, 0, s));         // Pre = X W1 + b1
+  run(launch_layernorm_gate(M, HD, a, uv, W, eps, w.z, s));
+  run(launch_transpose_pad(M, HD, w.z, HD, w.zt, Mp, s));
+  run(launch_copy_pad_rows(M, Mp, d_model, dy, d_model, w.dyp, s));
+  run(launch_linear_f32(HD, Mp, d_model, w.zt, Mp, w.dyp, dw2, s));
+  run(launch_colsum(M, d_model, dy, d_model, db2, s));
+  run(launch_transpose_pad(HD, d_model, w2, d_model, w.w2t, HD, s));
+  run(launch_linear(M, d_model, HD, dy, d_model, w.w2t, nullptr, w.dz, 0, s));
+  // dU = dZ * LN(A), dA = LayerNorm'(A)^T (dZ * U)
+  run(launch_layernorm_gate_bwd(M, HD, a, uv, W, eps, w.dz, w.da, w.du, s));
+  if (e != hipSuccess) return hip_fail(e, "hstu_layer_bwd launch");
+  // attention backward (no gate, no bias) with dO = dA
+  if (M > 0 && batch > 0) {
+    hstu_attn_desc ad = {};
+    ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim; ad.max_len = 1;
+    ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
+    ad.stride_q = ad.stride_k = ad.stride_v = W; ad.stride_u = 0;
+    st = hstu_attn_bwd(&ad, seq_offsets, num_targets, nullptr, nullptr, nullptr, uv + 2 * HD,
+                       uv + 3 * HD, uv + HD, nullptr, nullptr, w.da, w.dq, w.dk, w.dv, nullptr,
+                       nullptr, nullptr, w.attn, w.attn_bytes, stream);
+    if (st != HSTU_OK) return st;
+  }
+  // dPre = [dU, dV, dQ, dK] * SiLU'(Pre); db1 = colsum dPre; dW1 = X^T dPre; dX = dPre W1^T
+  run(launch_silu_bwd_uvqk(M, Mp, HD, w.pre, w.du, w.dv, w.dq, w.dk, w.d_pre, s));
+  run(launch_colsum(M, W, w.d_pre, W, db1, s));
+  run(launch_transpose_pad(M, d_model, x, d_model, w.xt, Mp, s));
+  run(launch_linear_f32(d_model, Mp, W, w.xt, Mp, w.d_pre, dw1, s));
+  run(launch_transpose_pad(d_model, W, w1, W, w.w1t, d_model, s));
+  run(launch_linear(M, W, d_model, w.d_pre, W, w.w1t, nullptr, dx, 0, s));
+  if (e != hipSuccess) return hip_fail(e, "hstu_layer_bwd launch");
+  return ok();
+}
+
 const char* hstu_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

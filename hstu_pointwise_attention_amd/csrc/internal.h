@@ -126,6 +126,20 @@ hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
                          const void* w, const float* bias, void* y, int apply_silu,
                          hipStream_t s);
+// Layer backward pieces (layer.hip).
+hipError_t launch_linear_f32(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                             const void* w, float* y, hipStream_t s);
+hipError_t launch_layernorm_gate_bwd(int64_t M, int64_t N, const float* a, const void* u,
+                                     int64_t ldu, float eps, const void* dout, void* da, void* du,
+                                     hipStream_t s);
+hipError_t launch_transpose_pad(int64_t R, int64_t C, const void* x, int64_t ldx, void* y,
+                                int64_t ldy, hipStream_t s);
+hipError_t launch_copy_pad_rows(int64_t M, int64_t Mp, int64_t N, const void* x, int64_t ldx,
+                                void* y, hipStream_t s);
+hipError_t launch_colsum(int64_t M, int64_t N, const void* x, int64_t ldx, float* out, hipStream_t s);
+hipError_t launch_silu_bwd_uvqk(int64_t M, int64_t Mp, int64_t HD, const void* pre, const void* g0,
+                                const void* g1, const void* g2, const void* g3, void* d_pre,
+                                hipStream_t s);
 hipError_t launch_layernorm_gate(int64_t M, int64_t N, const float* a, const void* u,
                                  int64_t ldu, float eps, void* out, hipStream_t s);
 

@@ -224,3 +224,34 @@ def layernorm_gate(a, u, eps: float = 1e-5):
     _lib.check(lib.hstu_layernorm_gate(M, N, _ptr(a), _ptr(u), u.stride(0), float(eps), _ptr(out),
                                        _stream()))
     return out
+
+
+def layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a, dy,
+              eps: float = 1e-5):
+    """Gradients of one HSTU layer (hstu_layer_bwd): dict dx (bf16), dw1, db1, dw2, db2 (fp32).
+
+    x [M, d_model], w1 [d_model, 4*H*D], b1 [4*H*D], w2 [H*D, d_model] as in the
+    forward; uvqk [M, 4*H*D] and a [M, H*D] the forward's outputs; dy [M, d_model].
+    """
+    lib = _lib.load()
+    M, dm = x.shape
+    W = w1.shape[1]
+    x, w1, w2, uvqk, dy = (t.contiguous() for t in (x, w1, w2, uvqk, dy))
+    a = a.contiguous()
+    b1 = _f32c(b1)
+    seq_offsets, num_targets = _i64(seq_offsets), _i64(num_targets)
+    dev = x.device
+    dx = torch.empty((M, dm), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((dm, W), dtype=torch.float32, device=dev)
+    db1 = torch.empty((W,), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((w2.shape[0], dm), dtype=torch.float32, device=dev)
+    db2 = torch.empty((dm,), dtype=torch.float32, device=dev)
+    B = seq_offsets.numel() - 1
+    nbytes = ctypes.c_size_t()
+    _lib.check(lib.hstu_layer_bwd_workspace_size(M, B, dm, heads, head_dim, ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
+    _lib.check(lib.hstu_layer_bwd(M, B, dm, heads, head_dim, _ptr(seq_offsets), _ptr(num_targets),
+                                  _ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(uvqk), _ptr(a),
+                                  float(eps), _ptr(dy), _ptr(dx), _ptr(dw1), _ptr(db1), _ptr(dw2),
+                                  _ptr(db2), _ptr(ws), nbytes.value, _stream()))
+    return dict(dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2)

@@ -225,6 +225,38 @@ HSTU_API hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, c
                                 int64_t ldu, float eps, void* out, void* stream);
 
 /*
+ * hstu_layer_bwd: gradients of one HSTU layer (the steps of hstu_linear,
+ *   hstu_attn_fwd and hstu_layernorm_gate above, as the Generative
+ *   Recommenders README's "HSTU Ultra attention benchmark" lists them:
+ *   UVQK = SiLU(X W1 + b1), column blocks U, V, Q, K (head h at columns
+ *   [h*head_dim, (h+1)*head_dim) of each block), A = attention(Q, K, V; no
+ *   gate, no bias, num_targets candidates), Y = (LayerNorm(A) * U) W2 + b2)
+ *   from dY, by the chain rule of those steps (the README gives no backward;
+ *   this is the training of the layer it describes).
+ *   M tokens in `batch` jagged sequences (seq_offsets, num_targets as in
+ *   hstu_attn_fwd); d_model and heads*head_dim multiples of 128, head_dim in
+ *   {32, 64, 128}; bf16 storage.
+ *   x (device) bf16 [M, d_model]; w1 bf16 [d_model, 4*H*D]; b1 fp32 [4*H*D];
+ *   w2 bf16 [H*D, d_model]; uvqk bf16 [M, 4*H*D] and a fp32 [M, H*D] as the
+ *   forward produced them; eps the forward's LayerNorm epsilon; dy bf16
+ *   [M, d_model]. Outputs (overwritten): dx bf16 [M, d_model]; dw1 fp32
+ *   [d_model, 4*H*D]; db1 fp32 [4*H*D]; dw2 fp32 [H*D, d_model]; db2 fp32
+ *   [d_model]. Pre = X W1 + b1 is recomputed (not saved by the forward).
+ *   workspace (device) >= hstu_layer_bwd_workspace_size bytes, 256-aligned.
+ *   dQ, the bias gradients and the attention's own sums use floating-point
+ *   atomics, so their last bits may differ between runs.
+ */
+HSTU_API hstu_status hstu_layer_bwd_workspace_size(int64_t M, int32_t batch, int32_t d_model,
+                                                   int32_t heads, int32_t head_dim, size_t* bytes);
+HSTU_API hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
+                                    int32_t head_dim, const int64_t* seq_offsets,
+                                    const int64_t* num_targets, const void* x, const void* w1,
+                                    const float* b1, const void* w2, const void* uvqk,
+                                    const float* a, float eps, const void* dy, void* dx,
+                                    float* dw1, float* db1, float* dw2, float* db2,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing for benchmarks (off by default). Between
  * hstu_profile_begin() and hstu_profile_end() every kernel launch of the
  * library is bracketed by two HIP events recorded on the caller's stream.
