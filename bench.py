@@ -8,8 +8,9 @@ conversion, all through the C ABI on torch's current stream, inputs already
 in HBM. Throughput is algorithmic TFLOP/s over unmasked pairs only
 (forward 2*Dqk + 2*Dv, backward 6*Dqk + 4*Dv per pair and head).
 
-Prints one JSON line. Also measures the M-FALCON inference layer (forward)
-and times the CPU oracle on a bounded sample as a reported baseline.
+Prints one JSON line. Also measures one HSTU layer forward and backward at
+the M-FALCON shape and candidate scoring against a cached history, and times
+the CPU oracle on a bounded sample as a reported baseline.
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ def parse():
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--cached-only", action="store_true",
                     help="only time candidate scoring against a cached history")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="only time one HSTU layer forward and backward at the M-FALCON shape")
     return ap.parse_args()
 
 
@@ -87,7 +90,13 @@ def main():
 
     import workloads as W
     from hstu_pointwise_attention_amd import _lib, ops
-    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd
+    from hstu_pointwise_attention_amd.attention import hstu_layer_bwd, hstu_layer_fwd
+
+    if args.layer_only:
+        _lib.load()
+        print(json.dumps({"layer_mfalcon": bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd)}),
+              flush=True)
+        return
     from hstu_pointwise_attention_amd.flops import attention_flops
 
     _lib.load()
@@ -165,7 +174,7 @@ def main():
     }
 
     if not args.no_layer:
-        out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd)
+        out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd)
         out["cached_scoring"] = bench_cached(torch)
 
     if not args.no_cpu_baseline:
@@ -174,8 +183,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_layer(torch, W, hstu_layer_fwd, iters=10):
-    """M-FALCON-style inference layer forward: 4 users x (8192 history + 1024 candidates)."""
+def bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd, iters=10):
+    """One HSTU layer at the M-FALCON-style shape, 4 users x (8192 history + 1024
+    candidates): the forward, then the backward from a seeded dY (the forward's
+    UVQK and A reused, the projection pre-activation recomputed inside)."""
     from hstu_pointwise_attention_amd.flops import unmasked_pairs_host
     w = W.MFALCON_LAYER
     li = W.make_layer_inputs(w)
@@ -201,8 +212,26 @@ def bench_layer(torch, W, hstu_layer_fwd, iters=10):
     pairs = unmasked_pairs_host(li["lengths"], li["num_targets"]) * w.heads
     attn = pairs * 4 * w.head_dim
     gemm = 2 * T * w.model_dim * (4 * w.heads * w.head_dim) + 2 * T * (w.heads * w.head_dim) * w.model_dim
+    y, a, uvqk = hstu_layer_fwd(x, w1, b1, w2, b2, offs, nt, w.heads, w.head_dim)
+    g = torch.Generator(device=dev).manual_seed(1007)
+    dy = torch.randn(y.shape, generator=g, device=dev).to(torch.bfloat16)
+    for _ in range(2):
+        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_b = e0.elapsed_time(e1) / iters
+    # backward: attention 6*Dqk + 4*Dv per pair and head; each projection's
+    # dX and dW cost twice its forward (the pre-activation recompute is not counted)
+    attn_b = pairs * 10 * w.head_dim
+    gemm_b = 2 * gemm
     return {"ms": round(ms, 4), "tflops": round((attn + gemm) / (ms * 1e-3) / 1e12, 2),
-            "attn_flops": attn, "gemm_flops": gemm, "tokens": T}
+            "attn_flops": attn, "gemm_flops": gemm, "tokens": T,
+            "bwd_ms": round(ms_b, 4), "bwd_tflops": round((attn_b + gemm_b) / (ms_b * 1e-3) / 1e12, 2),
+            "bwd_attn_flops": attn_b, "bwd_gemm_flops": gemm_b}
 
 
 def bench_cached(torch, users=4, hist=8192, n_cand=1024, micro=128, heads=4, d=128, iters=5):

@@ -459,14 +459,16 @@ hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, const void
 namespace {
 
 struct LayerBwdWs {
-  void *pre, *z, *zt, *dyp, *w2t, *dz, *da, *du, *dq, *dk, *dv, *d_pre, *xt, *w1t, *attn;
+  void *pre, *z, *dz, *da, *du, *dq, *dk, *dv, *d_pre, *attn;
+  float* part;                                   // split partial sums of the weight gradients
+  float* cpart;                                  // per-band column sums (bias gradients)
   size_t attn_bytes;
 };
 
 // Carve-up of the layer backward's workspace (base == nullptr: sizes only).
 hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
                             int32_t head_dim, void* base, LayerBwdWs* w, size_t* bytes) {
-  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD, Mp = (M + 31) / 32 * 32;
+  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD;
   hstu_attn_desc ad = {};
   ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim; ad.max_len = 1;
   ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
@@ -483,18 +485,20 @@ hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t h
   const size_t e = 2;                            // bf16
   w->pre = take(e * M * W);
   w->z = take(e * M * HD);
-  w->zt = take(e * HD * Mp);
-  w->dyp = take(e * Mp * d_model);
-  w->w2t = take(e * d_model * HD);
   w->dz = take(e * M * HD);
   w->da = take(e * M * HD);
   w->du = take(e * M * HD);
   w->dq = take(e * M * HD);
   w->dk = take(e * M * HD);
   w->dv = take(e * M * HD);
-  w->d_pre = take(e * Mp * W);
-  w->xt = take(e * d_model * Mp);
-  w->w1t = take(e * W * d_model);
+  w->d_pre = take(e * M * W);
+  auto part_bytes = [&](int64_t m, int64_t n) {
+    const int sp = wgrad_splits(m, n, M);
+    return sp > 1 ? (size_t)sp * m * n * sizeof(float) : (size_t)0;
+  };
+  const size_t p2 = part_bytes(HD, d_model), p1 = part_bytes(d_model, W);
+  w->part = static_cast<float*>(take(p1 > p2 ? p1 : p2));
+  w->cpart = static_cast<float*>(take(sizeof(float) * colsum_bands(M) * (W > d_model ? W : d_model)));
   w->attn = take(attn);
   w->attn_bytes = attn;
   *bytes = off;
@@ -551,7 +555,7 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
                 workspace_bytes);
   layer_bwd_carve(M, batch, d_model, heads, head_dim, workspace, &w, &need);
   hipStream_t s = (hipStream_t)stream;
-  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD, Mp = (M + 31) / 32 * 32;
+  const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD;
   if (M == 0) {                                  // no tokens: every gradient is 0
     hipError_t z = launch_fill_f32(dw1, (int64_t)d_model * W, 0.f, s);
     if (z == hipSuccess) z = launch_fill_f32(db1, W, 0.f, s);
@@ -566,12 +570,9 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
   // Z = LayerNorm(A) * U; dW2 = Z^T dY, db2 = colsum dY; dZ = dY W2^T
   run(launch_linear(M, d_model, W, x, d_model, w1, b1, w.pre, 0, s));         // Pre = X W1 + b1
   run(launch_layernorm_gate(M, HD, a, uv, W, eps, w.z, s));
-  run(launch_transpose_pad(M, HD, w.z, HD, w.zt, Mp, s));
-  run(launch_copy_pad_rows(M, Mp, d_model, dy, d_model, w.dyp, s));
-  run(launch_linear_f32(HD, Mp, d_model, w.zt, Mp, w.dyp, dw2, s));
-  run(launch_colsum(M, d_model, dy, d_model, db2, s));
-  run(launch_transpose_pad(HD, d_model, w2, d_model, w.w2t, HD, s));
-  run(launch_linear(M, d_model, HD, dy, d_model, w.w2t, nullptr, w.dz, 0, s));
+  run(launch_wgrad(HD, d_model, M, w.z, HD, dy, d_model, dw2, w.part, s));
+  run(launch_colsum(M, d_model, dy, d_model, db2, w.cpart, s));
+  run(launch_linear_nt(M, d_model, HD, dy, d_model, w2, d_model, w.dz, s));
   // dU = dZ * LN(A), dA = LayerNorm'(A)^T (dZ * U)
   run(launch_layernorm_gate_bwd(M, HD, a, uv, W, eps, w.dz, w.da, w.du, s));
   if (e != hipSuccess) return hip_fail(e, "hstu_layer_bwd launch");
@@ -587,12 +588,10 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
     if (st != HSTU_OK) return st;
   }
   // dPre = [dU, dV, dQ, dK] * SiLU'(Pre); db1 = colsum dPre; dW1 = X^T dPre; dX = dPre W1^T
-  run(launch_silu_bwd_uvqk(M, Mp, HD, w.pre, w.du, w.dv, w.dq, w.dk, w.d_pre, s));
-  run(launch_colsum(M, W, w.d_pre, W, db1, s));
-  run(launch_transpose_pad(M, d_model, x, d_model, w.xt, Mp, s));
-  run(launch_linear_f32(d_model, Mp, W, w.xt, Mp, w.d_pre, dw1, s));
-  run(launch_transpose_pad(d_model, W, w1, W, w.w1t, d_model, s));
-  run(launch_linear(M, W, d_model, w.d_pre, W, w.w1t, nullptr, dx, 0, s));
+  run(launch_silu_bwd_uvqk(M, M, HD, w.pre, w.du, w.dv, w.dq, w.dk, w.d_pre, s));
+  run(launch_colsum(M, W, w.d_pre, W, db1, w.cpart, s));
+  run(launch_wgrad(d_model, W, M, x, d_model, w.d_pre, W, dw1, w.part, s));
+  run(launch_linear_nt(M, W, d_model, w.d_pre, W, w1, W, dx, s));
   if (e != hipSuccess) return hip_fail(e, "hstu_layer_bwd launch");
   return ok();
 }

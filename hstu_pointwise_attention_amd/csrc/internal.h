@@ -127,16 +127,23 @@ hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t
                          const void* w, const float* bias, void* y, int apply_silu,
                          hipStream_t s);
 // Layer backward pieces (layer.hip).
-hipError_t launch_linear_f32(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
-                             const void* w, float* y, hipStream_t s);
+// y[M,N] (bf16) = x[M,K] w^T, w stored [N][K] with row stride ldw.
+hipError_t launch_linear_nt(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                            const void* w, int64_t ldw, void* y, hipStream_t s);
+// y[M,N] (fp32) = a^T b, a stored [K][M] (row stride lda), b stored [K][N]
+// (row stride ldb); the reduction is split wgrad_splits(M, N, K) ways, the
+// splits' partial sums kept in part ([splits][M][N] fp32) when more than one.
+int wgrad_splits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_wgrad(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda, const void* b,
+                        int64_t ldb, float* y, float* part, hipStream_t s);
 hipError_t launch_layernorm_gate_bwd(int64_t M, int64_t N, const float* a, const void* u,
                                      int64_t ldu, float eps, const void* dout, void* da, void* du,
                                      hipStream_t s);
-hipError_t launch_transpose_pad(int64_t R, int64_t C, const void* x, int64_t ldx, void* y,
-                                int64_t ldy, hipStream_t s);
-hipError_t launch_copy_pad_rows(int64_t M, int64_t Mp, int64_t N, const void* x, int64_t ldx,
-                                void* y, hipStream_t s);
-hipError_t launch_colsum(int64_t M, int64_t N, const void* x, int64_t ldx, float* out, hipStream_t s);
+// out[N] = column sums of x [M][N] (N a multiple of 8); part holds
+// colsum_bands(M) x N floats of per-band sums.
+int64_t colsum_bands(int64_t M);
+hipError_t launch_colsum(int64_t M, int64_t N, const void* x, int64_t ldx, float* out, float* part,
+                         hipStream_t s);
 hipError_t launch_silu_bwd_uvqk(int64_t M, int64_t Mp, int64_t HD, const void* pre, const void* g0,
                                 const void* g1, const void* g2, const void* g3, void* d_pre,
                                 hipStream_t s);

@@ -1,79 +1,128 @@
 // HSTU layer pieces around the attention, bf16 storage with fp32 accumulation:
-//  - linear: y = act(x W + b), act = SiLU or identity (the UVQK projection and
-//    the output projection; in the backward, with fp32 output, the weight
-//    gradients from transposed operands);
+//  - GEMM: y = act(x W + b), act = SiLU or identity (the UVQK projection and
+//    the output projection); in the backward, x W^T (input gradients) and
+//    x^T g with fp32 output split over the token axis (weight gradients);
 //  - layernorm_gate: LayerNorm(a) * u over each token's features (the output
 //    normalisation and gating), and its backward;
-//  - the backward's small pieces: transposes, row padding, column sums and
-//    the SiLU derivative of the UVQK projection.
+//  - the backward's small pieces: column sums (bias gradients) and the SiLU
+//    derivative of the UVQK projection.
 #include "internal.h"
 
 namespace hstu {
 
 namespace {
 
-constexpr int GM = 128, GN = 128, GK = 32;       // workgroup tile
-constexpr int G_LD = GK + 8;                     // LDS row stride (elements): 80 bytes
-
-struct GemmSmem {
-  bf16 a[2][GM * G_LD];                          // x tile, row-major [m][k]
-  bf16 bt[2][GN * G_LD];                         // W tile, transposed [n][k]
-};
-
 __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * kNegLog2e));
 }
 
-// Wave (wm, wn) of the 2 x 2 arrangement computes a 64 x 64 sub-tile as
-// 2 x 2 blocks of 32 x 32.
-template <typename OutT>
-__global__ __launch_bounds__(256) void linear_kernel(int64_t M, int64_t K, int64_t N,
-                                                     const bf16* __restrict__ x, int64_t ldx,
-                                                     const bf16* __restrict__ w,
-                                                     const float* __restrict__ bias,
-                                                     OutT* __restrict__ y, int apply_silu) {
+// GEMM tiles: a workgroup computes a TM x TN block of the output, its four
+// waves 64 x 64 each as 2 x 2 blocks of 32 x 32 (MFMA 32x32x16 bf16), over
+// TK reduction indices per double-buffered LDS stage.
+constexpr int TM = 128, TN = 128, TK = 64;
+
+// An operand is stored either with the reduction index contiguous (KC: A as
+// [M][K], B as [N][K]) or strided (KS: A as [K][M], B as [K][N]). Its LDS tile
+// keeps the memory layout (16-byte copies, no transposes): KC tiles are
+// [128][TK] at row stride LDK, read as 16-byte row fragments; KS tiles are
+// [TK][128] at row stride LDT, read by transposing LDS loads. Both strides
+// keep the respective fragment reads free of bank conflicts.
+enum { KC = 0, KS = 1 };
+constexpr int LDK = TK + 8;
+constexpr int LDT = 128 + 16;
+constexpr int TILE = 128 * LDK;
+static_assert(TILE == TK * LDT, "both tile shapes fill one buffer");
+
+struct GemmSmem {
+  bf16 a[2][TILE];
+  bf16 b[2][TILE];
+};
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const bf16* a;                                 // A operand (rows m), layout LA
+  int64_t lda;
+  const bf16* b;                                 // B operand (columns n), layout LB
+  int64_t ldb;
+  const float* bias;                             // [N] or nullptr
+  void* y;                                       // [M][N] dense; with a K split, fp32 partials [split][M][N]
+  int64_t k_split;                               // reduction indices per split (multiple of TK)
+  int apply_silu;
+};
+
+// The TK x 128 slab of one operand at reduction indices k0..k0+TK-1 and rows
+// (m of A, n of B) r0..r0+127, as four 16-byte chunks per thread; elements at
+// k >= k_end or row >= R read as 0.
+template <int L>
+__device__ __forceinline__ void slab_load(u32x4 (&v)[4], const bf16* __restrict__ p, int64_t ld,
+                                          int64_t r0, int64_t R, int64_t k0, int64_t k_end,
+                                          int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    if constexpr (L == KC) {                     // 8 chunks of 8 k per row
+      const int64_t r = r0 + (c >> 3), k = k0 + 8 * (c & 7);
+      v[i] = (r < R && k < k_end) ? ld16(p + r * ld + k) : u32x4{0, 0, 0, 0};
+    } else {                                     // 16 chunks of 8 rows per k
+      const int64_t k = k0 + (c >> 4), r = r0 + 8 * (c & 15);
+      v[i] = (k < k_end && r < R) ? ld16(p + k * ld + r) : u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int L>
+__device__ __forceinline__ void slab_store(bf16* t, const u32x4 (&v)[4], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    if constexpr (L == KC)
+      st16(t + (c >> 3) * LDK + 8 * (c & 7), v[i]);
+    else
+      st16(t + (c >> 4) * LDT + 8 * (c & 15), v[i]);
+  }
+}
+
+// MFMA operand of tile rows rb..rb+31 at reduction indices kr..kr+15: lane
+// 32g + c holds row rb + c, indices kr + 8g .. kr + 8g + 7. For a KS tile
+// these are two transposing reads: in each 16-lane group, lane s addresses
+// row kr + 8g + (s >> 2) (then 4 rows further) at columns rb + 16((lane >> 4) & 1)
+// + 4(s & 3) .. +3, and receives column rb + (lane & 31) of the four rows.
+template <int L>
+__device__ __forceinline__ bf16x8 slab_frag(const bf16* t, int rb, int kr) {
+  const int l = threadIdx.x & 63, g = l >> 5;
+  if constexpr (L == KC) {
+    return ld_frag(t + (rb + (l & 31)) * LDK + kr + 8 * g);
+  } else {
+    const int s = l & 15;
+    const bf16* p0 = t + (kr + 8 * g + (s >> 2)) * LDT + rb + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * LDT));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, f);
+  }
+}
+
+// y[m][n] = act(sum_k A(m, k) B(k, n) + bias[n]) over one TM x TN tile and one
+// split of the reduction (blockIdx.y). Tiles are numbered row-major and, when
+// their count is a multiple of 8, dealt out so that each of the 8 XCDs (which
+// receive workgroups round-robin) takes a contiguous run of them: the tiles
+// of one row band then share that XCD's L2.
+template <int LA, int LB, typename OutT>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   __shared__ GemmSmem sm;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int l32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t n_tiles_n = N / GN;
-  const int64_t m0 = (blockIdx.x / n_tiles_n) * GM;
-  const int64_t n0 = (blockIdx.x % n_tiles_n) * GN;
-
-  // staging: A = 128 rows x 4 chunks of 16 B -> 2 per thread;
-  //          W = 16 k-pairs x 16 n-chunks -> 1 unit (2 loads) per thread.
-  u32x4 areg[2], breg[2];
-  auto load = [&](int64_t k0) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int ch = tid + 256 * m;
-      const int row = ch >> 2, cc = ch & 3;
-      const int64_t gm = m0 + row;
-      areg[m] = gm < M ? ld16(x + gm * ldx + k0 + 8 * cc) : u32x4{0, 0, 0, 0};
-    }
-    const int kp = tid >> 4, nc = tid & 15;
-    const bf16* src = w + (k0 + 2 * kp) * N + n0 + 8 * nc;
-    breg[0] = ld16(src);
-    breg[1] = ld16(src + N);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int ch = tid + 256 * m;
-      const int row = ch >> 2, cc = ch & 3;
-      st16(sm.a[buf] + row * G_LD + 8 * cc, areg[m]);
-    }
-    const int kp = tid >> 4, nc = tid & 15;
-    const bf16* r0 = reinterpret_cast<const bf16*>(&breg[0]);
-    const bf16* r1 = reinterpret_cast<const bf16*>(&breg[1]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16* dst = sm.bt[buf] + (8 * nc + e) * G_LD + 2 * kp;
-      dst[0] = r0[e];
-      dst[1] = r1[e];
-    }
-  };
+  const int64_t tiles_n = (p.N + TN - 1) / TN;
+  const int64_t tiles = ((p.M + TM - 1) / TM) * tiles_n;
+  int64_t t = blockIdx.x;
+  if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+  const int64_t m0 = (t / tiles_n) * TM, n0 = (t % tiles_n) * TN;
+  const int64_t kb = (int64_t)blockIdx.y * p.k_split;
+  const int64_t ke = kb + p.k_split < p.K ? kb + p.k_split : p.K;
+  const int64_t nk = ke > kb ? (ke - kb + TK - 1) / TK : 0;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -83,48 +132,77 @@ __global__ __launch_bounds__(256) void linear_kernel(int64_t M, int64_t K, int64
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int64_t nk = K / GK;
-  load(0);
-  store(0);
+  // Stage kt is in LDS buffer kt & 1 while stage kt + 1 arrives in registers.
+  u32x4 ra[4], rb[4];
+  if (nk > 0) {
+    slab_load<LA>(ra, p.a, p.lda, m0, p.M, kb, ke, tid);
+    slab_load<LB>(rb, p.b, p.ldb, n0, p.N, kb, ke, tid);
+    slab_store<LA>(sm.a[0], ra, tid);
+    slab_store<LB>(sm.b[0], rb, tid);
+  }
   __syncthreads();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
     const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * GK);
+    if (more) {
+      slab_load<LA>(ra, p.a, p.lda, m0, p.M, kb + (kt + 1) * TK, ke, tid);
+      slab_load<LB>(rb, p.b, p.ldb, n0, p.N, kb + (kt + 1) * TK, ke, tid);
+    }
+    const bf16* ta = sm.a[buf];
+    const bf16* tb = sm.b[buf];
 #pragma unroll
-    for (int c = 0; c < GK / 16; ++c) {
+    for (int c = 0; c < TK / 16; ++c) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = ld_frag(sm.a[buf] + (64 * wm + 32 * a + l32) * G_LD + 16 * c + 8 * g);
+      for (int a = 0; a < 2; ++a) af[a] = slab_frag<LA>(ta, 64 * wm + 32 * a, 16 * c);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[b] = ld_frag(sm.bt[buf] + (64 * wn + 32 * b + l32) * G_LD + 16 * c + 8 * g);
+      for (int b = 0; b < 2; ++b) bfr[b] = slab_frag<LB>(tb, 64 * wn + 32 * b, 16 * c);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) mfma_32x32x16(acc[a][b], af[a], bfr[b]);
     }
-    if (more) store(buf ^ 1);
+    if (more) {
+      slab_store<LA>(sm.a[buf ^ 1], ra, tid);
+      slab_store<LB>(sm.b[buf ^ 1], rb, tid);
+    }
     __syncthreads();
   }
 
+  OutT* y = reinterpret_cast<OutT*>(p.y) + (int64_t)blockIdx.y * p.M * p.N;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int64_t n = n0 + 64 * wn + 32 * b + l32;
-    const float bv = bias ? bias[n] : 0.f;
+    if (n >= p.N) continue;
+    const float bv = p.bias ? p.bias[n] : 0.f;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M) {
+        if (m < p.M) {
           float z = acc[a][b][r] + bv;
-          if (apply_silu) z = silu_f(z);
-          y[m * N + n] = (OutT)z;
+          if (p.apply_silu) z = silu_f(z);
+          y[m * p.N + n] = (OutT)z;
         }
       }
     }
+  }
+}
+
+// out[e] = sum over s < splits of part[s * stride + e], four floats per thread.
+__global__ __launch_bounds__(256) void split_sum_kernel(int64_t n4, int splits, int64_t stride,
+                                                        const float* __restrict__ part,
+                                                        float* __restrict__ out) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + 4 * e);
+    for (int sp = 1; sp < splits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + sp * stride + 4 * e);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] += v[m];
+    }
+    *reinterpret_cast<f32x4*>(out + 4 * e) = acc;
   }
 }
 
@@ -221,48 +299,66 @@ __global__ __launch_bounds__(256) void layernorm_gate_bwd_kernel(
   }
 }
 
-// y[c][r] = x[r][c] for r < R, 0 for R <= r < ldy (columns of y padded to
-// ldy); 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_pad_kernel(int64_t R, int64_t C,
-                                                           const bf16* __restrict__ x, int64_t ldx,
-                                                           bf16* __restrict__ y, int64_t ldy) {
-  __shared__ bf16 t[64][65];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    t[i][tx] = (r < R && c < C) ? x[r * ldx + c] : (bf16)0.f;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < ldy) y[c * ldy + r] = t[tx][i];
-  }
-}
+// Column sums in two deterministic passes. colsum_kernel: part[band][c] =
+// sum of x[r][c] over the band's 128 rows; threads take 8 columns each
+// (16-byte loads), cw threads across the column chunks of the block and
+// 256 / cw rows at a time, the row groups then summed through LDS.
+// rows_sum_kernel: out[c] = sum over bands of part[band][c], 32 float4
+// column chunks x 8 band lanes per block.
+constexpr int kColsumRows = 128;
 
-// y[r][:] = x[r][:] for r < M, 0 for M <= r < Mp; N a multiple of 8.
-__global__ __launch_bounds__(256) void copy_pad_rows_kernel(int64_t M, int64_t Mp, int64_t N,
-                                                            const bf16* __restrict__ x, int64_t ldx,
-                                                            bf16* __restrict__ y) {
-  const int64_t n8 = N / 8;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < Mp * n8;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / n8, c = 8 * (e - r * n8);
-    const u32x4 v = r < M ? ld16(x + r * ldx + c) : u32x4{0, 0, 0, 0};
-    st16(y + r * N + c, v);
-  }
-}
-
-// out[c] += sum over rows r of x[r][c] (fp32 atomics; out cleared by the
-// caller): each thread one column of a 256-row chunk.
 __global__ __launch_bounds__(256) void colsum_kernel(int64_t M, int64_t N, const bf16* __restrict__ x,
-                                                     int64_t ldx, float* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= N) return;
-  const int64_t r0 = (int64_t)blockIdx.y * 256, r1 = r0 + 256 < M ? r0 + 256 : M;
-  float sum = 0.f;
-  for (int64_t r = r0; r < r1; ++r) sum += (float)x[r * ldx + c];
-  atomicAdd(out + c, sum);
+                                                     int64_t ldx, float* __restrict__ part) {
+  __shared__ float red[256 * 8];
+  const int64_t n8 = N / 8;
+  const int cw = n8 < 256 ? (int)n8 : 256, nr = 256 / cw;
+  const int tid = threadIdx.x, cx = tid % cw, ry = tid / cw;
+  const int64_t c = (int64_t)blockIdx.x * cw + cx;
+  const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
+  const int64_t r1 = r0 + kColsumRows < M ? r0 + kColsumRows : M;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (ry < nr && c < n8) {
+#pragma unroll 4
+    for (int64_t r = r0 + ry; r < r1; r += nr) {
+      const u32x4 v = ld16(x + r * ldx + 8 * c);
+      const bf16* e = reinterpret_cast<const bf16*>(&v);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] += (float)e[m];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) red[tid * 8 + m] = acc[m];
+  __syncthreads();
+  if (ry == 0 && c < n8) {
+    for (int k = 1; k < nr; ++k)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] += red[(k * cw + cx) * 8 + m];
+    float* dst = part + (int64_t)blockIdx.y * N + 8 * c;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+__global__ __launch_bounds__(256) void rows_sum_kernel(int64_t R, int64_t N, const float* __restrict__ part,
+                                                       float* __restrict__ out) {
+  __shared__ f32x4 red[256];
+  const int tid = threadIdx.x, cx = tid & 31, ry = tid >> 5;
+  const int64_t c4 = (int64_t)blockIdx.x * 32 + cx;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (4 * c4 < N)
+    for (int64_t r = ry; r < R; r += 8) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + r * N + 4 * c4);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] += v[m];
+    }
+  red[tid] = acc;
+  __syncthreads();
+  if (ry == 0 && 4 * c4 < N) {
+    for (int k = 1; k < 8; ++k)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] += red[32 * k + cx][m];
+    *reinterpret_cast<f32x4*>(out + 4 * c4) = acc;
+  }
 }
 
 // d_pre[m][c] = g[m][c] * SiLU'(pre[m][c]) over the 4 * HD columns of the
@@ -300,28 +396,60 @@ __global__ __launch_bounds__(256) void silu_bwd_uvqk_kernel(int64_t M, int64_t M
 
 }  // namespace
 
-hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
-                         const void* w, const float* bias, void* y, int apply_silu,
-                         hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  const int64_t grid = ((M + GM - 1) / GM) * (N / GN);
+namespace {
+
+template <int LA, int LB, typename OutT>
+hipError_t launch_gemm(const GemmArgs& g, int splits, hipStream_t s) {
+  const int64_t tiles = ((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
   prof_before(kKLinear, s);
-  hipLaunchKernelGGL(linear_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, s, M, K, N,
-                     reinterpret_cast<const bf16*>(x), ldx, reinterpret_cast<const bf16*>(w),
-                     bias, reinterpret_cast<bf16*>(y), apply_silu);
+  hipLaunchKernelGGL((gemm_kernel<LA, LB, OutT>), dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, s, g);
   prof_after(kKLinear, s);
   return hipGetLastError();
 }
 
-hipError_t launch_linear_f32(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
-                             const void* w, float* y, hipStream_t s) {
+}  // namespace
+
+hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                         const void* w, const float* bias, void* y, int apply_silu,
+                         hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const int64_t grid = ((M + GM - 1) / GM) * (N / GN);
-  prof_before(kKLinear, s);
-  hipLaunchKernelGGL(linear_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, M, K, N,
-                     reinterpret_cast<const bf16*>(x), ldx, reinterpret_cast<const bf16*>(w),
-                     nullptr, y, 0);
-  prof_after(kKLinear, s);
+  const GemmArgs g = {M, N, K, reinterpret_cast<const bf16*>(x), ldx,
+                      reinterpret_cast<const bf16*>(w), N, bias, y, K, apply_silu};
+  return launch_gemm<KC, KS, bf16>(g, 1, s);
+}
+
+hipError_t launch_linear_nt(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,
+                            const void* w, int64_t ldw, void* y, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const GemmArgs g = {M, N, K, reinterpret_cast<const bf16*>(x), ldx,
+                      reinterpret_cast<const bf16*>(w), ldw, nullptr, y, K, 0};
+  return launch_gemm<KC, KC, bf16>(g, 1, s);
+}
+
+// Splits of the reduction for a weight gradient: enough workgroups to cover
+// the chip about three times over, at least 8 stages of TK per split.
+int wgrad_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+  int64_t sp = (768 + tiles - 1) / tiles;
+  const int64_t by_k = K / (8 * TK);
+  if (sp > by_k) sp = by_k;
+  if (sp > 64) sp = 64;
+  return sp < 1 ? 1 : (int)sp;
+}
+
+hipError_t launch_wgrad(int64_t M, int64_t N, int64_t K, const void* a, int64_t lda, const void* b,
+                        int64_t ldb, float* y, float* part, hipStream_t s) {
+  const int splits = wgrad_splits(M, N, K);
+  int64_t k_split = (K + splits - 1) / splits;
+  k_split = (k_split + TK - 1) / TK * TK;
+  const GemmArgs g = {M, N, K, reinterpret_cast<const bf16*>(a), lda,
+                      reinterpret_cast<const bf16*>(b), ldb, nullptr,
+                      splits > 1 ? (void*)part : (void*)y, k_split, 0};
+  hipError_t e = launch_gemm<KS, KS, float>(g, splits, s);
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n4 = M * N / 4, blocks = (n4 + 255) / 256;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                     n4, splits, M * N, part, y);
   return hipGetLastError();
 }
 
@@ -337,29 +465,16 @@ hipError_t launch_layernorm_gate_bwd(int64_t M, int64_t N, const float* a, const
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_pad(int64_t R, int64_t C, const void* x, int64_t ldx, void* y,
-                                int64_t ldy, hipStream_t s) {
-  if (C == 0 || ldy == 0) return hipSuccess;
-  const dim3 g((unsigned)((ldy + 63) / 64), (unsigned)((C + 63) / 64));
-  hipLaunchKernelGGL(transpose_pad_kernel, g, dim3(256), 0, s, R, C, reinterpret_cast<const bf16*>(x),
-                     ldx, reinterpret_cast<bf16*>(y), ldy);
-  return hipGetLastError();
-}
+int64_t colsum_bands(int64_t M) { return (M + kColsumRows - 1) / kColsumRows; }
 
-hipError_t launch_copy_pad_rows(int64_t M, int64_t Mp, int64_t N, const void* x, int64_t ldx,
-                                void* y, hipStream_t s) {
-  if (Mp == 0) return hipSuccess;
-  const int64_t n = Mp * (N / 8), blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(copy_pad_rows_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
-                     M, Mp, N, reinterpret_cast<const bf16*>(x), ldx, reinterpret_cast<bf16*>(y));
-  return hipGetLastError();
-}
-
-hipError_t launch_colsum(int64_t M, int64_t N, const void* x, int64_t ldx, float* out, hipStream_t s) {
-  hipError_t e = launch_fill_f32(out, N, 0.f, s);
-  if (e != hipSuccess || M == 0) return e;
-  const dim3 g((unsigned)((N + 255) / 256), (unsigned)((M + 255) / 256));
-  hipLaunchKernelGGL(colsum_kernel, g, dim3(256), 0, s, M, N, reinterpret_cast<const bf16*>(x), ldx, out);
+hipError_t launch_colsum(int64_t M, int64_t N, const void* x, int64_t ldx, float* out, float* part,
+                         hipStream_t s) {
+  if (M == 0) return launch_fill_f32(out, N, 0.f, s);
+  const int64_t n8 = N / 8, cw = n8 < 256 ? n8 : 256, bands = colsum_bands(M);
+  const dim3 g((unsigned)((n8 + cw - 1) / cw), (unsigned)bands);
+  hipLaunchKernelGGL(colsum_kernel, g, dim3(256), 0, s, M, N, reinterpret_cast<const bf16*>(x), ldx, part);
+  hipLaunchKernelGGL(rows_sum_kernel, dim3((unsigned)((N / 4 + 31) / 32)), dim3(256), 0, s, bands, N,
+                     (const float*)part, out);
   return hipGetLastError();
 }
 
