@@ -31,7 +31,9 @@ logistic sigmoid; dQ = dS K, dK = dS^T Q, dV = P^T dA, and each rab table's
 gradient is the sum of dS over the unmasked pairs that read that entry
 (summed over heads when one table is shared by all heads).
 
-Every step is float64 (bf16 inputs are taken as the exact values they hold).
+Every step is float64 (bf16 inputs are taken as the exact values they hold),
+except FP8 quantisation (``oracle.fp8``), whose codes are integers decided in
+float32, the kernel's precision.
 Which checks pin these functions is stated in each function's docstring and
 in ``tests/test_oracle_*.py``.
 """
@@ -39,6 +41,7 @@ from .buckets import position_buckets, time_buckets, bit_length_u64
 from .attention import attention_fwd, attention_bwd, attention_fwd_rows, silu
 from .scalar import scalar_attention_fwd, scalar_attention_bwd
 from .layer import layer_fwd, layernorm
+from . import fp8
 
 __all__ = [
     "position_buckets", "time_buckets", "bit_length_u64",
