@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HSTU jagged attn fwd+bwd TFLOP/s @ max_len 8192; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE) scaled by the copy-kernel calibration; the
 # summaries are under profiles/. None when not measured for the kernel as it
@@ -51,6 +52,8 @@ def parse():
                     help="only run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--cached-only", action="store_true",
                     help="only time candidate scoring against a cached history")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only time the FP8 projection GEMMs")
     ap.add_argument("--layer-only", action="store_true",
                     help="only time one HSTU layer forward and backward at the M-FALCON shape")
     return ap.parse_args()
@@ -91,6 +94,11 @@ def main():
     import workloads as W
     from hstu_pointwise_attention_amd import _lib, ops
     from hstu_pointwise_attention_amd.attention import hstu_layer_bwd, hstu_layer_fwd
+
+    if args.fp8_only:
+        _lib.load()
+        print(json.dumps({"fp8_linear": bench_fp8(torch)}), flush=True)
+        return
 
     if args.layer_only:
         _lib.load()
@@ -176,6 +184,7 @@ def main():
     if not args.no_layer:
         out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd)
         out["cached_scoring"] = bench_cached(torch)
+        out["fp8_linear"] = bench_fp8(torch)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl)
@@ -273,6 +282,47 @@ def bench_cached(torch, users=4, hist=8192, n_cand=1024, micro=128, heads=4, d=1
             "shape": f"{users} users x {hist} history rows, {n_cand} candidates in micro-batches "
                      f"of {micro}, H {heads}, D {d}, bf16, no bias",
             "pair_heads": pairs, "flops": flops}
+
+
+def bench_fp8(torch, iters=20):
+    """FP8 (E4M3) projection GEMMs with prepared weights: the README's FP8 addmm
+    benchmark shape (m 4096, k 512, n 512) and the M-FALCON layer's two
+    projections (36864 tokens, 512 -> 2048 with SiLU, 512 -> 512), each
+    beside the bf16 GEMM of the same shape; the activation quantisation
+    (row-wise, from bf16) is timed on its own. Seeded synthetic inputs."""
+    from hstu_pointwise_attention_amd import ops
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(1008)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    out = {}
+    for name, (M, K, N, act) in {"m4096_k512_n512": (4096, 512, 512, False),
+                                 "layer_uvqk_36864_512_2048": (36864, 512, 2048, True),
+                                 "layer_out_36864_512_512": (36864, 512, 512, False)}.items():
+        x = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+        w = (torch.randn(K, N, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+        b = torch.randn(N, generator=g, device=dev)
+        wq, ws = ops.fp8_prepare_weight(w)
+        xq, xs = ops.fp8_quantize_rows(x)
+        ms8 = timed(lambda: ops.fp8_linear(xq, xs, wq, ws, b, silu=act))
+        msq = timed(lambda: ops.fp8_quantize_rows(x))
+        ms16 = timed(lambda: ops.linear(x, w, b, silu=act))
+        fl = 2 * M * K * N
+        out[name] = {"fp8_gemm_ms": round(ms8, 4), "fp8_tflops": round(fl / (ms8 * 1e-3) / 1e12, 2),
+                     "pct_of_fp8_peak": round(100 * fl / (ms8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+                     "quantize_ms": round(msq, 4), "bf16_gemm_ms": round(ms16, 4),
+                     "bf16_tflops": round(fl / (ms16 * 1e-3) / 1e12, 2), "flops": fl}
+    return out
 
 
 def cpu_baseline(inp, wl):

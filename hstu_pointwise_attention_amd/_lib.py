@@ -27,6 +27,8 @@ EXPORTS = ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size", "hstu
            "hstu_attn_fwd_cached_workspace_size", "hstu_attn_fwd_cached",
            "hstu_attn_bwd", "hstu_rab_bucketize", "hstu_linear", "hstu_layernorm_gate",
            "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
+           "hstu_fp8_quantize_rows", "hstu_fp8_prepare_weight", "hstu_fp8_linear",
+           "hstu_layernorm_gate_fp8",
            "hstu_profile_begin", "hstu_profile_end", "hstu_kernel_name", "hstu_kernel_count",
            "hstu_last_error")
 
@@ -76,6 +78,10 @@ _SIGS = {
     "hstu_layer_bwd": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                        _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
                        ctypes.c_size_t, _P],
+    "hstu_fp8_quantize_rows": [_I64, _I64, _P, _I64, _P, _P, _P],
+    "hstu_fp8_prepare_weight": [_I64, _I64, _P, _P, _P, _P],
+    "hstu_fp8_linear": [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P],
+    "hstu_layernorm_gate_fp8": [_I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _P],
     "hstu_profile_begin": [],
     "hstu_profile_end": [ctypes.c_int32, _P, _P],
     "hstu_kernel_count": [],

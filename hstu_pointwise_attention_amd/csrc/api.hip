@@ -455,6 +455,55 @@ hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, const void
   return ok();
 }
 
+// ---------------------------------------------------------------- FP8 projection
+hstu_status hstu_fp8_quantize_rows(int64_t M, int64_t K, const void* x, int64_t ldx, void* q,
+                                   float* scale, void* stream) {
+  if (M < 0 || K <= 0) return fail(HSTU_EINVAL, "bad sizes M=%lld K=%lld", (long long)M, (long long)K);
+  if (K % 16) return fail(HSTU_EUNSUPPORTED, "K must be a multiple of 16");
+  if (ldx < K || ldx % 8) return fail(HSTU_EINVAL, "ldx %lld must be >= K and a multiple of 8", (long long)ldx);
+  if (M > 0 && (!x || !q || !scale)) return fail(HSTU_EINVAL, "x, q and scale are required");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(HSTU_EINVAL, "x and q must be 16-byte aligned");
+  hipError_t e = launch_fp8_quantize_rows(M, K, x, ldx, q, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_fp8_quantize_rows launch");
+  return ok();
+}
+
+hstu_status hstu_fp8_prepare_weight(int64_t K, int64_t N, const void* w, void* q, float* scale,
+                                    void* stream) {
+  if (K <= 0 || N < 0) return fail(HSTU_EINVAL, "bad sizes K=%lld N=%lld", (long long)K, (long long)N);
+  if (K % 16) return fail(HSTU_EUNSUPPORTED, "K must be a multiple of 16");
+  if (N > 0 && (!w || !q || !scale)) return fail(HSTU_EINVAL, "w, q and scale are required");
+  if (!aligned(w, 2) || !aligned(q, 16)) return fail(HSTU_EINVAL, "misaligned w or q");
+  hipError_t e = launch_fp8_prepare_weight(K, N, w, q, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_fp8_prepare_weight launch");
+  return ok();
+}
+
+hstu_status hstu_fp8_linear(int64_t M, int64_t K, int64_t N, const void* xq, const float* x_scale,
+                            const void* wq, const float* w_scale, const float* bias, void* y,
+                            int32_t apply_silu, void* stream) {
+  if (M < 0 || K <= 0 || N < 0) return fail(HSTU_EINVAL, "bad sizes M=%lld K=%lld N=%lld", (long long)M, (long long)K, (long long)N);
+  if (K % 16) return fail(HSTU_EUNSUPPORTED, "K must be a multiple of 16");
+  if (M > 0 && N > 0 && (!xq || !x_scale || !wq || !w_scale || !y))
+    return fail(HSTU_EINVAL, "xq, x_scale, wq, w_scale and y are required");
+  if (!aligned(xq, 16) || !aligned(wq, 16)) return fail(HSTU_EINVAL, "xq and wq must be 16-byte aligned");
+  hipError_t e = launch_fp8_linear(M, K, N, xq, x_scale, wq, w_scale, bias, y, apply_silu, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_fp8_linear launch");
+  return ok();
+}
+
+hstu_status hstu_layernorm_gate_fp8(int64_t M, int64_t N, const float* a, const void* u, int64_t ldu,
+                                    float eps, void* q, float* scale, void* stream) {
+  if (M < 0 || N <= 0 || N % 64 || N > 4096) return fail(HSTU_EINVAL, "N must be a positive multiple of 64, <= 4096");
+  if (u && (ldu < N || ldu % 4)) return fail(HSTU_EINVAL, "ldu %lld must be >= N and a multiple of 4", (long long)ldu);
+  if (!(eps >= 0.f)) return fail(HSTU_EINVAL, "eps must be >= 0");
+  if (M > 0 && (!a || !q || !scale)) return fail(HSTU_EINVAL, "a, q and scale are required");
+  if (!aligned(a, 16) || !aligned(u, 8) || !aligned(q, 4)) return fail(HSTU_EINVAL, "misaligned buffer");
+  hipError_t e = launch_layernorm_gate_fp8(M, N, a, u, ldu, eps, q, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_layernorm_gate_fp8 launch");
+  return ok();
+}
+
 // ---------------------------------------------------------------- layer backward
 namespace {
 

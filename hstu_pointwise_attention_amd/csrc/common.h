@@ -120,6 +120,37 @@ __device__ __forceinline__ void st4_from_f32(bf16* p, f32x4 v) {
 }
 __device__ __forceinline__ void st4_from_f32(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
+// Output tiles of the 128 x 128 GEMMs leave through LDS: the waves write
+// their MFMA results at [row][col] with row stride tile_ld<T>() elements
+// (rows 4 apart, written by the two lane halves, land 128 bytes apart in
+// the banks), then the workgroup copies
+// rows out as 16-byte chunks. Element-wise stores straight from the MFMA
+// layout would write 2 or 4 bytes per lane, scattered over rows, and cost
+// more than the whole reduction at short K.
+template <typename T> __device__ __forceinline__ constexpr int tile_ld() { return 128 + 32 / (int)sizeof(T); }
+
+// Copies rows [0, 128) x cols [0, 128) of the LDS tile t to y[m0 + r][n0 + c]
+// (row stride ldy elements), skipping rows >= M and columns >= N; 256 threads.
+template <typename T>
+__device__ __forceinline__ void copy_tile_out(const T* t, T* __restrict__ y, int64_t ldy, int64_t m0,
+                                              int64_t n0, int64_t M, int64_t N) {
+  constexpr int EPC = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  constexpr int CPR = 128 / EPC;                 // chunks per row
+  const bool vec = ((uintptr_t)y % 16 == 0) && (ldy % EPC == 0);
+  for (int c = (int)threadIdx.x; c < 128 * CPR; c += 256) {
+    const int row = c / CPR, cc = c % CPR;
+    const int64_t m = m0 + row, n = n0 + (int64_t)cc * EPC;
+    if (m >= M || n >= N) continue;
+    const T* src = t + row * tile_ld<T>() + cc * EPC;
+    T* dst = y + m * ldy + n;
+    if (vec && n + EPC <= N) {
+      st16(dst, ld16(src));
+    } else {
+      for (int e = 0; e < EPC && n + e < N; ++e) dst[e] = src[e];
+    }
+  }
+}
+
 // Sum over the 64 lanes, returned to every lane. DPP adds within each 16-lane
 // row (quad swaps, then half-row and row mirrors) stay in the VALU; the four
 // row sums then come out through readlane. A shuffle ladder would instead make

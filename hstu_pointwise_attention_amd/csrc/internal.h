@@ -75,7 +75,7 @@ constexpr int kWideGrid = 512;
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
   kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
-  kKBucketize, kNumKernelIds
+  kKBucketize, kKFp8Linear, kKFp8Quant, kNumKernelIds
 };
 // Records a HIP event on `s` before / after a launch when timing is enabled.
 void prof_before(int id, hipStream_t s);
@@ -149,5 +149,16 @@ hipError_t launch_silu_bwd_uvqk(int64_t M, int64_t Mp, int64_t HD, const void* p
                                 hipStream_t s);
 hipError_t launch_layernorm_gate(int64_t M, int64_t N, const float* a, const void* u,
                                  int64_t ldu, float eps, void* out, hipStream_t s);
+
+// FP8 (E4M3FN) projection pieces (fp8.hip).
+hipError_t launch_fp8_quantize_rows(int64_t M, int64_t K, const void* x, int64_t ldx, void* q,
+                                    float* scale, hipStream_t s);
+hipError_t launch_fp8_prepare_weight(int64_t K, int64_t N, const void* w, void* q, float* scale,
+                                     hipStream_t s);
+hipError_t launch_fp8_linear(int64_t M, int64_t K, int64_t N, const void* xq, const float* x_scale,
+                             const void* wq, const float* w_scale, const float* bias, void* y,
+                             int apply_silu, hipStream_t s);
+hipError_t launch_layernorm_gate_fp8(int64_t M, int64_t N, const float* a, const void* u,
+                                     int64_t ldu, float eps, void* q, float* scale, hipStream_t s);
 
 }  // namespace hstu

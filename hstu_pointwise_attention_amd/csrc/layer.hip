@@ -169,25 +169,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  OutT* y = reinterpret_cast<OutT*>(p.y) + (int64_t)blockIdx.y * p.M * p.N;
+  // The loop's last barrier has retired every read of the stage buffers, so
+  // the output tile is staged in their place.
+  static_assert(128 * tile_ld<OutT>() * sizeof(OutT) <= sizeof(GemmSmem), "output tile fits");
+  OutT* ts = reinterpret_cast<OutT*>(&sm);
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int64_t n = n0 + 64 * wn + 32 * b + l32;
-    if (n >= p.N) continue;
-    const float bv = p.bias ? p.bias[n] : 0.f;
+    const int nl = 64 * wn + 32 * b + l32;
+    const float bv = (p.bias && n0 + nl < p.N) ? p.bias[n0 + nl] : 0.f;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < p.M) {
-          float z = acc[a][b][r] + bv;
-          if (p.apply_silu) z = silu_f(z);
-          y[m * p.N + n] = (OutT)z;
-        }
+        const int ml = 64 * wm + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+        float z = acc[a][b][r] + bv;
+        if (p.apply_silu) z = silu_f(z);
+        ts[ml * tile_ld<OutT>() + nl] = (OutT)z;
       }
     }
   }
+  __syncthreads();
+  copy_tile_out(ts, reinterpret_cast<OutT*>(p.y) + (int64_t)blockIdx.y * p.M * p.N, p.N, m0, n0, p.M, p.N);
 }
 
 // out[e] = sum over s < splits of part[s * stride + e], four floats per thread.

@@ -226,6 +226,58 @@ def layernorm_gate(a, u, eps: float = 1e-5):
     return out
 
 
+def fp8_quantize_rows(x):
+    """Row-wise E4M3 codes (uint8 [M, K]) and scales (fp32 [M]) of bf16 x [M, K]."""
+    lib = _lib.load()
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must have a contiguous last dim")
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _lib.check(lib.hstu_fp8_quantize_rows(M, K, _ptr(x), x.stride(0), _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
+def fp8_prepare_weight(w):
+    """Codes [N, K] and per-output-feature scales [N] of a bf16 weight w [K, N]."""
+    lib = _lib.load()
+    K, N = w.shape
+    w = w.contiguous()
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((N,), dtype=torch.float32, device=w.device)
+    _lib.check(lib.hstu_fp8_prepare_weight(K, N, _ptr(w), _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
+def fp8_linear(xq, x_scale, wq, w_scale, bias=None, silu: bool = False):
+    """y = act(x_scale w_scale (xq wq^T) + bias), bf16 [M, N]; xq [M, K], wq [N, K] E4M3 codes."""
+    lib = _lib.load()
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("wq must be [N, K]")
+    xq, wq = xq.contiguous(), wq.contiguous()
+    x_scale, w_scale, bias = _f32c(x_scale), _f32c(w_scale), _f32c(bias)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _lib.check(lib.hstu_fp8_linear(M, K, N, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale),
+                                   _ptr(bias), _ptr(y), 1 if silu else 0, _stream()))
+    return y
+
+
+def layernorm_gate_fp8(a, u=None, eps: float = 1e-5):
+    """Row-wise E4M3 codes and scales of LayerNorm(a) * u (u None: no gate); a fp32 [M, N]."""
+    lib = _lib.load()
+    M, N = a.shape
+    a = a.contiguous()
+    if u is not None and u.stride(1) != 1:
+        raise ValueError("u must have a contiguous last dim")
+    q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    scale = torch.empty((M,), dtype=torch.float32, device=a.device)
+    _lib.check(lib.hstu_layernorm_gate_fp8(M, N, _ptr(a), _ptr(u), u.stride(0) if u is not None else 0,
+                                           float(eps), _ptr(q), _ptr(scale), _stream()))
+    return q, scale
+
+
 def layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a, dy,
               eps: float = 1e-5):
     """Gradients of one HSTU layer (hstu_layer_bwd): dict dx (bf16), dw1, db1, dw2, db2 (fp32).

@@ -225,6 +225,54 @@ HSTU_API hstu_status hstu_layernorm_gate(int64_t M, int64_t N, const float* a, c
                                 int64_t ldu, float eps, void* out, void* stream);
 
 /*
+ * FP8 projection path (Generative Recommenders README, "FP8 linear reference
+ * and benchmark", and its description of the HSTU Ultra stack: row-wise E4M3
+ * quantisation, FP8 addmm with weights quantised once and cached, and
+ * normalisation steps fused with the quantisation of their output).
+ * Codes are OCP E4M3FN bytes (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite 448; 0x7F / 0xFF are NaN and never produced).
+ * Row-wise quantisation: scale = amax(row) / 448 (1.0 for a row of zeros),
+ * code = E4M3(x / scale) rounded to nearest even, both divisions IEEE fp32.
+ * All pointers are device pointers; calls are asynchronous on `stream`.
+ *
+ * hstu_fp8_quantize_rows: x bf16 [M, K], row stride ldx (multiple of 8) ->
+ *   q uint8 [M, K] dense, scale fp32 [M]. K a multiple of 16; x and q
+ *   16-byte aligned.
+ */
+HSTU_API hstu_status hstu_fp8_quantize_rows(int64_t M, int64_t K, const void* x, int64_t ldx,
+                                            void* q, float* scale, void* stream);
+
+/*
+ * hstu_fp8_prepare_weight: the weight w bf16 [K, N] (dense) of y = x w,
+ *   quantised per output feature n -> q uint8 [N, K] (reduction index
+ *   contiguous, the layout hstu_fp8_linear reads), scale fp32 [N]. A one-time
+ *   step; the caller keeps q and scale. K a multiple of 16; q 16-byte aligned.
+ */
+HSTU_API hstu_status hstu_fp8_prepare_weight(int64_t K, int64_t N, const void* w, void* q,
+                                             float* scale, void* stream);
+
+/*
+ * hstu_fp8_linear: y[m, n] = act(x_scale[m] * w_scale[n] * sum_k x[m, k] w[n, k]
+ *   + bias[n]) with x, w the E4M3 values of xq uint8 [M, K] and wq uint8
+ *   [N, K] (both dense, 16-byte aligned), fp32 accumulation; bias fp32 [N] or
+ *   NULL; act = SiLU when apply_silu != 0; y bf16 [M, N] dense. K a multiple
+ *   of 16; M, N >= 0 any.
+ */
+HSTU_API hstu_status hstu_fp8_linear(int64_t M, int64_t K, int64_t N, const void* xq,
+                                     const float* x_scale, const void* wq, const float* w_scale,
+                                     const float* bias, void* y, int32_t apply_silu, void* stream);
+
+/*
+ * hstu_layernorm_gate_fp8: row-wise quantisation of LayerNorm(a[m, :]) * u[m, :]
+ *   (as hstu_layernorm_gate; u NULL: no gate, LayerNorm alone) -> q uint8
+ *   [M, N] dense, scale fp32 [M]. a fp32 [M, N] dense; u bf16 with row stride
+ *   ldu (multiple of 4). N a multiple of 64, <= 4096.
+ */
+HSTU_API hstu_status hstu_layernorm_gate_fp8(int64_t M, int64_t N, const float* a, const void* u,
+                                             int64_t ldu, float eps, void* q, float* scale,
+                                             void* stream);
+
+/*
  * hstu_layer_bwd: gradients of one HSTU layer (the steps of hstu_linear,
  *   hstu_attn_fwd and hstu_layernorm_gate above, as the Generative
  *   Recommenders README's "HSTU Ultra attention benchmark" lists them:
