@@ -195,7 +195,9 @@ def main():
 def bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd, iters=10):
     """One HSTU layer at the M-FALCON-style shape, 4 users x (8192 history + 1024
     candidates): the forward, then the backward from a seeded dY (the forward's
-    UVQK and A reused, the projection pre-activation recomputed inside)."""
+    UVQK and A reused, the projection pre-activation recomputed inside), then
+    the forward with both projections in FP8 (weights prepared once, outside
+    the timed loop; activation quantisation inside it)."""
     from hstu_pointwise_attention_amd.flops import unmasked_pairs_host
     w = W.MFALCON_LAYER
     li = W.make_layer_inputs(w)
@@ -237,8 +239,20 @@ def bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd, iters=10):
     # dX and dW cost twice its forward (the pre-activation recompute is not counted)
     attn_b = pairs * 10 * w.head_dim
     gemm_b = 2 * gemm
+    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd_fp8, prepare_fp8_weights
+    fw = prepare_fp8_weights(w1, w2)
+    for _ in range(3):
+        hstu_layer_fwd_fp8(x, fw, b1, b2, offs, nt, w.heads, w.head_dim)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        hstu_layer_fwd_fp8(x, fw, b1, b2, offs, nt, w.heads, w.head_dim)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_8 = e0.elapsed_time(e1) / iters
     return {"ms": round(ms, 4), "tflops": round((attn + gemm) / (ms * 1e-3) / 1e12, 2),
             "attn_flops": attn, "gemm_flops": gemm, "tokens": T,
+            "fp8_ms": round(ms_8, 4), "fp8_tflops": round((attn + gemm) / (ms_8 * 1e-3) / 1e12, 2),
             "bwd_ms": round(ms_b, 4), "bwd_tflops": round((attn_b + gemm_b) / (ms_b * 1e-3) / 1e12, 2),
             "bwd_attn_flops": attn_b, "bwd_gemm_flops": gemm_b}
 

@@ -56,6 +56,35 @@ def hstu_layer_fwd(x, w1, b1, w2, b2, seq_offsets, num_targets, heads: int, head
     return y, a2, uvqk
 
 
+def prepare_fp8_weights(w1, w2):
+    """E4M3 codes and per-output-feature scales of the layer's two projection
+    weights (w1 [d_model, 4*H*D], w2 [H*D, d_model]), computed once and kept."""
+    w1q, w1s = ops.fp8_prepare_weight(w1)
+    w2q, w2s = ops.fp8_prepare_weight(w2)
+    return dict(w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s)
+
+
+def hstu_layer_fwd_fp8(x, fp8_weights, b1, b2, seq_offsets, num_targets, heads: int,
+                       head_dim: int, eps: float = 1e-5):
+    """:func:`hstu_layer_fwd` with both projections in FP8: X quantised row-wise,
+    UVQK = SiLU(FP8 GEMM with the prepared W1 + b1), the attention, LayerNorm(A) * U
+    quantised row-wise in the same kernel, Y = FP8 GEMM with the prepared W2 + b2.
+
+    Returns (y [T, d_model] bf16, a [T, H*D] fp32, uvqk [T, 4*H*D] bf16).
+    """
+    T = x.shape[0]
+    HD = heads * head_dim
+    w = fp8_weights
+    xq, xs = ops.fp8_quantize_rows(x)
+    uvqk = ops.fp8_linear(xq, xs, w["w1q"], w["w1s"], b1, silu=True)
+    u, v, q, k = (uvqk[:, n * HD:(n + 1) * HD].view(T, heads, head_dim) for n in range(4))
+    _, a = ops.attn_fwd(q, k, v, None, seq_offsets, 1, num_targets=num_targets, save_a=True)
+    a2 = a.view(T, HD)
+    zq, zs = ops.layernorm_gate_fp8(a2, uvqk[:, 0:HD], eps)
+    y = ops.fp8_linear(zq, zs, w["w2q"], w["w2s"], b2, silu=False)
+    return y, a2, uvqk
+
+
 def hstu_layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a,
                    dy, eps: float = 1e-5):
     """Gradients of :func:`hstu_layer_fwd` from dY: dict dx, dw1, db1, dw2, db2

@@ -30,8 +30,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import silu
-from .layer import layernorm
+from .attention import attention_fwd, silu
+from .layer import layernorm, split_uvqk
 
 E4M3_MAX = 448.0
 _MIN_NORMAL_EXP = -6          # smallest normal binade: 2^-6
@@ -108,3 +108,23 @@ def layernorm_gate_fp8(a, u, eps: float = 1e-5) -> tuple[np.ndarray, np.ndarray]
     """Codes and scales of the row-wise quantisation of LayerNorm(a) * u."""
     z = (layernorm(a, eps) * np.asarray(u, np.float64)).astype(np.float32)
     return quantize_rows(z)
+
+
+def layer_fwd_fp8(x, w1, b1, w2, b2, seq_offsets, num_targets, heads, head_dim,
+                  eps: float = 1e-5):
+    """oracle.layer.layer_fwd with both projections in FP8 (the README's
+    fp8_addmm_fwd layer): X quantised row-wise, UVQK = SiLU(FP8 addmm with the
+    prepared W1), attention as before, LayerNorm(A) * U quantised row-wise in
+    the same step, Y = FP8 addmm with the prepared W2. Returns dict uvqk, a, y."""
+    xq, xs = quantize_rows(x)
+    w1q, w1s = quantize_weight(w1)
+    uvqk = fp8_linear(xq, xs, w1q, w1s, b1, apply_silu=True)
+    u, v, q, k = split_uvqk(uvqk, heads, head_dim)
+    offs = np.asarray(seq_offsets)
+    max_len = max(int(np.max(np.diff(offs))) if len(offs) > 1 else 1, 1)
+    _, a = attention_fwd(q, k, v, None, offs, max_len, num_targets)
+    T = uvqk.shape[0]
+    a2 = a.reshape(T, heads * head_dim)
+    zq, zs = layernorm_gate_fp8(a2, u.reshape(T, heads * head_dim), eps)
+    w2q, w2s = quantize_weight(w2)
+    return dict(uvqk=uvqk, a=a2, y=fp8_addmm(zq, zs, w2q, w2s, b2))

@@ -189,6 +189,26 @@ def test_layer_bwd_validation(lib):
     assert layer_bwd_call(lib, ws=None) == _lib.HSTU_EWORKSPACE
 
 
+def test_fp8_validation(lib):
+    S = FAKE
+    assert lib.hstu_fp8_quantize_rows(10, 24, S, 24, S, S, None) == _lib.HSTU_EUNSUPPORTED
+    assert lib.hstu_fp8_quantize_rows(10, 32, S, 16, S, S, None) == _lib.HSTU_EINVAL      # ldx < K
+    assert lib.hstu_fp8_quantize_rows(-1, 32, S, 32, S, S, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_fp8_quantize_rows(10, 32, ctypes.c_void_p(4104), 32, S, S, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_fp8_quantize_rows(10, 32, S, 32, S, None, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_fp8_prepare_weight(0, 16, S, S, S, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_fp8_prepare_weight(40, 16, S, S, S, None) == _lib.HSTU_EUNSUPPORTED
+    assert lib.hstu_fp8_linear(10, 24, 16, S, S, S, S, None, S, 0, None) == _lib.HSTU_EUNSUPPORTED
+    assert lib.hstu_fp8_linear(10, 32, 16, S, None, S, S, None, S, 0, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_fp8_linear(10, 32, 16, ctypes.c_void_p(4100), S, S, S, None, S, 0, None) \
+        == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate_fp8(4, 100, S, None, 0, 1e-5, S, S, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate_fp8(4, 128, S, S, 64, 1e-5, S, S, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_layernorm_gate_fp8(4, 128, S, None, 0, -1.0, S, S, None) == _lib.HSTU_EINVAL
+    # nothing to do: no rows
+    assert lib.hstu_fp8_linear(0, 32, 16, None, None, None, None, None, None, 0, None) == _lib.HSTU_OK
+
+
 def test_bucketize_validation(lib):
     d = good_desc(max_len=40000)
     assert lib.hstu_rab_bucketize(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, None) \

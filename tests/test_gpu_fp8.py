@@ -125,3 +125,51 @@ def test_layernorm_gate_fp8(M, N, gated):
     same_sign = (q[diff] & 0x80) == (wq[diff] & 0x80)
     step = np.abs((q[diff] & 0x7F).astype(int) - (wq[diff] & 0x7F).astype(int))
     assert np.all(same_sign & (step == 1)) or not diff.any()
+
+
+def _layer_case(lengths, n_targets, d_model, heads, head_dim, seed):
+    """FP8 layer forward on the GPU, checked step by step on its own
+    intermediates (the UVQK GEMM on identical codes, LayerNorm-gate-to-FP8 on
+    the GPU's own A and U, the output GEMM on the GPU's own codes), then end to
+    end against oracle.fp8.layer_fwd_fp8 with one E4M3 rounding unit (2^-4) of
+    rel-L2: the GPU keeps UVQK in bf16, so requantising LayerNorm(A) * U may move
+    a code by one step where the fp64 oracle's z differs at bf16 precision."""
+    import torch
+    from hstu_pointwise_attention_amd import ops
+    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd_fp8, prepare_fp8_weights
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, np.int64)
+    offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    nt = np.asarray(n_targets, np.int64)
+    M, HD = int(offs[-1]), heads * head_dim
+    x = round_to(rng.standard_normal((M, d_model)), "bf16")
+    w1 = round_to(rng.standard_normal((d_model, 4 * HD)) / np.sqrt(d_model), "bf16")
+    b1 = (0.1 * rng.standard_normal(4 * HD)).astype(np.float32)
+    w2 = round_to(rng.standard_normal((HD, d_model)) / np.sqrt(HD), "bf16")
+    b2 = (0.1 * rng.standard_normal(d_model)).astype(np.float32)
+    fw = prepare_fp8_weights(_dev(w1, torch.bfloat16), _dev(w2, torch.bfloat16))
+    y, a, uvqk = hstu_layer_fwd_fp8(_dev(x, torch.bfloat16), fw, _dev(b1, torch.float32),
+                                    _dev(b2, torch.float32), _dev(offs, torch.int64),
+                                    _dev(nt, torch.int64), heads, head_dim)
+    zq, zs = ops.layernorm_gate_fp8(a, uvqk[:, :HD])
+    torch.cuda.synchronize()
+    tag = f"fp8 layer lengths {list(lengths)} d_model {d_model} H{heads} D{head_dim}"
+    print(tag, flush=True)
+    y, a, uvqk, zq, zs = (P.host(t) for t in (y, a, uvqk, zq, zs))
+    xq, xs = F.quantize_rows(x)
+    w1q, w1s = F.quantize_weight(w1)
+    w2q, w2s = F.quantize_weight(w2)
+    assert P.rel_l2(uvqk, F.fp8_linear(xq, xs, w1q, w1s, b1, apply_silu=True)) <= P.BF16_REL, tag
+    oq, os_ = F.layernorm_gate_fp8(a, uvqk[:, :HD])
+    assert np.allclose(zs, os_, rtol=1e-5, atol=0) and (zq.astype(np.uint8) != oq).mean() <= 1e-3, tag
+    assert P.rel_l2(y, F.fp8_addmm(zq.astype(np.uint8), zs, w2q, w2s, b2)) <= P.BF16_REL, tag
+    want = F.layer_fwd_fp8(x, w1, b1, w2, b2, offs, nt, heads, head_dim)
+    assert P.rel_l2(y, want["y"]) <= 2.0 ** -4, (tag, P.rel_l2(y, want["y"]))
+
+
+def test_layer_fwd_fp8_small():
+    _layer_case([128 + 32, 80 + 10, 5], [32, 10, 2], d_model=128, heads=2, head_dim=64, seed=21)
+
+
+def test_layer_fwd_fp8_medium():
+    _layer_case([1200, 1200], [200, 200], d_model=256, heads=2, head_dim=128, seed=22)

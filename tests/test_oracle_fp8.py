@@ -140,3 +140,20 @@ def test_layernorm_gate_fp8_dequantises_to_layernorm_times_gate():
     amax = np.max(np.abs(z), axis=1, keepdims=True)
     assert np.all(np.abs(deq - z) <= 2.0 ** -4 * np.abs(z) + 2.0 ** -10 * amax / 448 * 2)
     assert np.allclose(np.max(np.abs(deq), axis=1), amax[:, 0], rtol=1e-6)
+
+
+def test_layer_fwd_fp8_close_to_layer_fwd():
+    """The FP8 layer stays within FP8 rounding of the unquantised layer
+    (rel-L2 of Y below 2^-3), and is not the unquantised layer itself."""
+    from oracle.layer import layer_fwd
+    rng = np.random.default_rng(5)
+    offs = np.array([0, 40, 97], np.int64)
+    nt = np.array([8, 5], np.int64)
+    x = rng.standard_normal((97, 64))
+    w1 = rng.standard_normal((64, 4 * 64)) / 8
+    w2 = rng.standard_normal((64, 64)) / 8
+    b1, b2 = 0.1 * rng.standard_normal(256), 0.1 * rng.standard_normal(64)
+    ref = layer_fwd(x, w1, b1, w2, b2, offs, nt, 2, 32)
+    got = F.layer_fwd_fp8(x, w1, b1, w2, b2, offs, nt, 2, 32)
+    e = np.linalg.norm(got["y"] - ref["y"]) / np.linalg.norm(ref["y"])
+    assert 1e-4 < e < 2.0 ** -3, e
