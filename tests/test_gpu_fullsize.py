@@ -8,7 +8,8 @@ d_rab_pos entries as diagonal sums of dS. d_rab_time is checked through a
 property that holds at any size: every unmasked pair adds its dS to exactly
 one position bucket and one time bucket, so both tables sum to the same
 total. The M-FALCON layer workload (4 users x (8192 + 1024 candidates),
-d_model 512) is checked on sampled rows of UVQK, A and Y.
+d_model 512) is checked on sampled rows of UVQK, A and Y, and its backward
+on sampled rows of dX (with db2 whole).
 """
 import numpy as np
 import pytest
@@ -137,3 +138,108 @@ def test_layer_rows(layer):
     for key in ("uvqk", "a", "y"):
         e = P.rel_l2(got[key][rows], want[key])
         assert e <= P.BF16_REL, (key, e)
+
+
+@pytest.fixture(scope="module")
+def layer_bwd():
+    """The M-FALCON layer forward and backward through the C ABI, as bench.py
+    times them, with a seeded dY (N(0, 1), bf16)."""
+    import torch
+    from hstu_pointwise_attention_amd.attention import hstu_layer_bwd, hstu_layer_fwd
+    li = W.make_layer_inputs(W.MFALCON_LAYER)
+    dy = W.round_to(np.random.default_rng(1009).standard_normal((li["x"].shape[0], li["w2"].shape[1])),
+                    "bf16")
+    dev = "cuda"
+    t = {k: torch.from_numpy(li[k]).to(dev, torch.bfloat16) for k in ("x", "w1", "w2")}
+    t.update({k: torch.from_numpy(li[k]).to(dev) for k in ("b1", "b2", "seq_offsets", "num_targets")})
+    y, a, uvqk = hstu_layer_fwd(t["x"], t["w1"], t["b1"], t["w2"], t["b2"], t["seq_offsets"],
+                                t["num_targets"], li["heads"], li["head_dim"])
+    g = hstu_layer_bwd(t["x"], t["w1"], t["b1"], t["w2"], t["seq_offsets"], t["num_targets"],
+                       li["heads"], li["head_dim"], uvqk, a,
+                       torch.from_numpy(dy).to(dev, torch.bfloat16))
+    torch.cuda.synchronize()
+    print(f"layer backward workload: T={li['x'].shape[0]}", flush=True)
+    return li, dy, {k: P.host(v) for k, v in g.items()}
+
+
+def test_layer_bwd_rows(layer_bwd):
+    """Sampled rows of dX for user 1: the last history rows and candidates. For
+    those keys, dK and dV involve only queries from 40 rows before the end of
+    the history onwards, so the oracle needs A (and dA) for just those rows:
+    oracle.attention_fwd_rows, the LayerNorm and gate backward, and the
+    sampled attention gradients, chained as oracle.layer.layer_bwd does.
+    db2 (a column sum of dY) is checked whole."""
+    from oracle.layer import layernorm, layernorm_bwd, split_uvqk
+    li, dy, got = layer_bwd
+    H, D = li["heads"], li["head_dim"]
+    HD = H * D
+    offs, nt = li["seq_offsets"], li["num_targets"]
+    b = 1
+    s, e = int(offs[b]), int(offs[b + 1])
+    L = e - s
+    hist = L - int(nt[b])
+    w1 = li["w1"].astype(np.float64)
+    w2 = li["w2"].astype(np.float64)
+    pre = li["x"][s:e].astype(np.float64) @ w1 + li["b1"].astype(np.float64)
+    u, v, q, k = split_uvqk(oracle.silu(pre), H, D)
+    one = np.array([0, L], np.int64)
+    ntb = np.array([int(nt[b])], np.int64)
+    rows = np.arange(hist - 40, L)
+    _, A = oracle.attention_fwd_rows(q, k, v, None, one, L, rows, ntb)
+    A2 = A.reshape(len(rows), HD)
+    dz = dy[s:e][rows].astype(np.float64) @ w2.T
+    du_rows = dz * layernorm(A2)
+    dA = np.zeros((L, H, D))
+    dA[rows] = layernorm_bwd(A2, dz * u.reshape(L, HD)[rows]).reshape(len(rows), H, D)
+    pick = np.array([hist - 40, hist - 1, hist, hist + 511, L - 1], np.int64)
+    dq, _ = sampled.attention_bwd_rows(q, k, v, None, one, L, dA, pick, ntb)
+    dk, dv = sampled.attention_bwd_cols(q, k, v, None, one, L, dA, pick, ntb)
+    n = len(pick)
+    d_uvqk = np.concatenate([du_rows[pick - rows[0]], dv.reshape(n, HD), dq.reshape(n, HD),
+                             dk.reshape(n, HD)], axis=1)
+    z = pre[pick]
+    sig = 1.0 / (1.0 + np.exp(-z))
+    dx_want = (d_uvqk * sig * (1.0 + z * (1.0 - sig))) @ w1.T
+    e_dx = P.rel_l2(got["dx"][s + pick], dx_want)
+    assert e_dx <= P.BF16_REL, e_dx
+    db2 = dy.astype(np.float64).sum(axis=0)
+    assert P.rel_l2(got["db2"], db2) <= 1e-5
+
+
+def test_layer_fp8_rows():
+    """The FP8 layer forward at the M-FALCON shape on sampled rows of Y:
+    quantisation is row-wise, so a row's UVQK, A and output codes follow from
+    its own row and its sequence's keys and values (oracle.fp8 steps chained
+    as oracle.fp8.layer_fwd_fp8 does); bar: one E4M3 rounding unit (2^-4) of
+    rel-L2, as the small FP8 layer tests derive it."""
+    import torch
+    from oracle import fp8 as F8
+    from oracle.layer import split_uvqk
+    from hstu_pointwise_attention_amd.attention import hstu_layer_fwd_fp8, prepare_fp8_weights
+    li = W.make_layer_inputs(W.MFALCON_LAYER)
+    dev = "cuda"
+    t = {k: torch.from_numpy(li[k]).to(dev, torch.bfloat16) for k in ("x", "w1", "w2")}
+    t.update({k: torch.from_numpy(li[k]).to(dev) for k in ("b1", "b2", "seq_offsets", "num_targets")})
+    fw = prepare_fp8_weights(t["w1"], t["w2"])
+    y, _, _ = hstu_layer_fwd_fp8(t["x"], fw, t["b1"], t["b2"], t["seq_offsets"], t["num_targets"],
+                                 li["heads"], li["head_dim"])
+    torch.cuda.synchronize()
+    y = P.host(y)
+    H, D = li["heads"], li["head_dim"]
+    offs, nt = li["seq_offsets"], li["num_targets"]
+    b = 2
+    s, e = int(offs[b]), int(offs[b + 1])
+    L = e - s
+    hist = L - int(nt[b])
+    w1q, w1s = F8.quantize_weight(li["w1"])
+    w2q, w2s = F8.quantize_weight(li["w2"])
+    xq, xs = F8.quantize_rows(li["x"][s:e])
+    uvqk = F8.fp8_linear(xq, xs, w1q, w1s, li["b1"], apply_silu=True)
+    u, v, q, k = split_uvqk(uvqk, H, D)
+    pick = np.array([0, 1, 4095, hist - 1, hist, hist + 700, L - 1], np.int64)
+    _, A = oracle.attention_fwd_rows(q, k, v, None, np.array([0, L]), L, pick,
+                                     np.array([int(nt[b])]))
+    zq, zs = F8.layernorm_gate_fp8(A.reshape(len(pick), H * D), u.reshape(L, H * D)[pick])
+    want = F8.fp8_addmm(zq, zs, w2q, w2s, li["b2"])
+    e_y = P.rel_l2(y[s + pick], want)
+    assert e_y <= 2.0 ** -4, e_y
