@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu_attn.so")
-SOURCES = ["api.hip", "prep.hip", "fwd.hip", "bwd.hip", "bwd_k16.hip", "layer.hip", "fp8.hip", "prof.hip"]
+SOURCES = ["api.hip", "prep.hip", "fwd.hip", "bwd.hip", "bwd_k16.hip", "layer.hip", "fp8.hip", "dq_ds.hip", "prof.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -199,8 +199,19 @@ hipError_t dispatch_dq<bf16>(const AttnParams& p, hipStream_t s) {
   }
 }
 
+hipError_t dispatch_dq_ds(const AttnParams& p, hipStream_t s) {
+  switch (p.D) {
+    case 32: return launch_dq_ds<32>(p, s);
+    case 64: return launch_dq_ds<64>(p, s);
+    case 128: return launch_dq_ds<128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // dA' and dU, then dK / dV / d_rab per key block, then dQ per query block
-// (its own schedule, the forward's).
+// (its own schedule, the forward's). With the dS export (bf16), the device
+// flag set by the schedule picks one of the two dQ kernels; the other exits
+// at once.
 template <typename T>
 hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
   hipError_t e = launch_bwd_pre<T>(p, s);
@@ -208,6 +219,7 @@ hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
   AttnParams pq = p;                             // the dQ pass walks query blocks
   pq.items = p.items_q;
   if (e == hipSuccess) e = dispatch_dq<T>(pq, s);
+  if (e == hipSuccess && p.ds != nullptr) e = dispatch_dq_ds(pq, s);
   return e;
 }
 

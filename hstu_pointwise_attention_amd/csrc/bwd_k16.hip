@@ -154,6 +154,20 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
   const int last_row = k0 < hist ? L - 1 : min(k0 + C::BN - 1, L - 1);
   const int n_qt = last_row / C::BM - qt_first + 1;
 
+  // dS export: this lane's 8 values of each 32-query chunk (queries
+  // 16 h + 4 q4 + r of the chunk) sit together at positions 8 q4 + 4 h + r,
+  // so each chunk is one 16-byte store per lane; tile (this key block, query
+  // tile qt_first) of this head, query tile qt_first + n n tiles further.
+  // A wave that skips a tile, or the first chunk of a tile that lies before
+  // its keys, writes nothing there: the dQ pass applies the same rule and
+  // reads zeros instead.
+  static_assert(C::BN == kDsKeys && C::BM == kDsQueries, "dS tile shape");
+  bf16* ds_row = nullptr;
+  if (p.ds != nullptr && *p.ds_on != 0)
+    ds_row = reinterpret_cast<bf16*>(p.ds) +
+             (p.ds_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kDsTile;
+  const int ds_lane = jl * kDsQueries + 8 * q4;
+
   // ---------------------------------------------------------------- staging
   constexpr int RPM = C::NT / C::CPR;            // rows per staging step
   const bool stager = tid < C::SCH;              // all threads when D = 64, 128
@@ -211,6 +225,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
     __syncthreads();                               // tile n staged
     if (more) load_tile(q0 + C::BM);
     const bool pos_diag = has_pos && q0 + C::BM - 1 < hist;
+    bf16* const ds_w = ds_row ? ds_row + n * kDsTile : nullptr;
     const bool skip = jw >= L || q0 + C::BM - 1 < jw ||
                       (jw >= hist && (q0 > jw + 15 || q0 + C::BM - 1 < jw));
     if (!skip) {
@@ -341,6 +356,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           // halves of df's words (opaque, so that they are not converted again)
           asm volatile("" : "+v"(df));
           const u32x4 dfw = __builtin_bit_cast(u32x4, df);
+          if (ds_w) st16(ds_w + (ds_lane + 32 * kc), dfw);   // dS^T row: the chunk's 8 values
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll

@@ -240,4 +240,24 @@ struct WorkItem {
 // rows per forward workgroup and 128 keys per backward workgroup.
 constexpr int kBlk = 128;
 
+// dS export of the bf16 backward: the key-block kernel writes, for every
+// (key block kb, query tile qt) it visits, the tile dS^T [128 keys][64
+// queries] (bf16); within each 32-query chunk of a key's row, position
+// 8 q + 4 h + r holds query 16 h + 4 q + r (the key-block kernel's lane
+// order, so that a lane's values are contiguous); the dQ pass reads them
+// back and restores query order when it stages its output.
+// Key block kb visits query tiles 2 kb .. nqt - 1 at most, so the tiles of
+// one (sequence, head) are numbered row by row over that triangle.
+constexpr int kDsKeys = 128, kDsQueries = 64;
+constexpr int64_t kDsTile = (int64_t)kDsKeys * kDsQueries;    // elements per tile
+__host__ __device__ inline int64_t ds_seq_tiles(int L) {
+  const int64_t nkb = (L + kDsKeys - 1) / kDsKeys, nqt = (L + kDsQueries - 1) / kDsQueries;
+  return nkb * nqt - nkb * (nkb - 1);
+}
+// index of tile (kb, 2 kb) within its (sequence, head)
+__host__ __device__ inline int64_t ds_row_start(int L, int kb) {
+  const int64_t nqt = (L + kDsQueries - 1) / kDsQueries;
+  return (int64_t)kb * nqt - (int64_t)kb * (kb - 1);
+}
+
 }  // namespace hstu

@@ -592,6 +592,7 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQ_WAVES, DQ_WAVES)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
+  if (p.ds_on != nullptr && *p.ds_on != 0) return;   // dQ comes from the exported dS tiles
   if constexpr (WIDE) {
     // sequences needing 64-bit timestamps are rare: a small grid walks the
     // work slots and takes only theirs

@@ -54,6 +54,14 @@ struct AttnParams {
   int32_t kv_splits;
   int64_t m_rows;                    // candidate rows (rows of q)
   float* part;
+  // dS export (bf16 backward; ds null: the dQ pass recomputes dS): tile
+  // storage of ds_cap tiles, each (sequence, head)'s tiles from ds_base[b] +
+  // head * ds_seq_tiles(L); the schedule kernel fills ds_base and sets
+  // *ds_on to 1 when the batch's tiles fit, else 0 (the recompute pass runs)
+  void* ds;
+  int64_t ds_cap;
+  int64_t* ds_base;                  // [B]
+  int32_t* ds_on;
 };
 
 // Workspace layout: returns total bytes and fills the pointers in p (when
@@ -75,7 +83,7 @@ constexpr int kWideGrid = 512;
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
   kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
-  kKBucketize, kKFp8Linear, kKFp8Quant, kNumKernelIds
+  kKBucketize, kKFp8Linear, kKFp8Quant, kKDqDs, kNumKernelIds
 };
 // Records a HIP event on `s` before / after a launch when timing is enabled.
 void prof_before(int id, hipStream_t s);
@@ -120,6 +128,11 @@ template <int D> hipError_t launch_bwd_k16(const AttnParams& p, hipStream_t s);
 #define BWD_K16 1
 #endif
 template <typename T, int D> hipError_t launch_dq(const AttnParams& p, hipStream_t s);
+// dQ from the exported dS tiles (dq_ds.hip); exits at once unless *p.ds_on.
+template <int D> hipError_t launch_dq_ds(const AttnParams& p, hipStream_t s);
+// Capacity (tiles) of the dS export for a batch of T tokens in B sequences
+// of at most max_len rows each, H heads; 0 when the export is not used.
+int64_t ds_capacity(int64_t T, int B, int H, int max_len);
 template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 

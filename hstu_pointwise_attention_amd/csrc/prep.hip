@@ -292,6 +292,29 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     if (mode == 2) p.items_q[hist[blk] + atomicAdd(&fill_q[blk], 1)] = w;
   }
   if (threadIdx.x == 0) *p.n_items = total;
+  if (mode == 2 && p.ds != nullptr) {
+    // dS tile numbering: exclusive scan of H * ds_seq_tiles(L) over the
+    // sequences, each thread a contiguous run of them
+    __shared__ int64_t run[kSchedThreads];
+    const int per = (B + kSchedThreads - 1) / kSchedThreads;
+    const int b0 = threadIdx.x * per, b1 = b0 + per < B ? b0 + per : B;
+    int64_t sum = 0;
+    for (int b = b0; b < b1; ++b) sum += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
+    run[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
+      const int64_t add = threadIdx.x >= off ? run[threadIdx.x - off] : 0;
+      __syncthreads();
+      run[threadIdx.x] += add;
+      __syncthreads();
+    }
+    int64_t at = threadIdx.x > 0 ? run[threadIdx.x - 1] : 0;
+    for (int b = b0; b < b1; ++b) {
+      p.ds_base[b] = at;
+      at += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
+    }
+    if (threadIdx.x == kSchedThreads - 1) *p.ds_on = run[kSchedThreads - 1] <= p.ds_cap ? 1 : 0;
+  }
 }
 
 // rab bucket export: grid (64 row groups, B sequences).
@@ -434,11 +457,36 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 4 * NB));
   p.items_q = nullptr;
   p.d_a = nullptr;
+  p.ds = nullptr;
+  p.ds_cap = 0;
+  p.ds_base = nullptr;
+  p.ds_on = nullptr;
   if (bwd) {
     p.items_q = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
     p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
+    const int64_t cap = (elem_bytes == 2 && BWD_K16) ? ds_capacity(p.T, p.B, p.H, p.max_len) : 0;
+    if (cap > 0) {
+      p.ds_cap = cap;
+      p.ds_base = (int64_t*)take(sizeof(int64_t) * (size_t)p.B);
+      p.ds_on = (int32_t*)take(sizeof(int32_t));
+      p.ds = take((size_t)cap * kDsTile * 2);
+    }
   }
   return off;
+}
+
+// A sequence of L <= max_len rows holds ds_seq_tiles(L) <= nkb (nkb + 1)
+// tiles per head, nkb = ceil(L / 128) <= ceil(max_len / 128); summed over
+// the batch (sum of nkb <= T / 128 + B) that is at most
+// (ceil(max_len / 128) + 1) (T / 128 + B) per head. The exact count is
+// checked on the device, and a batch beyond the capacity (longer sequences
+// than max_len, or beyond the 4 GiB cap) takes the recompute pass.
+int64_t ds_capacity(int64_t T, int B, int H, int max_len) {
+  if (T <= 0 || B <= 0) return 0;
+  const int64_t nkb = (max_len + kDsKeys - 1) / kDsKeys;
+  int64_t cap = (int64_t)H * (nkb + 1) * (T / kDsKeys + B);
+  const int64_t max_tiles = ((int64_t)4 << 30) / (kDsTile * 2);
+  return cap < max_tiles ? cap : max_tiles;
 }
 
 // The forward's carve-up for the joined row count p.T, plus the per-sequence

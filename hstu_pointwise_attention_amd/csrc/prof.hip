@@ -36,7 +36,7 @@ hipEvent_t take_event() {
 
 const char* const kNames[kNumKernelIds] = {"prep", "schedule", "fwd", "bwd_pre", "bwd",
                                            "dq", "fill", "linear", "layernorm_gate",
-                                           "bucketize", "fp8_linear", "fp8_quantize"};
+                                           "bucketize", "fp8_linear", "fp8_quantize", "dq_ds"};
 
 }  // namespace
 

@@ -238,3 +238,25 @@ def test_autograd_function_matches_ops():
     for key, gk in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("u", "du"), ("rab_pos", "d_rab_pos"),
                     ("rab_time", "d_rab_time")):
         assert P.rel_l2(P.host(leaves[key].grad), want[gk]) <= P.FP32_REL, key
+
+
+def test_bf16_dq_paths_agree():
+    """The bf16 backward computes dQ from the key-block kernel's exported dS
+    tiles when the batch's tiles fit the workspace sized from max_len, and by
+    recomputing dS otherwise. Without a position bias max_len changes nothing
+    else, so the same inputs run both ways: lengths 300, 200, 77 with H 2 hold
+    2 * (9 + 6 + 2) = 34 tiles; max_len 512 sizes room for 2 * 5 * 7 = 70
+    (export), max_len 64 for 2 * 2 * 7 = 28 (recompute). Both match the oracle
+    and each other."""
+    lengths = (300, 200, 77)
+    w = W.AttnWorkload("dqpaths", 41, 3, 2, 64, 64, 512, 16, False, "bf16", "fixed", lengths)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.array([20, 0, 5], np.int64)
+    want = P.oracle_bwd(inp)
+    got = {}
+    for max_len in (512, 64):
+        run = dict(inp, max_len=max_len)
+        _, A = P.gpu_fwd(run)
+        got[max_len] = P.gpu_bwd(run, A)
+        P.check_bwd(run, got[max_len], want, f"max_len {max_len}")
+    assert P.rel_l2(P.host(got[512]["dq"]), P.host(got[64]["dq"])) <= P.BF16_REL
