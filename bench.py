@@ -34,8 +34,10 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # summaries are under profiles/. None when not measured for the kernel as it
 # stands.
 TRAFFIC = {
-    # hstu_bwd_k16_kernel<128>: 583.4 MiB fetched + 130.4 MiB written per launch
-    "bwd": {"fetch_bytes": 611_728_177, "write_bytes": 136_772_608, "total_bytes": 748_500_785,
+    # hstu_bwd_k16_kernel<128>: 827.0 MiB fetched + 1062.9 MiB written per
+    # launch; the writes include the dS^T tiles exported for the dQ pass
+    # (about 0.97 GB by design, not compulsory traffic of the algorithm)
+    "bwd": {"fetch_bytes": 867_166_140, "write_bytes": 1_114_567_573, "total_bytes": 1_981_733_713,
             "compulsory_bytes": 263_000_000, "unit": "B"},
 }
 
