@@ -237,11 +237,13 @@ def bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd, iters=10):
     g = torch.Generator(device=dev).manual_seed(1007)
     dy = torch.randn(y.shape, generator=g, device=dev).to(torch.bfloat16)
     for _ in range(2):
-        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy)
+        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy,
+                       max_len=w.history + w.candidates)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(iters):
-        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy)
+        hstu_layer_bwd(x, w1, b1, w2, offs, nt, w.heads, w.head_dim, uvqk, a, dy,
+                       max_len=w.history + w.candidates)
     e1.record()
     torch.cuda.synchronize()
     ms_b = e0.elapsed_time(e1) / iters

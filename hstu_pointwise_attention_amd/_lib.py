@@ -74,8 +74,9 @@ _SIGS = {
     "hstu_linear": [_I64, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_int32, _P],
     "hstu_layernorm_gate": [_I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P],
     "hstu_layer_bwd_workspace_size": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
-    "hstu_layer_bwd": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "hstu_layer_bwd": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int32, _P, _P,
                        _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
                        ctypes.c_size_t, _P],
     "hstu_fp8_quantize_rows": [_I64, _I64, _P, _I64, _P, _P, _P],

@@ -86,8 +86,9 @@ def hstu_layer_fwd_fp8(x, fp8_weights, b1, b2, seq_offsets, num_targets, heads: 
 
 
 def hstu_layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a,
-                   dy, eps: float = 1e-5):
+                   dy, eps: float = 1e-5, max_len: int = 0):
     """Gradients of :func:`hstu_layer_fwd` from dY: dict dx, dw1, db1, dw2, db2
-    (uvqk and a as the forward returned them)."""
+    (uvqk and a as the forward returned them; max_len, when given, bounds the
+    sequence lengths and lets the attention backward export dS)."""
     return ops.layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads, head_dim, uvqk, a, dy,
-                         eps)
+                         eps, max_len)

@@ -528,10 +528,12 @@ struct LayerBwdWs {
 
 // Carve-up of the layer backward's workspace (base == nullptr: sizes only).
 hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
-                            int32_t head_dim, void* base, LayerBwdWs* w, size_t* bytes) {
+                            int32_t head_dim, int32_t max_len, void* base, LayerBwdWs* w,
+                            size_t* bytes) {
   const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD;
   hstu_attn_desc ad = {};
-  ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim; ad.max_len = 1;
+  ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim;
+  ad.max_len = max_len > 0 ? max_len : 1;
   ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
   ad.stride_q = ad.stride_k = ad.stride_v = W; ad.stride_u = 0;
   size_t attn = 0;
@@ -566,9 +568,11 @@ hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t h
   return HSTU_OK;
 }
 
-hstu_status layer_bwd_check(int64_t M, int32_t batch, int32_t d_model, int32_t heads, int32_t head_dim) {
+hstu_status layer_bwd_check(int64_t M, int32_t batch, int32_t d_model, int32_t heads, int32_t head_dim,
+                            int32_t max_len) {
   if (M < 0 || M >= ((int64_t)1 << 31) || batch < 0 || heads < 1)
     return fail(HSTU_EINVAL, "bad sizes M=%lld batch=%d heads=%d", (long long)M, batch, heads);
+  if (max_len < 0 || max_len > (1 << 30)) return fail(HSTU_EINVAL, "max_len %d out of range", max_len);
   if (head_dim != 32 && head_dim != 64 && head_dim != 128)
     return fail(HSTU_EUNSUPPORTED, "head_dim %d is not supported", head_dim);
   if (d_model <= 0 || d_model % 128 || ((int64_t)heads * head_dim) % 128)
@@ -580,23 +584,24 @@ hstu_status layer_bwd_check(int64_t M, int32_t batch, int32_t d_model, int32_t h
 }  // namespace
 
 hstu_status hstu_layer_bwd_workspace_size(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
-                                          int32_t head_dim, size_t* bytes) {
-  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim);
+                                          int32_t head_dim, int32_t max_len, size_t* bytes) {
+  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim, max_len);
   if (st != HSTU_OK) return st;
   if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
   LayerBwdWs w;
-  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, nullptr, &w, bytes);
+  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, max_len, nullptr, &w, bytes);
   if (st != HSTU_OK) return st;
   return ok();
 }
 
 hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
-                           int32_t head_dim, const int64_t* seq_offsets, const int64_t* num_targets,
+                           int32_t head_dim, int32_t max_len, const int64_t* seq_offsets,
+                           const int64_t* num_targets,
                            const void* x, const void* w1, const float* b1, const void* w2,
                            const void* uvqk, const float* a, float eps, const void* dy, void* dx,
                            float* dw1, float* db1, float* dw2, float* db2, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim);
+  hstu_status st = layer_bwd_check(M, batch, d_model, heads, head_dim, max_len);
   if (st != HSTU_OK) return st;
   if (!(eps >= 0.f)) return fail(HSTU_EINVAL, "eps must be >= 0");
   if (batch > 0 && !seq_offsets) return fail(HSTU_EINVAL, "seq_offsets is NULL");
@@ -609,12 +614,12 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
     if (!aligned(q, 16)) return fail(HSTU_EINVAL, "layer backward buffers must be 16-byte aligned");
   LayerBwdWs w;
   size_t need = 0;
-  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, nullptr, &w, &need);
+  st = layer_bwd_carve(M, batch, d_model, heads, head_dim, max_len, nullptr, &w, &need);
   if (st != HSTU_OK) return st;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 workspace_bytes);
-  layer_bwd_carve(M, batch, d_model, heads, head_dim, workspace, &w, &need);
+  layer_bwd_carve(M, batch, d_model, heads, head_dim, max_len, workspace, &w, &need);
   hipStream_t s = (hipStream_t)stream;
   const int64_t HD = (int64_t)heads * head_dim, W = 4 * HD;
   if (M == 0) {                                  // no tokens: every gradient is 0
@@ -640,7 +645,8 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
   // attention backward (no gate, no bias) with dO = dA
   if (M > 0 && batch > 0) {
     hstu_attn_desc ad = {};
-    ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim; ad.max_len = 1;
+    ad.batch = batch; ad.heads = heads; ad.d_qk = head_dim; ad.d_v = head_dim;
+  ad.max_len = max_len > 0 ? max_len : 1;
     ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
     ad.stride_q = ad.stride_k = ad.stride_v = W; ad.stride_u = 0;
     st = hstu_attn_bwd(&ad, seq_offsets, num_targets, nullptr, nullptr, nullptr, uv + 2 * HD,

@@ -279,11 +279,13 @@ def layernorm_gate_fp8(a, u=None, eps: float = 1e-5):
 
 
 def layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int, uvqk, a, dy,
-              eps: float = 1e-5):
+              eps: float = 1e-5, max_len: int = 0):
     """Gradients of one HSTU layer (hstu_layer_bwd): dict dx (bf16), dw1, db1, dw2, db2 (fp32).
 
     x [M, d_model], w1 [d_model, 4*H*D], b1 [4*H*D], w2 [H*D, d_model] as in the
-    forward; uvqk [M, 4*H*D] and a [M, H*D] the forward's outputs; dy [M, d_model].
+    forward; uvqk [M, 4*H*D] and a [M, H*D] the forward's outputs; dy [M, d_model];
+    max_len a bound on the sequence lengths (0: none), which sizes the attention
+    backward's dS export.
     """
     lib = _lib.load()
     M, dm = x.shape
@@ -300,9 +302,11 @@ def layer_bwd(x, w1, b1, w2, seq_offsets, num_targets, heads: int, head_dim: int
     db2 = torch.empty((dm,), dtype=torch.float32, device=dev)
     B = seq_offsets.numel() - 1
     nbytes = ctypes.c_size_t()
-    _lib.check(lib.hstu_layer_bwd_workspace_size(M, B, dm, heads, head_dim, ctypes.byref(nbytes)))
+    _lib.check(lib.hstu_layer_bwd_workspace_size(M, B, dm, heads, head_dim, int(max_len),
+                                                 ctypes.byref(nbytes)))
     ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=dev)
-    _lib.check(lib.hstu_layer_bwd(M, B, dm, heads, head_dim, _ptr(seq_offsets), _ptr(num_targets),
+    _lib.check(lib.hstu_layer_bwd(M, B, dm, heads, head_dim, int(max_len), _ptr(seq_offsets),
+                                  _ptr(num_targets),
                                   _ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(uvqk), _ptr(a),
                                   float(eps), _ptr(dy), _ptr(dx), _ptr(dw1), _ptr(db1), _ptr(dw2),
                                   _ptr(db2), _ptr(ws), nbytes.value, _stream()))

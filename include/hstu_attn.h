@@ -290,14 +290,21 @@ HSTU_API hstu_status hstu_layernorm_gate_fp8(int64_t M, int64_t N, const float* 
  *   [M, d_model]. Outputs (overwritten): dx bf16 [M, d_model]; dw1 fp32
  *   [d_model, 4*H*D]; db1 fp32 [4*H*D]; dw2 fp32 [H*D, d_model]; db2 fp32
  *   [d_model]. Pre = X W1 + b1 is recomputed (not saved by the forward).
- *   workspace (device) >= hstu_layer_bwd_workspace_size bytes, 256-aligned.
- *   dQ, the bias gradients and the attention's own sums use floating-point
- *   atomics, so their last bits may differ between runs.
+ *   max_len: a bound on every sequence's length, or 0 for none. It sizes
+ *   the attention backward's exported dS tiles (about
+ *   H (ceil(max_len / 128) + 1) (M / 128 + batch) tiles of 16 KB, at most
+ *   4 GiB); with 0, or for a batch whose tiles exceed that room, the
+ *   attention backward recomputes dS for dQ instead (same results).
+ *   workspace (device) >= hstu_layer_bwd_workspace_size bytes (same sizes
+ *   and max_len), 256-aligned.
+ *   Every reduction runs in a fixed order (no atomics: this attention has no
+ *   bias tables), so results repeat exactly between runs.
  */
 HSTU_API hstu_status hstu_layer_bwd_workspace_size(int64_t M, int32_t batch, int32_t d_model,
-                                                   int32_t heads, int32_t head_dim, size_t* bytes);
+                                                   int32_t heads, int32_t head_dim, int32_t max_len,
+                                                   size_t* bytes);
 HSTU_API hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t heads,
-                                    int32_t head_dim, const int64_t* seq_offsets,
+                                    int32_t head_dim, int32_t max_len, const int64_t* seq_offsets,
                                     const int64_t* num_targets, const void* x, const void* w1,
                                     const float* b1, const void* w2, const void* uvqk,
                                     const float* a, float eps, const void* dy, void* dx,

@@ -157,12 +157,12 @@ def test_layer_validation(lib):
     assert lib.hstu_layernorm_gate(4, 512, FAKE, FAKE, 512, -1.0, FAKE, None) == _lib.HSTU_EINVAL
 
 
-def layer_bwd_call(lib, M=64, d_model=128, heads=2, head_dim=64, ws_bytes=1 << 30, **kw):
+def layer_bwd_call(lib, M=64, d_model=128, heads=2, head_dim=64, max_len=0, ws_bytes=1 << 30, **kw):
     a = dict(seq_offsets=FAKE, x=FAKE, w1=FAKE, b1=FAKE, w2=FAKE, uvqk=FAKE, a=FAKE, dy=FAKE,
              dx=FAKE, dw1=FAKE, db1=FAKE, dw2=FAKE, db2=FAKE, ws=ctypes.c_void_p(1 << 20),
              eps=1e-5)
     a.update(kw)
-    return lib.hstu_layer_bwd(M, 1, d_model, heads, head_dim, a["seq_offsets"], None, a["x"],
+    return lib.hstu_layer_bwd(M, 1, d_model, heads, head_dim, max_len, a["seq_offsets"], None, a["x"],
                               a["w1"], a["b1"], a["w2"], a["uvqk"], a["a"], a["eps"], a["dy"],
                               a["dx"], a["dw1"], a["db1"], a["dw2"], a["db2"], a["ws"], ws_bytes,
                               None)
@@ -170,14 +170,20 @@ def layer_bwd_call(lib, M=64, d_model=128, heads=2, head_dim=64, ws_bytes=1 << 3
 
 def test_layer_bwd_validation(lib):
     size = ctypes.c_size_t(0)
-    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 64, ctypes.byref(size)) == _lib.HSTU_OK
+    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 64, 0, ctypes.byref(size)) == _lib.HSTU_OK
     assert size.value > 0
-    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 48, ctypes.byref(size)) \
+    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 48, 0, ctypes.byref(size)) \
         == _lib.HSTU_EUNSUPPORTED
-    assert lib.hstu_layer_bwd_workspace_size(64, 1, 100, 2, 64, ctypes.byref(size)) \
+    assert lib.hstu_layer_bwd_workspace_size(64, 1, 100, 2, 64, 0, ctypes.byref(size)) \
         == _lib.HSTU_EUNSUPPORTED
-    assert lib.hstu_layer_bwd_workspace_size(-1, 1, 128, 2, 64, ctypes.byref(size)) \
+    assert lib.hstu_layer_bwd_workspace_size(-1, 1, 128, 2, 64, 0, ctypes.byref(size)) \
         == _lib.HSTU_EINVAL
+    big = ctypes.c_size_t(0)
+    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 64, 4096, ctypes.byref(big)) == _lib.HSTU_OK
+    assert big.value > size.value                          # room for the exported dS tiles
+    assert lib.hstu_layer_bwd_workspace_size(64, 1, 128, 2, 64, -1, ctypes.byref(big)) \
+        == _lib.HSTU_EINVAL
+    assert layer_bwd_call(lib, max_len=-5) == _lib.HSTU_EINVAL
     assert layer_bwd_call(lib, head_dim=48) == _lib.HSTU_EUNSUPPORTED
     assert layer_bwd_call(lib, heads=1, head_dim=64) == _lib.HSTU_EUNSUPPORTED  # H*D = 64
     assert layer_bwd_call(lib, eps=-1.0) == _lib.HSTU_EINVAL

@@ -156,7 +156,8 @@ def layer_bwd():
                                 t["num_targets"], li["heads"], li["head_dim"])
     g = hstu_layer_bwd(t["x"], t["w1"], t["b1"], t["w2"], t["seq_offsets"], t["num_targets"],
                        li["heads"], li["head_dim"], uvqk, a,
-                       torch.from_numpy(dy).to(dev, torch.bfloat16))
+                       torch.from_numpy(dy).to(dev, torch.bfloat16),
+                       max_len=int(li["lengths"].max()))
     torch.cuda.synchronize()
     print(f"layer backward workload: T={li['x'].shape[0]}", flush=True)
     return li, dy, {k: P.host(v) for k, v in g.items()}

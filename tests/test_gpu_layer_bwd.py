@@ -47,14 +47,19 @@ def _case(lengths, n_targets, d_model, heads, head_dim, seed):
     tx, tw1, tw2, tdy = bf(x), bf(w1), bf(w2), bf(dy)
     tb1, tb2 = f32(b1), f32(b2)
     y, a, uvqk = hstu_layer_fwd(tx, tw1, tb1, tw2, tb2, i64(offs), i64(nt), heads, head_dim)
-    g = hstu_layer_bwd(tx, tw1, tb1, tw2, i64(offs), i64(nt), heads, head_dim, uvqk, a, tdy)
-    torch.cuda.synchronize()
     want = oracle_layer_bwd(x, w1, b1, w2, b2, offs, nt, heads, head_dim, dy)
-    tag = f"lengths {list(lengths)} targets {list(nt)} d_model {d_model} H{heads} D{head_dim}"
-    print(tag, flush=True)
-    for key in ("dx", "dw1", "db1", "dw2", "db2"):
-        e = P.rel_l2(P.host(g[key]), want[key])
-        assert e <= P.BF16_REL, (tag, key, e)
+    # max_len 0: the attention backward recomputes dS for dQ; the longest
+    # length: it exports dS tiles instead
+    for max_len in (0, int(lengths.max()) if len(lengths) else 0):
+        g = hstu_layer_bwd(tx, tw1, tb1, tw2, i64(offs), i64(nt), heads, head_dim, uvqk, a, tdy,
+                           max_len=max_len)
+        torch.cuda.synchronize()
+        tag = (f"lengths {list(lengths)} targets {list(nt)} d_model {d_model} H{heads} D{head_dim}"
+               f" max_len {max_len}")
+        print(tag, flush=True)
+        for key in ("dx", "dw1", "db1", "dw2", "db2"):
+            e = P.rel_l2(P.host(g[key]), want[key])
+            assert e <= P.BF16_REL, (tag, key, e)
 
 
 def test_layer_bwd_small():
