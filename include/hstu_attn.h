@@ -83,7 +83,16 @@ typedef struct {
   int64_t stride_q, stride_k, stride_v, stride_u;  /* elements between tokens   */
 } hstu_attn_desc;
 
-/* Bytes of workspace hstu_attn_fwd / hstu_attn_bwd need for this shape. */
+/*
+ * Bytes of workspace hstu_attn_fwd / hstu_attn_bwd need for this shape.
+ * For bf16, the backward's figure includes room for the dS tiles it hands
+ * from the key-block pass to the dQ pass: 16 KB per (128-key block, 64-query
+ * tile) pair, sized for sequences no longer than max_len,
+ * heads * (ceil(max_len / 128) + 1) * (total_tokens / 128 + batch) tiles,
+ * capped at 4 GiB (about 1.5 GB for 8 sequences of up to 8192 rows, 4 heads).
+ * A batch whose tiles do not fit computes dQ by recomputing dS instead, with
+ * the same results.
+ */
 HSTU_API hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
 HSTU_API hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
 
