@@ -191,6 +191,8 @@ def main():
         "roofline": roofline,
     }
 
+    out["bucketize"] = bench_bucketize(torch, _lib, ops, inp, wl, offs, ts)
+
     if not args.no_layer:
         out["layer_mfalcon"] = bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd)
         out["cached_scoring"] = bench_cached(torch)
@@ -200,6 +202,27 @@ def main():
         out["cpu_baseline"] = cpu_baseline(inp, wl)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_bucketize(torch, _lib, ops, inp, wl, offs, ts, iters=10):
+    """The standalone rab bucketiser (hstu_rab_bucketize) on the efficiency
+    workload: position (uint16) and time (uint8) buckets of every unmasked
+    pair, timed by the library's HIP events around its kernel. Algorithmic
+    bytes: 3 written per pair plus the 8-byte timestamps read once."""
+    from hstu_pointwise_attention_amd.flops import unmasked_pairs_host
+    pairs = unmasked_pairs_host(inp["lengths"], None)
+    run = lambda: ops.rab_bucketize(offs, wl.max_len, timestamps=ts, n_time_buckets=wl.n_time_buckets)
+    run()
+    torch.cuda.synchronize()
+    with _lib.KernelTimer() as kt:
+        for _ in range(iters):
+            run()
+        torch.cuda.synchronize()
+    ms = kt.avg_ms("bucketize")
+    nbytes = 3 * pairs + 8 * int(inp["seq_offsets"][-1])
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "pairs": int(pairs), "bytes": int(nbytes), "gb_per_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_layer(torch, W, hstu_layer_fwd, hstu_layer_bwd, iters=10):
