@@ -23,9 +23,10 @@ STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_EINVAL", -2: "HSTU_EUNSUPPORTED",
                 -3: "HSTU_EWORKSPACE", -4: "HSTU_EHIP"}
 
 # Every symbol the header declares.
-EXPORTS = ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size", "hstu_attn_fwd",
+EXPORTS = ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size",
+           "hstu_attn_bwd_workspace_size_min", "hstu_attn_bwd_report", "hstu_attn_fwd",
            "hstu_attn_fwd_cached_workspace_size", "hstu_attn_fwd_cached",
-           "hstu_attn_bwd", "hstu_rab_bucketize", "hstu_linear", "hstu_layernorm_gate",
+           "hstu_attn_bwd", "hstu_rab_pair_offsets", "hstu_rab_bucketize", "hstu_linear", "hstu_layernorm_gate",
            "hstu_layer_bwd_workspace_size", "hstu_layer_bwd",
            "hstu_fp8_quantize_rows", "hstu_fp8_prepare_weight", "hstu_fp8_linear",
            "hstu_layernorm_gate_fp8",
@@ -54,7 +55,12 @@ class AttnDesc(ctypes.Structure):
         ("stride_k", ctypes.c_int64),
         ("stride_v", ctypes.c_int64),
         ("stride_u", ctypes.c_int64),
+        ("deterministic", ctypes.c_int32),
     ]
+
+
+class BwdInfo(ctypes.Structure):
+    _fields_ = [("dq_from_ds", ctypes.c_int32), ("rab_deterministic", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -62,6 +68,8 @@ _I64 = ctypes.c_int64
 _SIGS = {
     "hstu_attn_fwd_workspace_size": [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)],
     "hstu_attn_bwd_workspace_size": [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)],
+    "hstu_attn_bwd_workspace_size_min": [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)],
+    "hstu_attn_bwd_report": [ctypes.POINTER(AttnDesc), _P, ctypes.c_size_t, ctypes.POINTER(BwdInfo), _P],
     "hstu_attn_fwd": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       ctypes.c_size_t, _P],
     "hstu_attn_fwd_cached_workspace_size": [ctypes.POINTER(AttnDesc), _I64,
@@ -71,6 +79,7 @@ _SIGS = {
     "hstu_attn_bwd": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "hstu_rab_bucketize": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P],
+    "hstu_rab_pair_offsets": [ctypes.POINTER(AttnDesc), _P, _P, _P, _P],
     "hstu_linear": [_I64, _I64, _I64, _P, _I64, _P, _P, _P, ctypes.c_int32, _P],
     "hstu_layernorm_gate": [_I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P],
     "hstu_layer_bwd_workspace_size": [_I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -55,6 +55,8 @@ hstu_status check_desc(const hstu_attn_desc* d) {
   if (d->max_len < 1 || d->max_len > (1 << 30)) return fail(HSTU_EINVAL, "max_len %d out of range", d->max_len);
   if (d->n_time_buckets < 0 || d->n_time_buckets > 1024)
     return fail(HSTU_EINVAL, "n_time_buckets %d outside [0, 1024]", d->n_time_buckets);
+  if (d->deterministic != 0 && d->deterministic != 1)
+    return fail(HSTU_EINVAL, "deterministic %d must be 0 or 1", d->deterministic);
   if (d->rab_heads != 1 && d->rab_heads != d->heads)
     return fail(HSTU_EINVAL, "rab_heads %d must be 1 or heads (%d)", d->rab_heads, d->heads);
   if (d->total_tokens < 0 || d->total_tokens >= ((int64_t)1 << 31))
@@ -83,6 +85,8 @@ AttnParams base_params(const hstu_attn_desc* d, const int64_t* seq_offsets, cons
   p.max_len = d->max_len;
   p.n_time_buckets = rab_time ? d->n_time_buckets : 0;
   p.rab_heads = d->rab_heads;
+  p.det = d->deterministic;
+  p.n_time_room = d->n_time_buckets;
   p.T = d->total_tokens;
   p.sq = d->stride_q;
   p.sk = d->stride_k;
@@ -174,9 +178,9 @@ hipError_t dispatch_bwd(const AttnParams& p, hipStream_t s) {
 template <>
 hipError_t dispatch_bwd<bf16>(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
-    case 32: return BWD_K16 ? launch_bwd_k16<32>(p, s) : launch_bwd<bf16, 32>(p, s);
-    case 64: return BWD_K16 ? launch_bwd_k16<64>(p, s) : launch_bwd<bf16, 64>(p, s);
-    case 128: return BWD_K16 ? launch_bwd_k16<128>(p, s) : launch_bwd<bf16, 128>(p, s);
+    case 32: return launch_bwd_k16<32>(p, s);
+    case 64: return launch_bwd_k16<64>(p, s);
+    case 128: return launch_bwd_k16<128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -216,6 +220,7 @@ template <typename T>
 hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
   hipError_t e = launch_bwd_pre<T>(p, s);
   if (e == hipSuccess) e = dispatch_bwd<T>(p, s);
+  if (e == hipSuccess) e = launch_rab_reduce(p, s);
   AttnParams pq = p;                             // the dQ pass walks query blocks
   pq.items = p.items_q;
   if (e == hipSuccess) e = dispatch_dq<T>(pq, s);
@@ -233,7 +238,7 @@ hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* byt
   if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
   AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                              nullptr, nullptr);
-  *bytes = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype));
+  *bytes = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype), false);
   return ok();
 }
 
@@ -243,7 +248,17 @@ hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* byt
   if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
   AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                              nullptr, nullptr);
-  *bytes = carve_workspace(p, nullptr, true, elem_bytes(desc->dtype));
+  *bytes = carve_workspace(p, nullptr, true, elem_bytes(desc->dtype), true);
+  return ok();
+}
+
+hstu_status hstu_attn_bwd_workspace_size_min(const hstu_attn_desc* desc, size_t* bytes) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return fail(HSTU_EINVAL, "bytes is NULL");
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr);
+  *bytes = carve_workspace(p, nullptr, true, elem_bytes(desc->dtype), false);
   return ok();
 }
 
@@ -265,11 +280,11 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
                              v, u);
   p.o = o;
   p.a_saved = a_saved;
-  const size_t need = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype));
+  const size_t need = carve_workspace(p, nullptr, false, elem_bytes(desc->dtype), false);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 workspace_bytes);
-  carve_workspace(p, workspace, false, elem_bytes(desc->dtype));
+  carve_workspace(p, workspace, false, elem_bytes(desc->dtype), false);
   if (p.T == 0 || p.B == 0) return ok();
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_prep(p, s);
@@ -396,11 +411,13 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   p.d_rab_pos = rab_pos ? d_rab_pos : nullptr;
   p.d_rab_time = rab_time ? d_rab_time : nullptr;
   const int eb = elem_bytes(desc->dtype);
-  const size_t need = carve_workspace(p, nullptr, true, eb);
+  const size_t need = carve_workspace(p, nullptr, true, eb, false);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-    return fail(HSTU_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                workspace_bytes);
-  carve_workspace(p, workspace, true, eb);
+    return fail(HSTU_EWORKSPACE, "workspace needs at least %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  // the dS export when the workspace holds its room, else the recompute pass
+  const bool ds_room = workspace_bytes >= carve_workspace(p, nullptr, true, eb, true);
+  carve_workspace(p, workspace, true, eb, ds_room);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (p.T > 0 && p.B > 0) {
@@ -440,6 +457,18 @@ hstu_status hstu_rab_bucketize(const hstu_attn_desc* desc, const int64_t* seq_of
   p.timestamps = timestamps;
   hipError_t e = launch_bucketize(p, pair_offsets, bp_out, bt_out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hstu_rab_bucketize launch");
+  return ok();
+}
+
+hstu_status hstu_rab_pair_offsets(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                                  const int64_t* num_targets, int64_t* pair_offsets, void* stream) {
+  if (!desc) return fail(HSTU_EINVAL, "desc is NULL");
+  if (desc->batch < 0) return fail(HSTU_EINVAL, "batch %d < 0", desc->batch);
+  if (!pair_offsets || (desc->batch > 0 && !seq_offsets))
+    return fail(HSTU_EINVAL, "seq_offsets and pair_offsets are required");
+  hipError_t e = launch_pair_offsets(seq_offsets, num_targets, desc->batch, pair_offsets,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hstu_rab_pair_offsets launch");
   return ok();
 }
 
@@ -536,8 +565,11 @@ hstu_status layer_bwd_carve(int64_t M, int32_t batch, int32_t d_model, int32_t h
   ad.max_len = max_len > 0 ? max_len : 1;
   ad.n_time_buckets = 0; ad.rab_heads = 1; ad.dtype = HSTU_DTYPE_BF16; ad.total_tokens = M;
   ad.stride_q = ad.stride_k = ad.stride_v = W; ad.stride_u = 0;
+  // max_len 0 (no bound): the attention's minimum workspace, whose dQ pass
+  // recomputes dS; otherwise room for the dS export
   size_t attn = 0;
-  hstu_status st = hstu_attn_bwd_workspace_size(&ad, &attn);
+  hstu_status st = max_len > 0 ? hstu_attn_bwd_workspace_size(&ad, &attn)
+                               : hstu_attn_bwd_workspace_size_min(&ad, &attn);
   if (st != HSTU_OK) return st;
   size_t off = 0;
   auto take = [&](size_t b) {
@@ -660,6 +692,37 @@ hstu_status hstu_layer_bwd(int64_t M, int32_t batch, int32_t d_model, int32_t he
   run(launch_wgrad(d_model, W, M, x, d_model, w.d_pre, W, dw1, w.part, s));
   run(launch_linear_nt(M, W, d_model, w.d_pre, W, w1, W, dx, s));
   if (e != hipSuccess) return hip_fail(e, "hstu_layer_bwd launch");
+  return ok();
+}
+
+hstu_status hstu_attn_bwd_report(const hstu_attn_desc* desc, const void* workspace,
+                                 size_t workspace_bytes, hstu_attn_bwd_info* info, void* stream) {
+  hstu_status st = check_desc(desc);
+  if (st != HSTU_OK) return st;
+  if (!info) return fail(HSTU_EINVAL, "info is NULL");
+  AttnParams p = base_params(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, nullptr);
+  const int eb = elem_bytes(desc->dtype);
+  const size_t need = carve_workspace(p, nullptr, true, eb, false);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(HSTU_EWORKSPACE, "workspace needs at least %zu bytes, 256-byte aligned (got %zu)",
+                need, workspace_bytes);
+  const bool ds_room = workspace_bytes >= carve_workspace(p, nullptr, true, eb, true);
+  carve_workspace(p, const_cast<void*>(workspace), true, eb, ds_room);
+  info->dq_from_ds = 0;
+  info->rab_deterministic = 0;
+  if (p.T == 0 || p.B == 0) {
+    info->rab_deterministic = p.det;             // nothing summed: trivially repeatable
+    return ok();
+  }
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  // the dS-export and deterministic flags are adjacent (ds_on, det_on)
+  int32_t flags[2] = {0, 0};
+  const int32_t* dev_flags = p.ds_on ? p.ds_on : (p.det_on ? p.det_on - 1 : nullptr);
+  if (e == hipSuccess && dev_flags) e = hipMemcpy(flags, dev_flags, sizeof(flags), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hstu_attn_bwd_report");
+  info->dq_from_ds = p.ds_on ? flags[0] : 0;
+  info->rab_deterministic = p.det_on ? flags[1] : 0;
   return ok();
 }
 

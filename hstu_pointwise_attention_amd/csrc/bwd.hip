@@ -1,4 +1,5 @@
-// Fused backward of jagged HSTU pointwise attention for gfx950.
+// Key-block backward of jagged HSTU pointwise attention for gfx950, fp32
+// (the bf16 key-block kernel is bwd_k16.hip).
 //
 // One workgroup (4 waves) owns 128 keys of one sequence and one head; wave w
 // owns keys 32w..32w+31 and keeps their K, V fragments and the dK, dV
@@ -24,20 +25,6 @@
 // window instead.
 #include "internal.h"
 
-#ifndef BWD_SPLIT_PIN
-#define BWD_SPLIT_PIN 0
-#endif
-#ifndef BWD_DK_PIPE
-#define BWD_DK_PIPE 0
-#endif
-#ifndef BWD_KV_WAVES
-#define BWD_KV_WAVES 2
-#endif
-
-#ifndef BWD_PIPE
-#define BWD_PIPE true
-#endif
-
 namespace hstu {
 
 namespace {
@@ -46,9 +33,6 @@ namespace {
 // need an odd multiple of 16 bytes, transpose reads need consecutive rows
 // >= 8 banks apart.
 template <typename T, int D> struct BwdLd;
-template <> struct BwdLd<bf16, 32> { static constexpr int Q = 56; };
-template <> struct BwdLd<bf16, 64> { static constexpr int Q = 72; };
-template <> struct BwdLd<bf16, 128> { static constexpr int Q = 152; };
 template <> struct BwdLd<float, 32> { static constexpr int Q = 36; };
 template <> struct BwdLd<float, 64> { static constexpr int Q = 68; };
 
@@ -77,9 +61,12 @@ struct BwdCfg {
   // l adds into copy l % HREP, HREP_LD floats apart so a bucket's copies sit
   // in different banks) keep the per-element adds of one instruction from
   // piling onto one address; larger tables use a single copy.
+  // Deterministic mode keeps one copy per wave instead (no two waves add
+  // into one address, so the order of every sum is fixed by the program).
   static constexpr int HREP = 16, HREP_NT = 128, HREP_LD = HREP_NT + 1;
-  static constexpr int THIST = HREP * HREP_LD > MAX_TIME ? HREP * HREP_LD : MAX_TIME;
-  static constexpr bool PIPE = BWD_PIPE;
+  static constexpr int NW = NT / kWave;
+  static constexpr int THIST_DET = NW * (MAX_TIME + 1);
+  static constexpr int THIST = HREP * HREP_LD > THIST_DET ? HREP * HREP_LD : THIST_DET;
   static_assert(BM * CPR % NT == 0, "staging");
 };
 
@@ -91,7 +78,7 @@ struct BwdSmem {
   T qs[C::BM * C::Q_LD];
   T das[C::BM * C::Q_LD];
   float win[C::WIN];
-  float wing[C::WIN];
+  float wing[C::NW * C::WIN];    // position window (one copy per wave in deterministic mode)
   int64_t tsq[C::BM];
   T dsd[C::NDIAG * C::DG_LD];
   int64_t tsk[C::BN];            // timestamps of the key block
@@ -99,31 +86,15 @@ struct BwdSmem {
   float thist[C::THIST];
 };
 
-__device__ __forceinline__ float sum8(const bf16x8& v) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const bf16x2 pr = {v[2 * m], v[2 * m + 1]};
-    s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
-  }
-  return s;
-}
-
 __device__ __forceinline__ float sum8(const f32x8& v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
-// KV 0: dK, dV and the rab gradients in one pass; 1: dV only (S, SiLU,
-// s^T dA'); 2: dK and the rab gradients only (S, dP, dS, dS^T Q). The split
-// form spends one more GEMM (S twice) to fit two waves per SIMD.
-template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm, const WorkItem wi,
                                          const SeqInfo si, const int head) {
   using C = BwdCfg<T, D>;
   using F = typename Frag<T>::type;
-  constexpr bool DV = KV != 2;                   // this pass computes dV
-  constexpr bool DK = KV != 1;                   // this pass computes dK and d_rab
   const int H = p.H;
   const int L = si.len, hist = si.hist;
   const int64_t start = si.start;
@@ -140,8 +111,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   // straight-line code the scheduler can interleave.
   constexpr bool has_pos = POS;
   constexpr bool has_time = TIME;
-  constexpr bool pos_grad = has_pos && DK;       // this pass sums d_rab_pos
-  constexpr bool time_grad = has_time && DK;     // this pass sums d_rab_time
+  constexpr bool pos_grad = has_pos;
+  constexpr bool time_grad = has_time;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
   // timestamps and run in the second instantiation of the kernel.
@@ -156,26 +127,35 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   const T* __restrict__ dag = reinterpret_cast<const T*>(p.d_a);
 
   for (int x = tid; x < p.n_time_buckets; x += C::NT) sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+  // Deterministic mode: every sum has a fixed order (per-wave LDS copies,
+  // partials in the workspace instead of global atomics).
+  const bool det = p.det != 0 && *p.det_on != 0;
+  const int nt_ld = p.n_time_buckets + 1;
   for (int x = tid; x < C::THIST; x += C::NT) sm.thist[x] = 0.f;
   const bool hrep = p.n_time_buckets <= C::HREP_NT;
-  float* const thist_lane = sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
-  for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
+  float* const thist_lane = det ? sm.thist + wave * nt_ld : sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
+  float* const thist_wave = det ? sm.thist + wave * nt_ld : sm.thist;
+  for (int x = tid; x < C::NW * C::WIN; x += C::NT) sm.wing[x] = 0.f;
+  float* const wing_w = sm.wing + (det ? wave * C::WIN : 0);
+  float* const part_row =
+      det ? p.part_pos + (p.tile_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kPartW
+          : nullptr;
   // Diagonal-copy entries that no element maps to stay zero for the whole loop.
   if (pos_grad)
     for (int x = tid; x < C::NDIAG * C::DG_LD; x += C::NT) sm.dsd[x] = from_f32<T>(0.f);
 
   // Resident K, V fragments of this lane's key (B operands of Q K^T, dA' V^T).
-  F kf[C::KC], vf[DK ? C::KC : 1];
+  F kf[C::KC], vf[C::KC];
 #pragma unroll
   for (int c = 0; c < C::KC; ++c) {
     if (key_ok) {
       kf[c] = ld_frag(kg + (start + j) * p.sk + (int64_t)head * D + 16 * c + 8 * g);
-      if constexpr (DK) vf[c] = ld_frag(vg + (start + j) * p.sv + (int64_t)head * D + 16 * c + 8 * g);
+      vf[c] = ld_frag(vg + (start + j) * p.sv + (int64_t)head * D + 16 * c + 8 * g);
     } else {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         kf[c][m] = from_f32<T>(0.f);
-        if constexpr (DK) vf[c][m] = from_f32<T>(0.f);
+        vf[c][m] = from_f32<T>(0.f);
       }
     }
   }
@@ -235,13 +215,13 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     if (has_pos && tid < C::WIN) sm.win[tid] = winreg;
   };
 
-  f32x16 acc_dk[DK ? C::DB : 1], acc_dv[DV ? C::DB : 1];
+  f32x16 acc_dk[C::DB], acc_dv[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      if constexpr (DK) acc_dk[db][r] = 0.f;
-      if constexpr (DV) acc_dv[db][r] = 0.f;
+      acc_dk[db][r] = 0.f;
+      acc_dv[db][r] = 0.f;
     }
 
   // Per-lane base of this lane's entries in the diagonal copy.
@@ -261,19 +241,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     // Keep the loop-carried MFMA operands and accumulators in the
     // accumulation registers: left to itself the allocator parks them in
     // VGPRs between tiles and copies them back and forth every iteration.
-    if constexpr (KV == 0 || BWD_SPLIT_PIN) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        if constexpr (DK) asm volatile("" : "+a"(acc_dk[db]));
-        if constexpr (DV) asm volatile("" : "+a"(acc_dv[db]));
-      }
-    }
-    // (the split passes leave K and V to the allocator: their VGPR and AGPR
-    // budgets are half as large)
-    if constexpr (KV == 0) {
+    for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(acc_dk[db]), "+a"(acc_dv[db]));
 #pragma unroll
-      for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
-    }
+    for (int c = 0; c < C::KC; ++c) asm volatile("" : "+a"(kf[c]), "+a"(vf[c]));
     if (more) load_tile(q0 + C::BM);
 
     // Tiles of history rows only sum the position gradient along diagonals of
@@ -311,9 +282,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       // below stays branch-free).
       auto sp_block = [&](auto pd, int qb, f32x16& acc_s, f32x16& acc_p) {
         constexpr bool PD = decltype(pd)::value;
-        if constexpr (DK)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc_p[r] = 0.f;
         if constexpr (PD) {
           // history rows: entry y = (BN - 1 - jl) + ql, a per-lane base plus constants
           const float* w = sm.win + (C::BN - 1 - jl) + 32 * qb + 4 * g;
@@ -333,7 +303,7 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         for (int c = 0; c < C::KC; ++c) {
           const F a = ld_frag(sm.qs + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
           mfma_32x32x16(acc_s, a, kf[c]);
-          if constexpr (DK) {
+          {
             const F b = ld_frag(sm.das + (32 * qb + l32) * C::Q_LD + 16 * c + 8 * g);
             mfma_32x32x16(acc_p, b, vf[c]);
           }
@@ -364,11 +334,10 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           b_top = TM == 2 ? time_bucket_rel((uint32_t)sm.tsq[q_hi], (uint32_t)ts_j, t_last)
                           : time_bucket_wide(sm.tsq[q_hi], ts_j, t_last);
         }
-        // PIPE: the next block's S and dP MFMAs are issued before this
-        // block's elementwise work so the two overlap.
+        // The next block's S and dP MFMAs are issued before this block's
+        // elementwise work so the two overlap.
         f32x16 acc_sb[C::QB], acc_pb[C::QB];
-        // (the dK pass at two waves per SIMD lacks the registers)
-        constexpr bool PIPE = C::PIPE && (KV != 2 || BWD_DK_PIPE);
+        constexpr bool PIPE = true;
         if constexpr (PIPE) sp_block(pd, 0, acc_sb[0], acc_pb[0]);
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
@@ -380,16 +349,14 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           f32x16& acc_s = acc_sb[qb];
           f32x16& acc_p = acc_pb[qb];
           // B operands of the first 16-query chunk's dV / dK products, read
-          // now so the elementwise work below covers the LDS latency (one
-          // wave per SIMD); with two, the other wave covers it and the
-          // registers are short.
-          constexpr bool PREFETCH = KV == 0;
-          F bv0[DV ? C::DB : 1], bk0[DK ? C::DB : 1];
+          // now so the elementwise work below covers the LDS latency.
+          constexpr bool PREFETCH = true;
+          F bv0[C::DB], bk0[C::DB];
           if constexpr (PREFETCH) {
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              if constexpr (DV) bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
-              if constexpr (DK) bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+              bv0[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
+              bk0[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb, 32 * qb + 8);
             }
           }
           int bts[16];
@@ -416,14 +383,14 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             }
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * kNegLog2e));
             float sl = s * sg;
-            float ds = DK ? acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl)) : 0.f;
+            float ds = acc_p[r] * (sg + __builtin_fmaf(-sl, sg, sl));
             if constexpr (MASK) {
               const bool ok = j <= i && (j < hist || j == i) && i < L;
               sl = ok ? sl : 0.f;
               ds = ok ? ds : 0.f;
             }
             acc_s[r] = sl;
-            if constexpr (DK) acc_p[r] = ds;
+            acc_p[r] = ds;
             bts[r] = bt;
             if constexpr (TM <= 1 && time_grad) g_all += ds;
             if constexpr (TM == 1 && time_grad) g_hi += hi ? ds : 0.f;
@@ -436,12 +403,12 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           // candidate rows; LDS float atomics cost far more than stores.
           const bool to_copy = pos_grad && (PD || pos_diag);
 #pragma unroll
-          for (int r = 0; r < 16 && DK; ++r) {
+          for (int r = 0; r < 16; ++r) {
             const float ds = acc_p[r];
             if constexpr (pos_grad && !PD) {
               if (!pos_diag) {
                 const int i = q0 + 32 * qb + 8 * (r >> 2) + 4 * g + (r & 3);
-                atomicAdd(&sm.wing[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
+                atomicAdd(&wing_w[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
               }
             }
             if constexpr (time_grad && TM >= 2) {
@@ -456,26 +423,26 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
           F sf[2], df[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            if constexpr (DV) sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
-            if constexpr (DK) df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
+            sf[h] = pack8<T>(reinterpret_cast<const float*>(&acc_s) + 8 * h);
+            df[h] = pack8<T>(reinterpret_cast<const float*>(&acc_p) + 8 * h);
           }
           if constexpr (PREFETCH) {
             // second chunk's operands in flight while the first chunk's MFMAs run
-            F bv1[DV ? C::DB : 1], bk1[DK ? C::DB : 1];
+            F bv1[C::DB], bk1[C::DB];
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              if constexpr (DV) bv1[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
-              if constexpr (DK) bk1[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+              bv1[db] = ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
+              bk1[db] = ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, 32 * qb + 16, 32 * qb + 24);
             }
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[0], bv0[db]);
-              if constexpr (DK) mfma_32x32x16(acc_dk[db], df[0], bk0[db]);
+              mfma_32x32x16(acc_dv[db], sf[0], bv0[db]);
+              mfma_32x32x16(acc_dk[db], df[0], bk0[db]);
             }
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-              if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
-              if constexpr (DK) mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
+              mfma_32x32x16(acc_dv[db], sf[1], bv1[db]);
+              mfma_32x32x16(acc_dk[db], df[1], bk1[db]);
             }
           } else {
 #pragma unroll
@@ -483,8 +450,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
 #pragma unroll
               for (int db = 0; db < C::DB; ++db) {
                 const int kr = 32 * qb + 16 * h;
-                if constexpr (DV) mfma_32x32x16(acc_dv[db], sf[h], ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8));
-                if constexpr (DK) mfma_32x32x16(acc_dk[db], df[h], ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8));
+                mfma_32x32x16(acc_dv[db], sf[h], ld_frag_kmajor(sm.das, C::Q_LD, 32 * db, kr, kr + 8));
+                mfma_32x32x16(acc_dk[db], df[h], ld_frag_kmajor(sm.qs, C::Q_LD, 32 * db, kr, kr + 8));
               }
           }
         }
@@ -498,8 +465,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
             g_all = wave_sum(g_all);
             if constexpr (TM == 1) g_hi = wave_sum(g_hi);
             if (lane == 0) {
-              atomicAdd(&sm.thist[b_lo], g_all - g_hi);
-              if constexpr (TM == 1) atomicAdd(&sm.thist[b_hi], g_hi);
+              atomicAdd(&thist_wave[b_lo], g_all - g_hi);
+              if constexpr (TM == 1) atomicAdd(&thist_wave[b_hi], g_hi);
             }
           }
         }
@@ -555,7 +522,9 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
         const T* row = sm.dsd + dd * C::DG_LD;
 #pragma unroll
         for (int c = 0; c < C::BM / 8; ++c) sum += sum8(ld_frag(row + 8 * c));
-        if (sum != 0.f)
+        if (det)
+          part_row[(int64_t)n * kPartW + dd] = sum;
+        else if (sum != 0.f)
           atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
                         pos_bucket(k0 - q0 + (C::BN - 1) - dd, p.max_len),
                     sum);
@@ -563,13 +532,22 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
     }
     if (pos_grad && !pos_diag && tid < C::WIN) {
       // Flush the position-gradient window of this tile.
-      const float gsum = sm.wing[tid];
-      if (gsum != 0.f) {
-        const int p_min = min(q0, hist);
-        atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
-                      pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len),
-                  gsum);
-        sm.wing[tid] = 0.f;
+      if (det) {
+        float gsum = 0.f;
+        for (int w = 0; w < C::NW; ++w) {
+          gsum += sm.wing[w * C::WIN + tid];
+          sm.wing[w * C::WIN + tid] = 0.f;
+        }
+        part_row[(int64_t)n * kPartW + tid] = gsum;
+      } else {
+        const float gsum = sm.wing[tid];
+        if (gsum != 0.f) {
+          const int p_min = min(q0, hist);
+          atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos +
+                        pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len),
+                    gsum);
+          sm.wing[tid] = 0.f;
+        }
       }
     }
   }
@@ -577,10 +555,16 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   // Time-gradient histogram of this workgroup.
   if constexpr (time_grad) {
     __syncthreads();
+    const int64_t slot = det ? ((int64_t)p.blk_base[wi.seq] + wi.blk) * H + head : 0;
     for (int x = tid; x < p.n_time_buckets; x += C::NT) {
       float gsum = 0.f;
-      for (int c = 0; c < (hrep ? C::HREP : 1); ++c) gsum += sm.thist[c * C::HREP_LD + x];
-      if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
+      if (det) {
+        for (int w = 0; w < C::NW; ++w) gsum += sm.thist[w * nt_ld + x];
+        p.part_time[slot * p.n_time_buckets + x] = gsum;
+      } else {
+        for (int c = 0; c < (hrep ? C::HREP : 1); ++c) gsum += sm.thist[c * C::HREP_LD + x];
+        if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
+      }
     }
   }
 
@@ -593,62 +577,54 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
       const int jj = jw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (jj < L) {
         const int64_t o = ((start + jj) * H + head) * (int64_t)D + 32 * db + l32;
-        if constexpr (DK) reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
-        if constexpr (DV) reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
+        reinterpret_cast<T*>(p.dk)[o] = from_f32<T>(acc_dk[db][r]);
+        reinterpret_cast<T*>(p.dv)[o] = from_f32<T>(acc_dv[db][r]);
       }
     }
   }
 }
 
-#define HSTU_BWD_KERNEL(NAME, WAVES)                                                           \
-  template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>                         \
-  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))         \
-  void NAME(AttnParams p) {                                                                    \
-    __shared__ BwdSmem<T, D> sm;                                                               \
-    if constexpr (WIDE) {                                                                      \
-      /* rare sequences needing 64-bit timestamps: a small grid walks the work slots */        \
-      if (p.n_items[1] == 0) return;                                                           \
-      const int64_t slots = (int64_t)*p.n_items * p.H;                                         \
-      for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {                                \
-        const int item = (int)(w / p.H);                                                       \
-        const int head = (int)(w - (int64_t)item * p.H);                                       \
-        const WorkItem wi = p.items[item];                                                     \
-        const SeqInfo si = p.seq[wi.seq];                                                      \
-        if ((si.flags & kSeqWideTs) == 0) continue;                                            \
-        bwd_body<T, D, true, POS, TIME, KV>(p, sm, wi, si, head);                              \
-        __syncthreads(); /* the next slot reuses the LDS */                                    \
-      }                                                                                        \
-    } else {                                                                                   \
-      const int item = blockIdx.x / p.H;                                                       \
-      const int head = blockIdx.x - item * p.H;                                                \
-      if (item >= *p.n_items) return;                                                          \
-      const WorkItem wi = p.items[item];                                                       \
-      const SeqInfo si = p.seq[wi.seq];                                                        \
-      if ((si.flags & kSeqWideTs) != 0) return; /* the other instantiation takes it */         \
-      bwd_body<T, D, false, POS, TIME, KV>(p, sm, wi, si, head);                               \
-    }                                                                                          \
+// K, V, dK and dV stay in registers: one wave per SIMD.
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void hstu_bwd_kernel(AttnParams p) {
+  __shared__ BwdSmem<T, D> sm;
+  if constexpr (WIDE) {
+    // rare sequences needing 64-bit timestamps: a small grid walks the work slots
+    if (p.n_items[1] == 0) return;
+    const int64_t slots = (int64_t)*p.n_items * p.H;
+    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
+      const int item = (int)(w / p.H);
+      const int head = (int)(w - (int64_t)item * p.H);
+      const WorkItem wi = p.items[item];
+      const SeqInfo si = p.seq[wi.seq];
+      if ((si.flags & kSeqWideTs) == 0) continue;
+      bwd_body<T, D, true, POS, TIME>(p, sm, wi, si, head);
+      __syncthreads();                             // the next slot reuses the LDS
+    }
+  } else {
+    const int item = blockIdx.x / p.H;
+    const int head = blockIdx.x - item * p.H;
+    if (item >= *p.n_items) return;
+    const WorkItem wi = p.items[item];
+    const SeqInfo si = p.seq[wi.seq];
+    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+    bwd_body<T, D, false, POS, TIME>(p, sm, wi, si, head);
   }
-// The one-pass form holds dK, dV, K and V in registers: one wave per SIMD.
-// The dV-only and dK-only passes fit two.
-HSTU_BWD_KERNEL(hstu_bwd_kernel, 1)
-HSTU_BWD_KERNEL(hstu_bwd_split_kernel, BWD_KV_WAVES)
-#undef HSTU_BWD_KERNEL
-
-template <typename T, int D, bool WIDE, bool POS, bool TIME, int KV>
-void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
-  if constexpr (KV == 0)
-    hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME, 0>), g, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((hstu_bwd_split_kernel<T, D, WIDE, POS, TIME, KV>), g, dim3(256), 0, s, p);
 }
 
-template <typename T, int D, bool WIDE, int KV>
+template <typename T, int D, bool WIDE, bool POS, bool TIME>
+void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
+  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+}
+
+template <typename T, int D, bool WIDE>
 void launch_rab(const AttnParams& p, dim3 g, hipStream_t s) {
   const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
-  if (pos && time) launch_one<T, D, WIDE, true, true, KV>(p, g, s);
-  else if (pos) launch_one<T, D, WIDE, true, false, KV>(p, g, s);
-  else if (time) launch_one<T, D, WIDE, false, true, KV>(p, g, s);
-  else launch_one<T, D, WIDE, false, false, KV>(p, g, s);
+  if (pos && time) launch_one<T, D, WIDE, true, true>(p, g, s);
+  else if (pos) launch_one<T, D, WIDE, true, false>(p, g, s);
+  else if (time) launch_one<T, D, WIDE, false, true>(p, g, s);
+  else launch_one<T, D, WIDE, false, false>(p, g, s);
 }
 
 }  // namespace
@@ -659,25 +635,17 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   const dim3 g((unsigned)grid);
   prof_before(kKBwd, s);
-  if constexpr (bwd_kv_split((int)sizeof(T), D)) {
-    launch_rab<T, D, false, 1>(p, g, s);
-    launch_rab<T, D, false, 2>(p, g, s);
-  } else {
-    launch_rab<T, D, false, 0>(p, g, s);
-  }
+  launch_rab<T, D, false>(p, g, s);
   // Only a time bias can mark a sequence as needing 64-bit timestamps.
   if (p.rab_time != nullptr) {
     const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
-    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true, 0>(p, gw, s);
-    else launch_one<T, D, true, false, true, 0>(p, gw, s);
+    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true>(p, gw, s);
+    else launch_one<T, D, true, false, true>(p, gw, s);
   }
   prof_after(kKBwd, s);
   return hipGetLastError();
 }
 
-template hipError_t launch_bwd<bf16, 32>(const AttnParams&, hipStream_t);
-template hipError_t launch_bwd<bf16, 64>(const AttnParams&, hipStream_t);
-template hipError_t launch_bwd<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_bwd<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_bwd<float, 64>(const AttnParams&, hipStream_t);
 

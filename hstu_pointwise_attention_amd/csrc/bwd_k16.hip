@@ -41,9 +41,16 @@ struct K16Cfg {
   static constexpr int WIN = BN + BM;
   static constexpr int SCH = BM * CPR;           // staging chunks per tensor per tile
   static constexpr int CH = SCH >= NT ? SCH / NT : 1;   // per staging thread
+  static constexpr int NW = NT / kWave;          // waves
   static constexpr int MAX_TIME = 1024;
+  // Time-gradient histogram: with up to HREP_NT buckets, HREP copies (lane l
+  // adds into copy l % HREP) keep the adds of one instruction from piling
+  // onto one address; larger tables use one copy. Deterministic mode keeps
+  // one copy per wave instead (no two waves add into one address, so the
+  // order of every sum is fixed by the program).
   static constexpr int HREP = 16, HREP_NT = 128, HREP_LD = HREP_NT + 1;
-  static constexpr int THIST = HREP * HREP_LD > MAX_TIME ? HREP * HREP_LD : MAX_TIME;
+  static constexpr int THIST_DET = NW * (MAX_TIME + 1);
+  static constexpr int THIST = HREP * HREP_LD > THIST_DET ? HREP * HREP_LD : THIST_DET;
   static_assert(SCH % NT == 0 || NT % SCH == 0, "staging");
 };
 
@@ -53,7 +60,7 @@ struct K16Smem {
   bf16 qs[C::BM * C::Q_LD];
   bf16 das[C::BM * C::Q_LD];
   float win[C::WIN];
-  float wing[C::WIN];
+  float wing[C::NW * C::WIN];    // position window (one copy per wave in deterministic mode)
   int64_t tsq[C::BM];
   bf16 dsd[C::NDIAG * C::DG_LD];
   int64_t tsk[C::BN];
@@ -126,10 +133,19 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
 
   if constexpr (has_time)
     for (int x = tid; x < p.n_time_buckets; x += C::NT) sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+  // Deterministic mode: every sum has a fixed order (per-wave LDS copies,
+  // partials in the workspace instead of global atomics).
+  const bool det = p.det != 0 && *p.det_on != 0;
+  const int nt_ld = p.n_time_buckets + 1;
   for (int x = tid; x < C::THIST; x += C::NT) sm.thist[x] = 0.f;
   const bool hrep = p.n_time_buckets <= C::HREP_NT;
-  float* const thist_lane = sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
-  for (int x = tid; x < C::WIN; x += C::NT) sm.wing[x] = 0.f;
+  float* const thist_lane = det ? sm.thist + wave * nt_ld : sm.thist + (hrep ? (lane % C::HREP) * C::HREP_LD : 0);
+  float* const thist_wave = det ? sm.thist + wave * nt_ld : sm.thist;
+  for (int x = tid; x < C::NW * C::WIN; x += C::NT) sm.wing[x] = 0.f;
+  float* const wing_w = sm.wing + (det ? wave * C::WIN : 0);
+  float* const part_row =
+      det ? p.part_pos + (p.tile_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kPartW
+          : nullptr;
   if (has_pos)
     for (int x = tid; x < C::NDIAG * C::DG_LD; x += C::NT) sm.dsd[x] = (bf16)0.f;
 
@@ -165,7 +181,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
   bf16* ds_row = nullptr;
   if (p.ds != nullptr && *p.ds_on != 0)
     ds_row = reinterpret_cast<bf16*>(p.ds) +
-             (p.ds_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kDsTile;
+             (p.tile_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kDsTile;
   const int ds_lane = jl * kDsQueries + 8 * q4;
 
   // ---------------------------------------------------------------- staging
@@ -365,7 +381,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
               if constexpr (has_pos && !PD) {
                 if (!pos_diag) {
                   const int i = q0 + 32 * kc + 16 * h + 4 * q4 + r;
-                  atomicAdd(&sm.wing[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
+                  atomicAdd(&wing_w[(C::BN - 1 - jl) + min(i, hist) - p_min], ds);
                 }
               }
               if constexpr (has_time && TM >= 2) {
@@ -413,8 +429,8 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           g_all = wave_sum(g_all);
           if constexpr (TM == 1) g_hi = wave_sum(g_hi);
           if (lane == 0) {
-            atomicAdd(&sm.thist[b_lo], g_all - g_hi);
-            if constexpr (TM == 1) atomicAdd(&sm.thist[b_hi], g_hi);
+            atomicAdd(&thist_wave[b_lo], g_all - g_hi);
+            if constexpr (TM == 1) atomicAdd(&thist_wave[b_hi], g_hi);
           }
         }
       };
@@ -449,25 +465,42 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
         const bf16* row = sm.dsd + dd * C::DG_LD;
 #pragma unroll
         for (int c = 0; c < C::BM / 8; ++c) sum += k16_sum8(ld_frag(row + 8 * c));
-        if (sum != 0.f)
+        if (det)
+          part_row[(int64_t)n * kPartW + dd] = sum;
+        else if (sum != 0.f)
           atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos + pos_bucket(k0 - q0 + (C::BN - 1) - dd, p.max_len), sum);
       }
     } else if (has_pos && tid < C::WIN) {
-      const float gsum = sm.wing[tid];
-      if (gsum != 0.f) {
-        const int p_min = min(q0, hist);
-        atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos + pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len), gsum);
-        sm.wing[tid] = 0.f;
+      if (det) {
+        float gsum = 0.f;
+        for (int w = 0; w < C::NW; ++w) {
+          gsum += sm.wing[w * C::WIN + tid];
+          sm.wing[w * C::WIN + tid] = 0.f;
+        }
+        part_row[(int64_t)n * kPartW + tid] = gsum;
+      } else {
+        const float gsum = sm.wing[tid];
+        if (gsum != 0.f) {
+          const int p_min = min(q0, hist);
+          atomicAdd(p.d_rab_pos + (int64_t)hr * n_pos + pos_bucket(k0 + C::BN - 1 - p_min - tid, p.max_len), gsum);
+          sm.wing[tid] = 0.f;
+        }
       }
     }
   }
 
   if constexpr (has_time) {
     __syncthreads();
+    const int64_t slot = det ? ((int64_t)p.blk_base[wi.seq] + wi.blk) * H + head : 0;
     for (int x = tid; x < p.n_time_buckets; x += C::NT) {
       float gsum = 0.f;
-      for (int c = 0; c < (hrep ? C::HREP : 1); ++c) gsum += sm.thist[c * C::HREP_LD + x];
-      if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
+      if (det) {
+        for (int w = 0; w < C::NW; ++w) gsum += sm.thist[w * nt_ld + x];
+        p.part_time[slot * p.n_time_buckets + x] = gsum;
+      } else {
+        for (int c = 0; c < (hrep ? C::HREP : 1); ++c) gsum += sm.thist[c * C::HREP_LD + x];
+        if (gsum != 0.f) atomicAdd(p.d_rab_time + (int64_t)hr * p.n_time_buckets + x, gsum);
+      }
     }
   }
 

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void dq_ds_kernel(AttnParams p) {
   const int n_kb = n_hist + (qb >= kb_hist ? 1 : 0);
   const int64_t nk = 2 * (int64_t)n_kb;           // stages of 64 keys
   const bf16* const dsb = reinterpret_cast<const bf16*>(p.ds) +
-                          (p.ds_base[wi.seq] + (int64_t)head * ds_seq_tiles(L)) * kDsTile;
+                          (p.tile_base[wi.seq] + (int64_t)head * ds_seq_tiles(L)) * kDsTile;
   const bf16* const kg = reinterpret_cast<const bf16*>(p.k) + start * p.sk + (int64_t)head * D;
 
   const int tid = threadIdx.x;

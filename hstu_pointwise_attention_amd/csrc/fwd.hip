@@ -20,13 +20,6 @@
 // before the elementwise work of the current one so the two overlap.
 #include "internal.h"
 
-#ifndef DQ_WAVES
-#define DQ_WAVES 2
-#endif
-#ifndef DQ_PIPE
-#define DQ_PIPE 0
-#endif
-
 namespace hstu {
 
 namespace {
@@ -329,9 +322,10 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
         const float tb_lo = (TM < 2 && has_time) ? sm.ttab[b_lo] : 0.f;
         const float tb_hi = (TM == 1) ? sm.ttab[b_hi] : 0.f;
         // The next 32-key block's MFMAs are issued before this block's
-        // elementwise work (PIPE) unless the gradient pass runs two waves
-        // per SIMD and lacks the registers.
-        constexpr bool PIPE = !GRAD || DQ_PIPE;
+        // elementwise work (PIPE) unless the gradient pass, which runs two
+        // waves per SIMD, lacks the registers (measured: issuing them early
+        // there spills).
+        constexpr bool PIPE = !GRAD;
         f32x16 sacc[C::KB], pacc[GRAD ? C::KB : 1];
         if constexpr (PIPE) s_block(0, sacc[0], pacc[0]);
 #pragma unroll
@@ -589,7 +583,7 @@ __global__ __launch_bounds__(256) void cand_finish_kernel(AttnParams p) {
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQ_WAVES, DQ_WAVES)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
   if (p.ds_on != nullptr && *p.ds_on != 0) return;   // dQ comes from the exported dS tiles

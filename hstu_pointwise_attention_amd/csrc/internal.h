@@ -54,27 +54,44 @@ struct AttnParams {
   int32_t kv_splits;
   int64_t m_rows;                    // candidate rows (rows of q)
   float* part;
-  // dS export (bf16 backward; ds null: the dQ pass recomputes dS): tile
-  // storage of ds_cap tiles, each (sequence, head)'s tiles from ds_base[b] +
-  // head * ds_seq_tiles(L); the schedule kernel fills ds_base and sets
-  // *ds_on to 1 when the batch's tiles fit, else 0 (the recompute pass runs)
+  // Backward tile numbering: every (sequence, head, key block, 64-query
+  // tile) a key-block workgroup visits has an index, each (sequence, head)'s
+  // tiles from tile_base[b] + head * ds_seq_tiles(L), numbered row by row
+  // (ds_row_start). The schedule kernel fills tile_base (when ds or det is
+  // set) and blk_base (first key block of each sequence, when det is set).
+  int64_t* tile_base;                // [B]
+  int32_t* blk_base;                 // [B + 1]
+  // dS export (bf16 backward; ds null: the dQ pass recomputes dS): storage
+  // of ds_cap tiles; the schedule kernel sets *ds_on to 1 when the batch's
+  // tiles fit, else 0 (the recompute pass runs)
   void* ds;
   int64_t ds_cap;
-  int64_t* ds_base;                  // [B]
   int32_t* ds_on;
+  // Deterministic rab gradients (det != 0): instead of adding into
+  // d_rab_pos / d_rab_time with atomics, each key-block workgroup writes
+  // its sums to part_pos (kPartW floats per tile: the tile's diagonal sums,
+  // or its position-window sums when it holds candidate rows) and part_time
+  // (n_time_buckets floats per (key block, head) slot, slot (blk_base[b] +
+  // key block) * H + head); rab_reduce then sums them in a fixed order. The
+  // schedule kernel sets *det_on to 1 when the batch's tiles fit part_cap,
+  // else 0 (that call falls back to atomics).
+  int32_t det;
+  int32_t n_time_room;               // desc->n_time_buckets: sizes part_time whether
+                                     // or not this call passes a time table
+  float* part_pos;
+  float* part_time;
+  int64_t part_cap;
+  int32_t* det_on;
 };
 
-// Workspace layout: returns total bytes and fills the pointers in p (when
-// base != nullptr).
-size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes);
+// Floats per tile of the position partials (>= the diagonals of a tile and
+// the entries of a position window).
+constexpr int kPartW = 192;
 
-// Shapes whose backward computes dV and dK (with the rab gradients) in two
-// key-block passes instead of one: the one-pass kernel then holds too many
-// registers for two waves per SIMD.
-#ifndef BWD_KVSPLIT
-#define BWD_KVSPLIT 0
-#endif
-constexpr bool bwd_kv_split(int elem_bytes, int D) { return BWD_KVSPLIT && elem_bytes == 2 && D == 128; }
+// Workspace layout: returns total bytes and fills the pointers in p (when
+// base != nullptr). ds_room: the bf16 backward's room for the dS export;
+// p.det: the deterministic rab-gradient partials.
+size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool ds_room);
 
 // Grid of the attention kernels' 64-bit-timestamp instantiations, which walk
 // the work slots of the (rare) sequences that need them.
@@ -83,7 +100,7 @@ constexpr int kWideGrid = 512;
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
   kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
-  kKBucketize, kKFp8Linear, kKFp8Quant, kKDqDs, kNumKernelIds
+  kKBucketize, kKFp8Linear, kKFp8Quant, kKDqDs, kKRabReduce, kNumKernelIds
 };
 // Records a HIP event on `s` before / after a launch when timing is enabled.
 void prof_before(int id, hipStream_t s);
@@ -96,6 +113,9 @@ hipError_t launch_prep(const AttnParams& p, hipStream_t s);
 hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s);
 hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, uint16_t* bp,
                             uint8_t* bt, hipStream_t s);
+// out[b] = unmasked pairs of sequences 0..b-1; out[B] = all of them.
+hipError_t launch_pair_offsets(const int64_t* seq_offsets, const int64_t* num_targets, int B,
+                               int64_t* out, hipStream_t s);
 
 template <typename T, int D> hipError_t launch_fwd(const AttnParams& p, hipStream_t s);
 // Candidate scoring against a cached history (p.cand set): query blocks
@@ -118,21 +138,22 @@ size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base);
 // Splits of the history for a candidate call: enough workgroups to fill the
 // chip, at least 8 history tiles (512 keys) per split on average.
 int cand_kv_splits(int64_t m_rows, int64_t hist_rows, int B, int H);
-// Backward: launch_bwd computes dK, dV and the rab gradients per key block;
+// Backward: launch_bwd (fp32, bwd.hip) and launch_bwd_k16 (bf16,
+// bwd_k16.hip) compute dK, dV and the rab gradients per key block;
 // launch_dq computes dQ per query block (schedule mode 0, like the forward).
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);
-// The same for bf16 with eight waves of 16 keys, two per SIMD
-// (bwd_k16.hip); BWD_K16 = 0 selects launch_bwd<bf16, D> instead.
 template <int D> hipError_t launch_bwd_k16(const AttnParams& p, hipStream_t s);
-#ifndef BWD_K16
-#define BWD_K16 1
-#endif
 template <typename T, int D> hipError_t launch_dq(const AttnParams& p, hipStream_t s);
 // dQ from the exported dS tiles (dq_ds.hip); exits at once unless *p.ds_on.
 template <int D> hipError_t launch_dq_ds(const AttnParams& p, hipStream_t s);
-// Capacity (tiles) of the dS export for a batch of T tokens in B sequences
-// of at most max_len rows each, H heads; 0 when the export is not used.
+// Tiles of a batch of T tokens in B sequences of at most max_len rows each,
+// H heads (an upper bound of the exact count), capped at max_tiles.
+int64_t tile_capacity(int64_t T, int B, int H, int max_len, int64_t max_tiles);
+// Capacity (tiles) of the dS export; 0 when the export is not used.
 int64_t ds_capacity(int64_t T, int B, int H, int max_len);
+// Fixed-order sums of the deterministic rab-gradient partials into
+// d_rab_pos / d_rab_time (exits at once unless *p.det_on).
+hipError_t launch_rab_reduce(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 

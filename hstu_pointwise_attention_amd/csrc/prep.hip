@@ -29,43 +29,6 @@ struct MinOp { __device__ int64_t operator()(int64_t a, int64_t b) const { retur
 struct MaxOp { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
 struct AndOp { __device__ int32_t operator()(int32_t a, int32_t b) const { return a & b; } };
 
-// Smallest / largest timestamp and sortedness of tokens [s, e).
-struct TsStats { int64_t lo, hi; int32_t sorted; };
-
-__device__ TsStats ts_stats(const int64_t* ts, int64_t s, int64_t e, int64_t* lds64, int32_t* lds32) {
-  int64_t lo = INT64_MAX, hi = INT64_MIN;
-  int32_t sorted = 1;
-  // four rounds of loads in flight per step: the loop is latency-bound
-  constexpr int U = 4;
-  for (int64_t t0 = s + threadIdx.x; t0 < e; t0 += U * (int64_t)blockDim.x) {
-    int64_t x[U], y[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + u * (int64_t)blockDim.x;
-      x[u] = t < e ? ts[t] : 0;
-      y[u] = (t < e && t > s) ? ts[t - 1] : INT64_MIN;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (t0 + u * (int64_t)blockDim.x < e) {
-        lo = x[u] < lo ? x[u] : lo;
-        hi = x[u] > hi ? x[u] : hi;
-        if (y[u] > x[u]) sorted = 0;
-      }
-    }
-  }
-  TsStats r;
-  r.lo = block_reduce(lo, lds64, MinOp());
-  r.hi = block_reduce(hi, lds64, MaxOp());
-  r.sorted = block_reduce(sorted, lds32, AndOp());
-  return r;
-}
-
-// A sequence whose timestamp span reaches 2^31 - 1 uses 64-bit bucket math.
-__device__ __forceinline__ bool span_is_wide(int64_t lo, int64_t hi) {
-  return (uint64_t)hi - (uint64_t)lo >= 0x7fffffffull;
-}
-
 // One workgroup per sequence: metadata + rebased timestamps. In the backward
 // the workgroups also clear the rab gradient tables (overwritten outputs).
 __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p) {
@@ -292,9 +255,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     if (mode == 2) p.items_q[hist[blk] + atomicAdd(&fill_q[blk], 1)] = w;
   }
   if (threadIdx.x == 0) *p.n_items = total;
-  if (mode == 2 && p.ds != nullptr) {
-    // dS tile numbering: exclusive scan of H * ds_seq_tiles(L) over the
-    // sequences, each thread a contiguous run of them
+  if (mode == 2 && p.blk_base != nullptr) {
+    for (int b = threadIdx.x; b <= B; b += blockDim.x) p.blk_base[b] = seq_base[b];
+  }
+  if (mode == 2 && p.tile_base != nullptr) {
+    // backward tile numbering: exclusive scan of H * ds_seq_tiles(L) over
+    // the sequences, each thread a contiguous run of them
     __shared__ int64_t run[kSchedThreads];
     const int per = (B + kSchedThreads - 1) / kSchedThreads;
     const int b0 = threadIdx.x * per, b1 = b0 + per < B ? b0 + per : B;
@@ -310,52 +276,150 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     }
     int64_t at = threadIdx.x > 0 ? run[threadIdx.x - 1] : 0;
     for (int b = b0; b < b1; ++b) {
-      p.ds_base[b] = at;
+      p.tile_base[b] = at;
       at += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
     }
-    if (threadIdx.x == kSchedThreads - 1) *p.ds_on = run[kSchedThreads - 1] <= p.ds_cap ? 1 : 0;
+    if (threadIdx.x == kSchedThreads - 1) {
+      const int64_t tiles = run[kSchedThreads - 1];
+      if (p.ds_on) *p.ds_on = tiles <= p.ds_cap ? 1 : 0;
+      if (p.det_on) *p.det_on = tiles <= p.part_cap ? 1 : 0;
+    }
   }
 }
 
-// rab bucket export: grid (64 row groups, B sequences).
-__global__ __launch_bounds__(kPrepThreads) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
-                                                                  uint16_t* bp, uint8_t* bt) {
-  __shared__ int64_t lds64[kPrepThreads / kWave];
-  __shared__ int32_t lds32[kPrepThreads / kWave];
-  const int b = blockIdx.y;
-  const int64_t s = p.seq_offsets[b];
-  const int64_t e = p.seq_offsets[b + 1];
-  const int L = (int)(e - s);
-  int nt = p.num_targets ? (int)p.num_targets[b] : 0;
+// rab bucket export, laid out over the jagged lower triangle: sequence
+// after sequence, query row i, then key j ascending (history rows i < hist
+// see keys 0..i, candidate rows see the history and themselves). Thread g of
+// the grid writes export slots 8g .. 8g + 7, so a wave stores 1 KB of bp and
+// 512 bytes of bt contiguously (16- and 8-byte stores). Time buckets use
+// 64-bit timestamp arithmetic, exact for any int64 pair.
+constexpr int kBktPer = 8;
+constexpr int kBktThreads = 256;
+constexpr int kBktGrid = 4096;
+
+__device__ __forceinline__ int64_t pairs_of(int L, int hist) {
+  return (int64_t)hist * (hist + 1) / 2 + (int64_t)(L - hist) * (hist + 1);
+}
+
+__device__ __forceinline__ void seq_rows(const int64_t* seq_offsets, const int64_t* num_targets, int b,
+                                         int64_t& s, int& L, int& hist) {
+  s = seq_offsets[b];
+  L = (int)(seq_offsets[b + 1] - s);
+  int nt = num_targets ? (int)num_targets[b] : 0;
   nt = nt < 0 ? 0 : (nt > L ? L : nt);
-  const int hist = L - nt;
-  bool wide = false;
-  int64_t lo = 0;
+  hist = L - nt;
+}
+
+__global__ __launch_bounds__(kBktThreads) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
+                                                                uint16_t* bp, uint8_t* bt) {
+  const int64_t total = pair_offsets[p.B];
   const bool want_t = bt != nullptr;
-  if (want_t && L > 0) {
-    TsStats st = ts_stats(p.timestamps, s, e, lds64, lds32);
-    lo = st.lo;
-    wide = span_is_wide(st.lo, st.hi);
-  }
   const int last = p.n_time_buckets - 1;
-  const int64_t base = pair_offsets[b];
-  const int64_t hist_pairs = (int64_t)hist * (hist + 1) / 2;
-  for (int i = blockIdx.x; i < L; i += gridDim.x) {
-    const int64_t row = i < hist ? (int64_t)i * (i + 1) / 2
-                                 : hist_pairs + (int64_t)(i - hist) * (hist + 1);
-    const int n = i < hist ? i + 1 : hist + 1;
-    const int pi = i < hist ? i : hist;
-    for (int c = threadIdx.x; c < n; c += blockDim.x) {
-      const int j = (i < hist || c < hist) ? c : i;
-      const int64_t o = base + row + c;
-      if (bp) bp[o] = (uint16_t)pos_bucket(j - pi, p.max_len);
+  const bool vec = ((uintptr_t)bp % 16 == 0) && ((uintptr_t)bt % 8 == 0);
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g * kBktPer < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t o0 = g * kBktPer;
+    // the sequence holding slot o0: the last b with pair_offsets[b] <= o0
+    int lo = 0, hi = p.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pair_offsets[mid] <= o0) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    int64_t s;
+    int L, hist;
+    seq_rows(p.seq_offsets, p.num_targets, b, s, L, hist);
+    // row i and position c within the row of slot o0
+    int64_t o = o0 - pair_offsets[b];
+    const int64_t hp = (int64_t)hist * (hist + 1) / 2;
+    int i, c;
+    if (o < hp) {
+      int64_t r = (int64_t)((sqrt(8.0 * (double)o + 1.0) - 1.0) * 0.5);
+      while (r * (r + 1) / 2 > o) --r;
+      while ((r + 1) * (r + 2) / 2 <= o) ++r;
+      i = (int)r;
+      c = (int)(o - r * (r + 1) / 2);
+    } else {
+      const int64_t q = o - hp;
+      i = hist + (int)(q / (hist + 1));
+      c = (int)(q % (hist + 1));
+    }
+    int64_t ti = want_t ? p.timestamps[s + i] : 0;
+    uint16_t vp[kBktPer];
+    uint8_t vt[kBktPer];
+    const int n = total - o0 < kBktPer ? (int)(total - o0) : kBktPer;
+#pragma unroll
+    for (int m = 0; m < kBktPer; ++m) {
+      vp[m] = 0;
+      vt[m] = 0;
+      if (m < n) {
+        const int j = (i < hist || c < hist) ? c : i;
+        vp[m] = (uint16_t)pos_bucket(j - (i < hist ? i : hist), p.max_len);
+        if (want_t) vt[m] = (uint8_t)time_bucket_wide(ti, p.timestamps[s + j], last);
+        // next slot: the next key of the row, else the next row, else the
+        // first row of the next non-empty sequence
+        if (++c >= (i < hist ? i + 1 : hist + 1)) {
+          c = 0;
+          if (++i >= L && m + 1 < n) {
+            do { ++b; } while (p.seq_offsets[b + 1] == p.seq_offsets[b]);
+            seq_rows(p.seq_offsets, p.num_targets, b, s, L, hist);
+            i = 0;
+          }
+          if (want_t && m + 1 < n) ti = p.timestamps[s + i];
+        }
+      }
+    }
+    if (vec && n == kBktPer) {
+      if (bp) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (uint32_t)vp[2 * q] | ((uint32_t)vp[2 * q + 1] << 16);
+        st16(bp + o0, w);
+      }
       if (want_t) {
-        const int64_t ti = p.timestamps[s + i], tj = p.timestamps[s + j];
-        bt[o] = (uint8_t)(wide ? time_bucket_wide(ti, tj, last)
-                               : time_bucket_rel((uint32_t)(ti - lo), (uint32_t)(tj - lo), last));
+        uint2 w;
+        w.x = (uint32_t)vt[0] | ((uint32_t)vt[1] << 8) | ((uint32_t)vt[2] << 16) | ((uint32_t)vt[3] << 24);
+        w.y = (uint32_t)vt[4] | ((uint32_t)vt[5] << 8) | ((uint32_t)vt[6] << 16) | ((uint32_t)vt[7] << 24);
+        *reinterpret_cast<uint2*>(bt + o0) = w;
+      }
+    } else {
+      for (int m = 0; m < n; ++m) {
+        if (bp) bp[o0 + m] = vp[m];
+        if (want_t) bt[o0 + m] = vt[m];
       }
     }
   }
+}
+
+// pair_offsets[b] = unmasked pairs of sequences 0..b-1, pair_offsets[B] = all
+// of them (one workgroup, chunks of blockDim.x sequences with a running carry).
+__global__ __launch_bounds__(kSchedThreads) void pair_offsets_kernel(const int64_t* seq_offsets,
+                                                                     const int64_t* num_targets, int B,
+                                                                     int64_t* out) {
+  __shared__ int64_t lds[kSchedThreads];
+  int64_t carry = 0;
+  for (int base = 0; base < B; base += blockDim.x) {
+    const int idx = base + threadIdx.x;
+    int64_t v = 0;
+    if (idx < B) {
+      int64_t s;
+      int L, hist;
+      seq_rows(seq_offsets, num_targets, idx, s, L, hist);
+      v = pairs_of(L, hist);
+    }
+    lds[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+      const int64_t add = threadIdx.x >= (unsigned)off ? lds[threadIdx.x - off] : 0;
+      __syncthreads();
+      lds[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (idx < B) out[idx] = carry + lds[threadIdx.x] - v;
+    carry += lds[blockDim.x - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[B] = carry;
 }
 
 __global__ void fill_f32_kernel(float* x, int64_t n, float value) {
@@ -441,7 +505,7 @@ int grid_for(int64_t n, int threads) {
 
 }  // namespace
 
-size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
+size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool ds_room) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -457,18 +521,35 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 4 * NB));
   p.items_q = nullptr;
   p.d_a = nullptr;
+  p.tile_base = nullptr;
+  p.blk_base = nullptr;
   p.ds = nullptr;
   p.ds_cap = 0;
-  p.ds_base = nullptr;
   p.ds_on = nullptr;
+  p.part_pos = nullptr;
+  p.part_time = nullptr;
+  p.part_cap = 0;
+  p.det_on = nullptr;
   if (bwd) {
     p.items_q = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
     p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
-    const int64_t cap = (elem_bytes == 2 && BWD_K16) ? ds_capacity(p.T, p.B, p.H, p.max_len) : 0;
+    const int64_t cap = (elem_bytes == 2 && ds_room) ? ds_capacity(p.T, p.B, p.H, p.max_len) : 0;
+    const bool det = p.det != 0 && p.T > 0 && p.B > 0;
+    if (cap > 0 || det) {
+      p.tile_base = (int64_t*)take(sizeof(int64_t) * (size_t)p.B);
+      int32_t* flags = (int32_t*)take(2 * sizeof(int32_t));
+      p.ds_on = cap > 0 ? flags : nullptr;
+      p.det_on = det ? flags + 1 : nullptr;
+    }
+    if (det) {
+      p.blk_base = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1));
+      p.part_cap = tile_capacity(p.T, p.B, p.H, p.max_len, ((int64_t)2 << 30) / (kPartW * 4));
+      p.part_pos = (float*)take(sizeof(float) * kPartW * (size_t)p.part_cap);
+      const int64_t slots = (p.T / kBlk + p.B) * (int64_t)p.H;
+      p.part_time = (float*)take(sizeof(float) * (size_t)slots * (size_t)(p.n_time_room > 0 ? p.n_time_room : 1));
+    }
     if (cap > 0) {
       p.ds_cap = cap;
-      p.ds_base = (int64_t*)take(sizeof(int64_t) * (size_t)p.B);
-      p.ds_on = (int32_t*)take(sizeof(int32_t));
       p.ds = take((size_t)cap * kDsTile * 2);
     }
   }
@@ -481,18 +562,22 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes) {
 // (ceil(max_len / 128) + 1) (T / 128 + B) per head. The exact count is
 // checked on the device, and a batch beyond the capacity (longer sequences
 // than max_len, or beyond the 4 GiB cap) takes the recompute pass.
-int64_t ds_capacity(int64_t T, int B, int H, int max_len) {
+int64_t tile_capacity(int64_t T, int B, int H, int max_len, int64_t max_tiles) {
   if (T <= 0 || B <= 0) return 0;
-  const int64_t nkb = (max_len + kDsKeys - 1) / kDsKeys;
-  int64_t cap = (int64_t)H * (nkb + 1) * (T / kDsKeys + B);
-  const int64_t max_tiles = ((int64_t)4 << 30) / (kDsTile * 2);
+  const int64_t len = max_len < T ? max_len : T;          // no sequence is longer than T
+  const int64_t nkb = (len + kDsKeys - 1) / kDsKeys;
+  const int64_t cap = (int64_t)H * (nkb + 1) * (T / kDsKeys + B);
   return cap < max_tiles ? cap : max_tiles;
+}
+
+int64_t ds_capacity(int64_t T, int B, int H, int max_len) {
+  return tile_capacity(T, B, H, max_len, ((int64_t)4 << 30) / (kDsTile * 2));
 }
 
 // The forward's carve-up for the joined row count p.T, plus the per-sequence
 // candidate records and, with a time bias, the joined 64-bit timestamps.
 size_t carve_workspace_cand(AttnParams& p, CandArgs& c, void* base) {
-  size_t off = carve_workspace(p, base, false, 2);
+  size_t off = carve_workspace(p, base, false, 2, false);
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += (bytes + 255) & ~(size_t)255;
@@ -543,9 +628,16 @@ hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, ui
                             uint8_t* bt, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   prof_before(kKBucketize, s);
-  hipLaunchKernelGGL(bucketize_kernel, dim3(64, p.B), dim3(kPrepThreads), 0, s, p, pair_offsets,
+  hipLaunchKernelGGL(bucketize_kernel, dim3(kBktGrid), dim3(kBktThreads), 0, s, p, pair_offsets,
                      bp, bt);
   prof_after(kKBucketize, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_offsets(const int64_t* seq_offsets, const int64_t* num_targets, int B,
+                               int64_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(pair_offsets_kernel, dim3(1), dim3(kSchedThreads), 0, s, seq_offsets,
+                     num_targets, B, out);
   return hipGetLastError();
 }
 

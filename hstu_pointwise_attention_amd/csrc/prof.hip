@@ -36,7 +36,8 @@ hipEvent_t take_event() {
 
 const char* const kNames[kNumKernelIds] = {"prep", "schedule", "fwd", "bwd_pre", "bwd",
                                            "dq", "fill", "linear", "layernorm_gate",
-                                           "bucketize", "fp8_linear", "fp8_quantize", "dq_ds"};
+                                           "bucketize", "fp8_linear", "fp8_quantize", "dq_ds",
+                                           "rab_reduce"};
 
 }  // namespace
 

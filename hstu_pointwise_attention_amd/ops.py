@@ -135,13 +135,21 @@ def attn_fwd_cached(q, k, v, u, cand_offsets, cand_first, n_cands, k_hist, v_his
 
 
 def attn_bwd(q, k, v, u, seq_offsets, max_len, a_saved, d_o, *, num_targets=None,
-             timestamps=None, rab_pos=None, rab_time=None):
-    """Returns dict dq, dk, dv, du (None without gate), d_rab_pos, d_rab_time."""
+             timestamps=None, rab_pos=None, rab_time=None, deterministic: bool = False,
+             ds_room: bool = True, report: bool = False):
+    """Returns dict dq, dk, dv, du (None without gate), d_rab_pos, d_rab_time.
+
+    deterministic: sum the rab gradients in a fixed order (desc.deterministic).
+    ds_room: give the workspace the dS-export room (the preferred size) or
+    only the minimum (dQ then recomputes dS). report: also return, under
+    "info", what hstu_attn_bwd_report says the call did (waits for the stream).
+    """
     lib = _lib.load()
     seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
     rab_pos, rab_time = _f32c(rab_pos), _f32c(rab_time)
     nt, hr = _rab_meta(rab_pos, rab_time)
     desc = make_desc(q, k, v, u, seq_offsets, max_len, nt, hr)
+    desc.deterministic = 1 if deterministic else 0
     d_o = d_o.contiguous()
     T, H, D = q.shape
     Dv = v.shape[2]
@@ -152,25 +160,22 @@ def attn_bwd(q, k, v, u, seq_offsets, max_len, a_saved, d_o, *, num_targets=None
     drp = torch.empty_like(rab_pos) if rab_pos is not None else None
     drt = torch.empty_like(rab_time) if rab_time is not None else None
     nbytes = ctypes.c_size_t()
-    _lib.check(lib.hstu_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    size_fn = lib.hstu_attn_bwd_workspace_size if ds_room else lib.hstu_attn_bwd_workspace_size_min
+    _lib.check(size_fn(ctypes.byref(desc), ctypes.byref(nbytes)))
     ws = torch.empty(max(nbytes.value, 1), dtype=torch.uint8, device=q.device)
     _lib.check(lib.hstu_attn_bwd(ctypes.byref(desc), _ptr(seq_offsets), _ptr(num_targets),
                                  _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(u), _ptr(a_saved), _ptr(d_o), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(du), _ptr(drp), _ptr(drt), _ptr(ws), nbytes.value,
                                  _stream()))
-    return dict(dq=dq, dk=dk, dv=dv, du=du, d_rab_pos=drp, d_rab_time=drt)
-
-
-def pair_offsets_host(lengths, num_targets=None) -> list:
-    """First output slot of each sequence in the bucket export (host arithmetic)."""
-    offs = [0]
-    for b, L in enumerate(lengths):
-        L = int(L)
-        nt = 0 if num_targets is None else min(max(int(num_targets[b]), 0), L)
-        hist = L - nt
-        offs.append(offs[-1] + hist * (hist + 1) // 2 + (L - hist) * (hist + 1))
-    return offs
+    out = dict(dq=dq, dk=dk, dv=dv, du=du, d_rab_pos=drp, d_rab_time=drt)
+    if report:
+        info = _lib.BwdInfo()
+        _lib.check(lib.hstu_attn_bwd_report(ctypes.byref(desc), _ptr(ws), nbytes.value,
+                                            ctypes.byref(info), _stream()))
+        out["info"] = {"dq_from_ds": bool(info.dq_from_ds),
+                       "rab_deterministic": bool(info.rab_deterministic)}
+    return out
 
 
 def rab_bucketize(seq_offsets, max_len, *, num_targets=None, timestamps=None,
@@ -179,18 +184,17 @@ def rab_bucketize(seq_offsets, max_len, *, num_targets=None, timestamps=None,
     lib = _lib.load()
     dev = seq_offsets.device
     seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
-    lengths = (seq_offsets[1:] - seq_offsets[:-1]).cpu().tolist()
-    nts = num_targets.cpu().tolist() if num_targets is not None else None
-    offs = pair_offsets_host(lengths, nts)
-    n = offs[-1]
-    po = torch.tensor(offs, dtype=torch.int64, device=dev)
-    bp = torch.empty(max(n, 1), dtype=torch.int16, device=dev) if want_pos else None
-    bt = torch.empty(max(n, 1), dtype=torch.uint8, device=dev) if timestamps is not None else None
     d = _lib.AttnDesc()
-    d.batch = len(lengths)
+    d.batch = seq_offsets.numel() - 1
     d.heads = 1
     d.max_len = int(max_len)
     d.n_time_buckets = int(n_time_buckets)
+    po = torch.empty(d.batch + 1, dtype=torch.int64, device=dev)
+    _lib.check(lib.hstu_rab_pair_offsets(ctypes.byref(d), _ptr(seq_offsets), _ptr(num_targets),
+                                         _ptr(po), _stream()))
+    n = int(po[-1])                       # the output size (waits for the stream)
+    bp = torch.empty(max(n, 1), dtype=torch.int16, device=dev) if want_pos else None
+    bt = torch.empty(max(n, 1), dtype=torch.uint8, device=dev) if timestamps is not None else None
     _lib.check(lib.hstu_rab_bucketize(ctypes.byref(d), _ptr(seq_offsets), _ptr(num_targets),
                                       _ptr(timestamps), _ptr(po), _ptr(bp), _ptr(bt), _stream()))
     bp = bp[:n].to(torch.int32) & 0xFFFF if bp is not None else None

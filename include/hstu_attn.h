@@ -29,8 +29,10 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream). Nothing synchronises with the host.
  *  - The caller allocates and owns every buffer, including the workspace;
- *    the library allocates nothing and keeps no state between calls, so calls
- *    are reentrant. Calls that share a workspace must not overlap.
+ *    the library allocates nothing and keeps no state between calls (apart
+ *    from the optional per-launch timing of hstu_profile_begin/end, off by
+ *    default), so calls are reentrant. Calls that share a workspace must not
+ *    overlap.
  *  - Every call validates its host-side arguments before it launches
  *    anything; on any error it returns a negative status without writing any
  *    output and hstu_last_error() describes the problem. Device-side data
@@ -81,20 +83,34 @@ typedef struct {
   int32_t dtype;           /* hstu_dtype of Q,K,V,U,O,dO,dQ,dK,dV,dU             */
   int64_t total_tokens;    /* T = seq_offsets[B], 0 <= T < 2^31                  */
   int64_t stride_q, stride_k, stride_v, stride_u;  /* elements between tokens   */
+  int32_t deterministic;   /* 0 or 1; backward only: 1 sums the rab gradients in
+                              a fixed order (bitwise repeatable, see hstu_attn_bwd) */
 } hstu_attn_desc;
 
 /*
  * Bytes of workspace hstu_attn_fwd / hstu_attn_bwd need for this shape.
- * For bf16, the backward's figure includes room for the dS tiles it hands
- * from the key-block pass to the dQ pass: 16 KB per (128-key block, 64-query
- * tile) pair, sized for sequences no longer than max_len,
- * heads * (ceil(max_len / 128) + 1) * (total_tokens / 128 + batch) tiles,
- * capped at 4 GiB (about 1.5 GB for 8 sequences of up to 8192 rows, 4 heads).
- * A batch whose tiles do not fit computes dQ by recomputing dS instead, with
- * the same results.
+ *
+ * The backward has two figures. hstu_attn_bwd_workspace_size_min is the
+ * least it accepts: O(T * H * D) bytes (the dA' tensor, per-sequence
+ * metadata and work lists), plus, when desc->deterministic is set, the
+ * rab-gradient partials (768 bytes per (128-key block, 64-query tile) pair
+ * and one row of n_time_buckets floats per (128-key block, head), sized like
+ * the tiles below, at most 2 GiB).
+ * hstu_attn_bwd_workspace_size is the preferred figure: for bf16 it adds
+ * room for the dS tiles the key-block pass hands to the dQ pass, 16 KB per
+ * (128-key block, 64-query tile) pair, sized for sequences no longer than
+ * max_len: heads * (ceil(min(max_len, T) / 128) + 1) * (T / 128 + batch)
+ * tiles, at most 4 GiB (about 1.5 GB for 8 sequences of up to 8192 rows, 4
+ * heads). That room is O(sum of L^2) bytes.
+ * hstu_attn_bwd uses the dS export when workspace_bytes reaches the preferred
+ * figure and the batch's tiles fit; otherwise it computes dQ by recomputing dS
+ * per query block (the same results; measured about 1.7x the dQ time at 8
+ * sequences of 4096..8192 rows, 4 heads, head dim 128).
+ * hstu_attn_bwd_report tells which ran.
  */
 HSTU_API hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
 HSTU_API hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
+HSTU_API hstu_status hstu_attn_bwd_workspace_size_min(const hstu_attn_desc* desc, size_t* bytes);
 
 /*
  * Forward.
@@ -181,8 +197,16 @@ HSTU_API hstu_status hstu_attn_fwd_cached(const hstu_attn_desc* desc, const int6
  *  du           dtype [T, H, d_v]; required iff u != NULL
  *  d_rab_pos    fp32 [rab_heads, 2*max_len-1]; required iff rab_pos != NULL
  *  d_rab_time   fp32 [rab_heads, n_time_buckets]; required iff rab_time != NULL
- * dQ and the rab gradients are summed with floating-point atomics, so their
- * last bits may differ between runs.
+ *  workspace    (device) >= hstu_attn_bwd_workspace_size_min bytes, 256-aligned
+ * Reductions. dQ, dK, dV and dU are each written once by one workgroup, in a
+ * fixed order of summation: they repeat bit for bit between runs. The rab
+ * gradients are sums over many workgroups: with desc->deterministic = 0 each
+ * workgroup adds its partial sums with floating-point atomics, so their last
+ * bits may differ between runs; with desc->deterministic = 1 the partial
+ * sums go to the workspace and one more kernel adds them in a fixed order,
+ * so they repeat bit for bit (a batch whose tiles exceed the partials' room,
+ * i.e. with sequences longer than max_len, falls back to the atomics;
+ * hstu_attn_bwd_report tells).
  */
 HSTU_API hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets,
                           const int64_t* num_targets, const int64_t* timestamps,
@@ -194,15 +218,40 @@ HSTU_API hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* se
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * What the last hstu_attn_bwd on this workspace did (for checking and
+ * reporting; it waits for `stream`, then reads two flags the call left in the
+ * workspace). desc, workspace and workspace_bytes as passed to that call.
+ *  dq_from_ds         1: dQ came from the exported dS tiles; 0: dQ came
+ *                     from the pass that recomputes dS (no room, or fp32)
+ *  rab_deterministic  1: the rab gradients were summed in a fixed order
+ */
+typedef struct {
+  int32_t dq_from_ds;
+  int32_t rab_deterministic;
+} hstu_attn_bwd_info;
+HSTU_API hstu_status hstu_attn_bwd_report(const hstu_attn_desc* desc, const void* workspace,
+                                          size_t workspace_bytes, hstu_attn_bwd_info* info,
+                                          void* stream);
+
+/*
  * rab bucket export (for checking and debugging): for every unmasked pair,
  * in sequence order, then query row i, then key j ascending, writes the
- * position bucket bp(i,j) and the time bucket bt(i,j).
- *  pair_offsets (device) int64 [B+1]: first output slot of each sequence;
- *               sequence b has hist*(hist+1)/2 + (L-hist)*(hist+1) pairs
+ * position bucket bp(i,j) and the time bucket bt(i,j) (the bucket
+ * definitions at the top of this file, which the attention kernels apply to
+ * each pair inside their tiles).
+ *  pair_offsets (device) int64 [B+1]: first output slot of each sequence, as
+ *               written by hstu_rab_pair_offsets; pair_offsets[B] = pairs
  *  bp_out       (device) uint16 [pairs] or NULL (requires max_len <= 32768)
  *  bt_out       (device) uint8 [pairs] or NULL (requires timestamps and
- *               n_time_buckets >= 1)
+ *               1 <= n_time_buckets <= 256)
+ * hstu_rab_pair_offsets writes pair_offsets (device, int64 [B+1]) from the
+ * same seq_offsets / num_targets: sequence b has hist*(hist+1)/2 +
+ * (L-hist)*(hist+1) unmasked pairs (hist = L - num_targets[b]). Only
+ * desc->batch is read. A caller sizing bp_out / bt_out reads pair_offsets[B].
  */
+HSTU_API hstu_status hstu_rab_pair_offsets(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                                           const int64_t* num_targets, int64_t* pair_offsets,
+                                           void* stream);
 HSTU_API hstu_status hstu_rab_bucketize(const hstu_attn_desc* desc, const int64_t* seq_offsets,
                                const int64_t* num_targets, const int64_t* timestamps,
                                const int64_t* pair_offsets, uint16_t* bp_out,

@@ -9,9 +9,14 @@ The same definition as ``oracle/attention.py`` (written out in
   rows. Without candidates, and with every sequence no longer than
   max_len, such a diagonal is exactly the set of pairs that read position
   bucket delta + max_len - 1, so the sum is that entry of d_rab_pos (summed
-  over heads when one table is shared).
+  over heads when one table is shared);
+* the whole rab-table gradients (``rab_gradients``): dS over every unmasked
+  pair, added into the bucket each pair reads, without forming dQ, dK or dV.
 
-Each item costs O(L * D) in float64, so 8192-long sequences are cheap.
+Each sampled item costs O(L * D) in float64, so 8192-long sequences are
+cheap; the rab gradients cost the pairs' S and dP (two matrix products per
+block of rows) and may spread the (sequence, head) units over worker
+processes, whose per-unit tables are added in unit order.
 Pins: the scalar brute force of ``oracle/scalar.py`` on tiny inputs with
 candidates and both rab tables (``tests/test_oracle_sampled.py``).
 """
@@ -139,3 +144,82 @@ def diagonal_ds_sums(q, k, v, u, seq_offsets, max_len, d_o, deltas, timestamps=N
                 dP = np.einsum("md,md->m", dA[s + rows, h, :], v[s + cols, h, :])
                 out[h, n] += float(np.sum(dP * sg * (1.0 + S * (1.0 - sg)))) / L
     return out.sum(axis=0) if shared else out
+
+
+def _one_blas_thread():
+    """Worker processes use one BLAS thread each (the processes are the parallelism)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _rab_unit(args):
+    """d_rab_pos / d_rab_time contributions of one (sequence, head)."""
+    (q, k, v, dA, s, L, hist, max_len, ts, rab_pos_row, rab_time_row, n_pos, n_time, rows_per) = args
+    gp = np.zeros(n_pos) if rab_pos_row is not None else None
+    gt = np.zeros(n_time) if rab_time_row is not None else None
+    for r0 in range(0, L, rows_per):
+        rows = np.arange(r0, min(L, r0 + rows_per))
+        cols = np.arange(rows[-1] + 1)                 # every unmasked pair has j <= i
+        S = q[rows] @ k[cols].T
+        bp = position_buckets(rows, cols, hist, max_len) if gp is not None else None
+        bt = time_buckets(ts[rows], ts[cols], n_time) if gt is not None else None
+        if bp is not None:
+            S = S + rab_pos_row[bp]
+        if bt is not None:
+            S = S + rab_time_row[bt]
+        m = ((cols[None, :] <= rows[:, None]) & (cols[None, :] < hist)) | (cols[None, :] == rows[:, None])
+        sg = _sigmoid(S)
+        dP = dA[rows] @ v[cols].T
+        dS = np.where(m, dP * sg * (1.0 + S * (1.0 - sg)), 0.0) / L
+        if gp is not None:
+            gp += np.bincount(bp[m], weights=dS[m], minlength=n_pos)
+        if gt is not None:
+            gt += np.bincount(bt[m], weights=dS[m], minlength=n_time)
+    return gp, gt
+
+
+def rab_gradients(q, k, v, u, seq_offsets, max_len, d_o, num_targets=None, timestamps=None,
+                  rab_pos=None, rab_time=None, workers: int = 1, rows_per: int = 256):
+    """The rab-table gradients of the backward: ``(d_rab_pos or None, d_rab_time or None)``.
+
+    Entry p of a table is the sum of dS_ij over the unmasked pairs (b, h, i, j)
+    whose bucket is p, over the heads that read that table row. The (sequence,
+    head) units run in ``workers`` processes (1: in this one); their tables
+    are added in unit order.
+    """
+    q, k, v, u, d_o, dA, rab_pos, rab_time = _prep(q, k, v, u, d_o, rab_pos, rab_time)
+    H = q.shape[1]
+    tab = rab_pos if rab_pos is not None else rab_time
+    Hr = 1 if tab is None else tab.shape[0]
+    n_pos = 2 * max_len - 1
+    n_time = rab_time.shape[1] if rab_time is not None else 0
+    units, dest = [], []
+    for b in range(len(seq_offsets) - 1):
+        s, e, L, hist = _seq_meta(seq_offsets, num_targets, b)
+        if L == 0:
+            continue
+        ts = None if timestamps is None else np.asarray(timestamps[s:e], dtype=np.int64)
+        for h in range(H):
+            hr = _rab_head(h, rab_pos, rab_time)
+            units.append((np.ascontiguousarray(q[s:e, h]), np.ascontiguousarray(k[s:e, h]),
+                          np.ascontiguousarray(v[s:e, h]), np.ascontiguousarray(dA[s:e, h]), s, L,
+                          hist, max_len, ts, None if rab_pos is None else rab_pos[hr],
+                          None if rab_time is None else rab_time[hr], n_pos, n_time, rows_per))
+            dest.append(hr)
+    if workers > 1 and len(units) > 1:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(min(workers, len(units)), initializer=_one_blas_thread) as pool:
+            parts = pool.map(_rab_unit, units, chunksize=1)
+    else:
+        parts = [_rab_unit(a) for a in units]
+    gp = np.zeros((Hr, n_pos)) if rab_pos is not None else None
+    gt = np.zeros((Hr, n_time)) if rab_time is not None else None
+    for hr, (a, c) in zip(dest, parts):
+        if gp is not None:
+            gp[hr] += a
+        if gt is not None:
+            gt[hr] += c
+    return gp, gt

@@ -63,13 +63,14 @@ def gpu_fwd(inp, dev=None):
                         rab_pos=dev["rab_pos"], rab_time=dev["rab_time"], save_a=True)
 
 
-def gpu_bwd(inp, a, dev=None):
+def gpu_bwd(inp, a, dev=None, **kw):
+    """kw: deterministic, ds_room, report (ops.attn_bwd)."""
     from hstu_pointwise_attention_amd import ops
     dev = dev or to_dev(inp)
     return ops.attn_bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["seq_offsets"], inp["max_len"],
                         a if dev["u"] is not None else None, dev["d_o"],
                         num_targets=dev["num_targets"], timestamps=dev["timestamps"],
-                        rab_pos=dev["rab_pos"], rab_time=dev["rab_time"])
+                        rab_pos=dev["rab_pos"], rab_time=dev["rab_time"], **kw)
 
 
 def check_fwd(inp, O, A, want_O, want_A, tag=""):

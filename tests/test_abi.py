@@ -8,7 +8,6 @@ import pytest
 
 from hstu_pointwise_attention_amd import _lib
 from hstu_pointwise_attention_amd.flops import unmasked_pairs_host, attention_flops
-from hstu_pointwise_attention_amd.ops import pair_offsets_host
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hstu_attn.h")
@@ -64,6 +63,7 @@ def fwd_call(lib, d, ws_bytes=1 << 30, rab_time=FAKE, timestamps=FAKE, ws=ctypes
     ("total_tokens", 1 << 31, _lib.HSTU_EINVAL),
     ("stride_q", 64, _lib.HSTU_EINVAL),
     ("stride_k", 130, _lib.HSTU_EINVAL),
+    ("deterministic", 2, _lib.HSTU_EINVAL),
 ])
 def test_desc_validation(lib, field, value, status):
     d = good_desc(**{field: value})
@@ -102,6 +102,50 @@ def test_workspace_checks(lib):
     assert lib.hstu_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(bneed)) == 0
     assert bneed.value >= need.value + 50 * 128 * 2        # holds dA' = dO*U/L (bf16 [T, H, D])
     assert lib.hstu_attn_fwd_workspace_size(ctypes.byref(d), None) == _lib.HSTU_EINVAL
+
+
+def _bwd_sizes(lib, d):
+    pref, least = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.hstu_attn_bwd_workspace_size(ctypes.byref(d), ctypes.byref(pref)) == 0
+    assert lib.hstu_attn_bwd_workspace_size_min(ctypes.byref(d), ctypes.byref(least)) == 0
+    return pref.value, least.value
+
+
+def test_bwd_workspace_min_and_preferred(lib):
+    # bf16: the preferred size adds the dS-tile room (at least one 16 KB tile)
+    pref, least = _bwd_sizes(lib, good_desc())
+    assert pref >= least + 16384
+    # fp32 recomputes dS for dQ: both figures agree
+    d32 = good_desc(dtype=_lib.DTYPE_FP32, stride_q=128, stride_k=128, stride_v=128, stride_u=128)
+    pref32, least32 = _bwd_sizes(lib, d32)
+    assert pref32 == least32
+    # the deterministic mode adds its partials to both figures
+    pref_d, least_d = _bwd_sizes(lib, good_desc(deterministic=1))
+    # (the per-sequence tile numbering is carved once for both)
+    assert least_d > least and 16384 <= pref_d - least_d <= pref - least
+    # below the minimum: rejected before any launch
+    st = lib.hstu_attn_bwd(ctypes.byref(good_desc()), FAKE, None, FAKE, None, FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                           ctypes.c_void_p(1 << 20), least - 1, None)
+    assert st == _lib.HSTU_EWORKSPACE
+
+
+def test_bwd_report_validation(lib):
+    d = good_desc()
+    pref, least = _bwd_sizes(lib, d)
+    info = _lib.BwdInfo()
+    assert lib.hstu_attn_bwd_report(ctypes.byref(d), ctypes.c_void_p(1 << 20), pref, None,
+                                    None) == _lib.HSTU_EINVAL
+    assert lib.hstu_attn_bwd_report(ctypes.byref(d), ctypes.c_void_p(1 << 20), least - 1,
+                                    ctypes.byref(info), None) == _lib.HSTU_EWORKSPACE
+    assert lib.hstu_attn_bwd_report(ctypes.byref(good_desc(heads=0)), ctypes.c_void_p(1 << 20),
+                                    pref, ctypes.byref(info), None) == _lib.HSTU_EINVAL
+    # an empty batch ran nothing: no device read, nothing summed
+    d0 = good_desc(batch=0, total_tokens=0, deterministic=1)
+    pref0, _ = _bwd_sizes(lib, d0)
+    assert lib.hstu_attn_bwd_report(ctypes.byref(d0), ctypes.c_void_p(1 << 20), pref0,
+                                    ctypes.byref(info), None) == 0
+    assert info.dq_from_ds == 0 and info.rab_deterministic == 1
 
 
 def test_bwd_requires_gradients(lib):
@@ -224,6 +268,15 @@ def test_bucketize_validation(lib):
         == _lib.HSTU_EINVAL
 
 
+def test_pair_offsets_validation(lib):
+    d = good_desc(batch=-1)
+    assert lib.hstu_rab_pair_offsets(ctypes.byref(d), FAKE, None, FAKE, None) == _lib.HSTU_EINVAL
+    d = good_desc()
+    assert lib.hstu_rab_pair_offsets(ctypes.byref(d), None, None, FAKE, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_rab_pair_offsets(ctypes.byref(d), FAKE, None, None, None) == _lib.HSTU_EINVAL
+    assert lib.hstu_rab_pair_offsets(None, FAKE, None, FAKE, None) == _lib.HSTU_EINVAL
+
+
 def test_host_pair_accounting_matches_oracle():
     import numpy as np
     from oracle.attention import unmasked_pairs
@@ -233,6 +286,5 @@ def test_host_pair_accounting_matches_oracle():
         nt = np.minimum(rng.integers(0, 10, size=6), L)
         offs = np.concatenate([[0], np.cumsum(L)])
         assert unmasked_pairs_host(L, nt) == unmasked_pairs(offs, nt)
-        assert pair_offsets_host(L, nt)[-1] == unmasked_pairs(offs, nt)
     f = attention_flops([3, 4], heads=2, d_qk=32, d_v=32)
     assert f["pair_heads"] == 2 * (6 + 10) and f["total"] == f["pair_heads"] * 14 * 32

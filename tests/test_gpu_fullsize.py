@@ -1,16 +1,19 @@
-"""Full-size parity of the HIP path on sampled outputs (needs a gfx950 GPU).
+"""Full-size parity of the HIP path (needs a gfx950 GPU).
 
 The efficiency workload (8 sequences, lengths U[4096, 8192], 4 heads, head
 dim 128, bf16, both rab tables) runs through the C ABI exactly as the
 benchmark times it; the oracle then evaluates sampled outputs one by one
-(oracle/sampled.py): rows of O, A, dQ and dU, key rows of dK and dV, and
-d_rab_pos entries as diagonal sums of dS. d_rab_time is checked through a
-property that holds at any size: every unmasked pair adds its dS to exactly
-one position bucket and one time bucket, so both tables sum to the same
-total. The M-FALCON layer workload (4 users x (8192 + 1024 candidates),
-d_model 512) is checked on sampled rows of UVQK, A and Y, and its backward
-on sampled rows of dX (with db2 whole).
+(oracle/sampled.py): rows of O, A, dQ and dU, key rows of dK and dV,
+d_rab_pos entries as diagonal sums of dS, and both rab-table gradients whole
+(every entry, from dS over all 478 M unmasked pair-heads, spread over the
+host's cores), in the default and in the deterministic mode. The bucket
+export is compared bit for bit on rows at tile edges of every sequence,
+with all their keys. The M-FALCON layer workload (4 users x (8192 + 1024
+candidates), d_model 512) is checked on sampled rows of UVQK, A and Y, and
+its backward on sampled rows of dX (with db2 whole).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -45,10 +48,15 @@ def _sample_rows(offs, rng, per_seq=6):
 
 
 @pytest.fixture(scope="module")
-def efficiency():
-    import torch
+def eff_inputs():
     inp = W.make_attention_inputs(W.EFFICIENCY)
-    dev = P.to_dev(inp)
+    return inp, P.to_dev(inp)
+
+
+@pytest.fixture(scope="module")
+def efficiency(eff_inputs):
+    import torch
+    inp, dev = eff_inputs
     O, A = P.gpu_fwd(inp, dev)
     g = P.gpu_bwd(inp, A, dev)
     torch.cuda.synchronize()
@@ -56,6 +64,17 @@ def efficiency():
     got.update({k: P.host(v) for k, v in g.items()})
     print(f"efficiency workload: T={int(inp['seq_offsets'][-1])}", flush=True)
     return inp, got
+
+
+@pytest.fixture(scope="module")
+def eff_rab_oracle(eff_inputs):
+    """Both rab-table gradients of the efficiency workload, every entry (float64)."""
+    inp, _ = eff_inputs
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    print(f"oracle rab gradients on {workers} processes", flush=True)
+    return sampled.rab_gradients(inp["q"], inp["k"], inp["v"], inp["u"], inp["seq_offsets"],
+                                 inp["max_len"], inp["d_o"], inp["num_targets"], inp["timestamps"],
+                                 inp["rab_pos"], inp["rab_time"], workers=workers)
 
 
 def test_efficiency_forward_rows(efficiency):
@@ -106,6 +125,74 @@ def test_efficiency_rab_gradients(efficiency):
     assert abs(tp - tt) <= 1e-3 * scale, (tp, tt, scale)
 
 
+def test_efficiency_rab_gradients_whole(efficiency, eff_rab_oracle):
+    """Every entry of d_rab_pos (16383) and d_rab_time (128), element by element."""
+    inp, got = efficiency
+    wp, wt = eff_rab_oracle
+    for key, want in (("d_rab_pos", wp), ("d_rab_time", wt)):
+        e = P.rel_l2(got[key], want)
+        assert e <= P.BF16_REL, (key, e)
+    # entries no pair reads stay exactly zero (positive offsets: no candidates)
+    assert np.all(got["d_rab_pos"][0, inp["max_len"]:] == 0)
+    assert np.all(wp[0, inp["max_len"]:] == 0)
+
+
+def test_efficiency_deterministic(eff_inputs, eff_rab_oracle):
+    """The deterministic mode at full size: two runs bit for bit equal, the
+    same parity, and the report says the fixed-order sums and the dS export ran."""
+    import torch
+    from hstu_pointwise_attention_amd import ops
+    inp, dev = eff_inputs
+    _, A = P.gpu_fwd(inp, dev)
+    runs = []
+    for _ in range(2):
+        g = ops.attn_bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["seq_offsets"], inp["max_len"],
+                         A, dev["d_o"], timestamps=dev["timestamps"], rab_pos=dev["rab_pos"],
+                         rab_time=dev["rab_time"], deterministic=True, report=True)
+        torch.cuda.synchronize()
+        assert g["info"] == {"dq_from_ds": True, "rab_deterministic": True}, g["info"]
+        runs.append({k: v.clone() for k, v in g.items() if k != "info"})
+    for key in runs[0]:
+        assert torch.equal(runs[0][key], runs[1][key]), key
+    wp, wt = eff_rab_oracle
+    assert P.rel_l2(P.host(runs[0]["d_rab_pos"]), wp) <= P.BF16_REL
+    assert P.rel_l2(P.host(runs[0]["d_rab_time"]), wt) <= P.BF16_REL
+
+
+def _edge_rows(L, rng):
+    picks = {0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 4095, 4096, L - 129, L - 128, L - 65,
+             L - 64, L - 2, L - 1}
+    picks |= set(int(x) for x in rng.integers(0, L, size=4))
+    return sorted(i for i in picks if 0 <= i < L)
+
+
+def test_efficiency_bucket_export_rows(eff_inputs):
+    """hstu_rab_bucketize at full size, bit for bit, on rows at tile edges of
+    every sequence (and random rows), each with all of its keys."""
+    from hstu_pointwise_attention_amd import ops
+    inp, dev = eff_inputs
+    bp, bt = ops.rab_bucketize(dev["seq_offsets"], inp["max_len"], timestamps=dev["timestamps"],
+                               n_time_buckets=inp["rab_time"].shape[1])
+    offs = inp["seq_offsets"]
+    ts = inp["timestamps"]
+    rng = np.random.default_rng(12)
+    base = 0
+    n_rows = 0
+    for b in range(len(offs) - 1):
+        s, e = int(offs[b]), int(offs[b + 1])
+        L = e - s
+        for i in _edge_rows(L, rng):
+            o = base + i * (i + 1) // 2
+            cols = np.arange(i + 1)
+            want_bp = oracle.position_buckets(np.array([i]), cols, L, inp["max_len"])[0]
+            want_bt = oracle.time_buckets(ts[s + i:s + i + 1], ts[s:s + i + 1], inp["rab_time"].shape[1])[0]
+            assert np.array_equal(bp[o:o + i + 1].cpu().numpy().astype(np.int64), want_bp), (b, i)
+            assert np.array_equal(bt[o:o + i + 1].cpu().numpy().astype(np.int64), want_bt), (b, i)
+            n_rows += 1
+        base += L * (L + 1) // 2
+    assert base == bp.numel() and n_rows > 8 * 16
+
+
 @pytest.fixture(scope="module")
 def layer():
     import torch
@@ -138,6 +225,9 @@ def test_layer_rows(layer):
     for key in ("uvqk", "a", "y"):
         e = P.rel_l2(got[key][rows], want[key])
         assert e <= P.BF16_REL, (key, e)
+    # the layer's output Y also under the bf16 output bar
+    err = float(np.max(np.abs(got["y"][rows] - want["y"])))
+    assert err <= P.BF16_O_MAXABS, ("Y max-abs", err)
 
 
 @pytest.fixture(scope="module")

@@ -1,4 +1,5 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle. Needs a gfx950 GPU."""
+import ctypes
 import dataclasses
 
 import numpy as np
@@ -79,6 +80,33 @@ def test_bucketize_edge_timestamps():
             inp = dict(seq_offsets=offs, num_targets=np.array([1, 0, 3, 1, 12]),
                        timestamps=ts.astype(np.int64), max_len=6, dtype="fp32")
             _bucket_case(inp, nb)
+
+
+def test_pair_offsets_match_oracle():
+    """hstu_rab_pair_offsets: exclusive sums of each sequence's unmasked pairs
+    (counted on the oracle's mask), with empty sequences, candidates, and more
+    sequences than one workgroup's chunk."""
+    import torch
+    from hstu_pointwise_attention_amd import _lib, ops
+    from oracle.attention import _mask
+    rng = np.random.default_rng(21)
+    for B in (0, 1, 7, 1500):
+        L = rng.integers(0, 60, size=B)
+        nt = np.minimum(rng.integers(0, 12, size=B), L)
+        offs = np.concatenate([[0], np.cumsum(L)]).astype(np.int64)
+        d = _lib.AttnDesc()
+        d.batch = B
+        po = torch.empty(B + 1, dtype=torch.int64, device="cuda")
+        for targets in (None, nt):
+            t = None if targets is None else torch.from_numpy(targets.astype(np.int64)).cuda()
+            _lib.check(_lib.load().hstu_rab_pair_offsets(
+                ctypes.byref(d), ops._ptr(torch.from_numpy(offs).cuda()), ops._ptr(t), ops._ptr(po),
+                ops._stream()))
+            got = po.cpu().numpy()
+            counts = [int(_mask(np.arange(L[b]), int(L[b]), int(L[b] - (0 if targets is None else targets[b]))).sum())
+                      for b in range(B)]
+            want = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+            assert np.array_equal(got, want), (B, targets is None)
 
 
 def _run_parity(inp, backward=True, tag=""):
@@ -242,21 +270,67 @@ def test_autograd_function_matches_ops():
 
 def test_bf16_dq_paths_agree():
     """The bf16 backward computes dQ from the key-block kernel's exported dS
-    tiles when the batch's tiles fit the workspace sized from max_len, and by
-    recomputing dS otherwise. Without a position bias max_len changes nothing
-    else, so the same inputs run both ways: lengths 300, 200, 77 with H 2 hold
-    2 * (9 + 6 + 2) = 34 tiles; max_len 512 sizes room for 2 * 5 * 7 = 70
-    (export), max_len 64 for 2 * 2 * 7 = 28 (recompute). Both match the oracle
-    and each other."""
+    tiles when the workspace holds their room and the batch's tiles fit it,
+    and by recomputing dS otherwise. Without a position bias max_len changes
+    nothing else, so the same inputs run three ways: lengths 300, 200, 77 with
+    H 2 hold 2 * (9 + 6 + 2) = 34 tiles; max_len 512 sizes room for
+    2 * 5 * 7 = 70 (export), max_len 64 for 2 * 2 * 7 = 28 (recompute: the
+    tiles do not fit), and the minimum workspace has no room (recompute). The
+    report names the path each time; all match the oracle and each other."""
     lengths = (300, 200, 77)
     w = W.AttnWorkload("dqpaths", 41, 3, 2, 64, 64, 512, 16, False, "bf16", "fixed", lengths)
     inp = W.make_attention_inputs(w)
     inp["num_targets"] = np.array([20, 0, 5], np.int64)
     want = P.oracle_bwd(inp)
     got = {}
-    for max_len in (512, 64):
+    for name, max_len, room, from_ds in (("export", 512, True, True), ("no fit", 64, True, False),
+                                         ("min workspace", 512, False, False)):
         run = dict(inp, max_len=max_len)
         _, A = P.gpu_fwd(run)
-        got[max_len] = P.gpu_bwd(run, A)
-        P.check_bwd(run, got[max_len], want, f"max_len {max_len}")
-    assert P.rel_l2(P.host(got[512]["dq"]), P.host(got[64]["dq"])) <= P.BF16_REL
+        got[name] = P.gpu_bwd(run, A, ds_room=room, report=True)
+        assert got[name]["info"]["dq_from_ds"] is from_ds, (name, got[name]["info"])
+        P.check_bwd(run, got[name], want, name)
+    for name in ("no fit", "min workspace"):
+        assert P.rel_l2(P.host(got["export"]["dq"]), P.host(got[name]["dq"])) <= P.BF16_REL
+
+
+def _det_case(name):
+    if name == "tiny_fp32":
+        return W.make_attention_inputs(W.TINY)
+    if name in ("public", "long"):
+        return W.make_attention_inputs(W.PUBLIC if name == "public" else W.LONG)
+    # candidates with both tables (the position window path), 64-bit timestamps
+    # in every other sequence, per-head tables, fp32 and bf16
+    dtype = "fp32" if name.endswith("fp32") else "bf16"
+    D = 64 if dtype == "fp32" else 128
+    lengths = (130, 0, 70, 200, 1, 65)
+    w = W.AttnWorkload("det", 51, len(lengths), 2, D, D, 160, 64, True, dtype, "fixed", lengths,
+                       rab_heads=2)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.array([40, 0, 3, 70, 1, 0], np.int64)
+    inp["timestamps"] = _timestamps("mixed", inp["seq_offsets"], np.random.default_rng(5)).astype(np.int64)
+    return inp
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "public", "long", "cand_fp32", "cand_bf16"])
+def test_deterministic_rab_repeatable(name):
+    """desc.deterministic: the rab gradients (and every other output) repeat bit
+    for bit over three runs, match the oracle, and the report says so."""
+    import torch
+    inp = _det_case(name)
+    dev = P.to_dev(inp)
+    _, A = P.gpu_fwd(inp, dev)
+    runs = []
+    for _ in range(3):
+        g = P.gpu_bwd(inp, A, dev, deterministic=True, report=True)
+        torch.cuda.synchronize()
+        assert g["info"]["rab_deterministic"], g["info"]
+        # the preferred workspace holds the dS room in this mode too (bf16)
+        assert g["info"]["dq_from_ds"] == (inp["dtype"] == "bf16"), g["info"]
+        runs.append(g)
+    for key in ("dq", "dk", "dv", "du", "d_rab_pos", "d_rab_time"):
+        if runs[0][key] is None:
+            continue
+        for r in runs[1:]:
+            assert torch.equal(runs[0][key], r[key]), (name, key)
+    P.check_bwd(inp, runs[0], P.oracle_bwd(inp), name)

@@ -78,3 +78,27 @@ def test_locate():
     assert sampled.locate(offs, 2) == (0, 2)
     assert sampled.locate(offs, 3) == (2, 0)      # empty sequence 1 is skipped
     assert sampled.locate(offs, 9) == (2, 6)
+
+
+RAB_CASES = [
+    dict(seed=41, targets=[1, 0, 0, 2]),
+    dict(seed=42, targets=None, rab_heads=2),
+    dict(seed=43, targets=[0, 3, 1, 1], gate=False),
+    dict(seed=44, targets=None, pos=False),
+]
+
+
+@pytest.mark.parametrize("kw", RAB_CASES, ids=lambda k: f"seed{k['seed']}")
+@pytest.mark.parametrize("workers", [1, 2])
+def test_rab_gradients_match_scalar(kw, workers):
+    c, d_o = pins.tiny_case(**kw)
+    want = _scalar(c, d_o)
+    gp, gt = sampled.rab_gradients(c["q"], c["k"], c["v"], c["u"], c["seq_offsets"], c["max_len"],
+                                   d_o, c["num_targets"], c["timestamps"], c["rab_pos"],
+                                   c["rab_time"], workers=workers, rows_per=3)
+    for got, key in ((gp, "d_rab_pos"), (gt, "d_rab_time")):
+        w = want[key]
+        if w is None:
+            assert got is None
+        else:
+            assert pins.rel(got, np.array(w)) < 1e-12, key
