@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu_attn.so")
 SOURCES = ["api.hip", "prep.hip", "fwd.hip", "bwd.hip", "bwd_k16.hip", "layer.hip", "fp8.hip", "dq_ds.hip",
-           "rab_reduce.hip", "prof.hip"]
+           "rab_reduce.hip", "noalloc.hip", "prof.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

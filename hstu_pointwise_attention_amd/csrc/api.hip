@@ -30,6 +30,20 @@ hstu_status ok() {
   return HSTU_OK;
 }
 
+}  // namespace
+
+int hstu::set_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+namespace {
+
 hstu_status hip_fail(hipError_t e, const char* what) {
   return fail(HSTU_EHIP, "%s: %s", what, hipGetErrorString(e));
 }

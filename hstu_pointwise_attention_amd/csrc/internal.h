@@ -88,6 +88,9 @@ struct AttnParams {
 // the entries of a position window).
 constexpr int kPartW = 192;
 
+// Records the message hstu_last_error() returns on this thread; returns status.
+int set_error(int status, const char* fmt, ...);
+
 // Workspace layout: returns total bytes and fills the pointers in p (when
 // base != nullptr). ds_room: the bf16 backward's room for the dS export;
 // p.det: the deterministic rab-gradient partials.

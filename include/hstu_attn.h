@@ -134,6 +134,25 @@ HSTU_API hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* se
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Arguments, results and errors as
+ * in hstu_attn_fwd, without the workspace: the call uses a fixed 16 MiB
+ * device array inside the library (enough for about 3.5 million tokens),
+ * which each GPU the library runs on holds until the process ends. A shape
+ * whose hstu_attn_fwd_workspace_size exceeds 16 MiB returns HSTU_EWORKSPACE
+ * before any launch. All calls on one GPU share that array: calls on one GPU
+ * that overlap in time (other streams or host threads) race and must not be
+ * made. The first call on each device looks up the array's device address
+ * (the device must be current).
+ */
+HSTU_API hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* desc, const int64_t* seq_offsets,
+                                           const int64_t* num_targets, const int64_t* timestamps,
+                                           const float* rab_pos, const float* rab_time,
+                                           const void* q, const void* k, const void* v,
+                                           const void* u, void* o, float* a_saved, void* stream);
+
+/*
  * Candidate scoring against a cached history (M-FALCON-style micro-batched
  * inference; the pages name M-FALCON for inference in the abstract of
  * "Actions Speak Louder than Words" and in the Generative Recommenders
