@@ -132,7 +132,8 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
   const bf16* __restrict__ dag = reinterpret_cast<const bf16*>(p.d_a);
 
   if constexpr (has_time)
-    for (int x = tid; x < p.n_time_buckets; x += C::NT) sm.ttab[x] = p.rab_time[(int64_t)hr * p.n_time_buckets + x];
+    for (int x = tid; x < p.n_time_buckets; x += C::NT)
+      sm.ttab[x] = kNegLog2e * p.rab_time[(int64_t)hr * p.n_time_buckets + x];
   // Deterministic mode: every sum has a fixed order (per-wave LDS copies,
   // partials in the workspace instead of global atomics).
   const bool det = p.det != 0 && *p.det_on != 0;
@@ -248,7 +249,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
       const bool need_mask = !(q0 >= jw + 15 && jw + 15 < hist && q0 + C::BM - 1 < L);
       const int p_min = min(q0, hist);
       int tmode = has_time ? 2 : 1, b_lo = 0, b_hi = 0;
-      uint32_t thr = 0;
+      int istar = C::BM;                           // first query of the tile in bucket b_hi
       if (has_time && !wide && !need_mask && sorted_ts) {
         const int qi_hi = min(q0 + C::BM - 1, L - 1) - q0;
         const int kj_hi = min(jw + 15, L - 1) - k0;
@@ -256,10 +257,18 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
         b_lo = time_bucket_rel((uint32_t)sm.tsq[0], (uint32_t)sm.tsk[kj_hi], t_last);
         if (b_hi == b_lo) {
           tmode = 1;
-          thr = 0xffffffffu;
         } else if (b_hi == b_lo + 1) {
           tmode = 1;
-          thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);   // hi iff ts_i - ts_j + 1 >= 2^b_hi
+          // query i of this key's pairs is in b_hi iff ts_i - ts_j + 1 >= 2^b_hi;
+          // the tile's 64 timestamps are valid and sorted, so those queries
+          // are a suffix: count the ones below the threshold (binary search)
+          const uint32_t thr = (uint32_t)ts_j + ((1u << b_hi) - 1u);
+          int pos = 0;
+#pragma unroll
+          for (int step = C::BM / 2; step > 0; step >>= 1)
+            if ((uint32_t)sm.tsq[pos + step - 1] < thr) pos += step;
+          // the steps reach BM - 1 at most: the last query decides BM
+          istar = pos + ((uint32_t)sm.tsq[pos] < thr ? 1 : 0);
         }
       }
       auto tile_math = [&](auto tm, auto mk, auto pd) {
@@ -316,39 +325,42 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
           bool his[8];
           float sv[8], sg[8];
 #pragma unroll
+          // sv = -log2(e) * S (the time table is stored scaled), so that
+          // sigma(S) = 1 / (1 + 2^sv) and sl = sv * sigma(S) = -log2(e) SiLU(S)
           for (int e = 0; e < 8; ++e) {
             const int ql = 32 * kc + 16 * (e >> 2) + 4 * q4 + (e & 3);
-            float s = acc_s[kc][e >> 2][e & 3];
+            float tb = 0.f;
             int bt = 0;
             bool hi = false;
             if constexpr (has_time) {
               if constexpr (TM == 0) {
-                s += tb_lo;
+                tb = tb_lo;
               } else if constexpr (TM == 1) {
-                hi = (uint32_t)sm.tsq[ql] >= thr;
-                s += hi ? tb_hi : tb_lo;
+                hi = 32 * kc + 16 * (e >> 2) + (e & 3) >= istar - 4 * q4;
+                tb = hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
                 bt = time_bucket_rel((uint32_t)sm.tsq[ql], (uint32_t)ts_j, t_last);
-                s += sm.ttab[bt];
+                tb = sm.ttab[bt];
               } else {
                 bt = time_bucket_wide(sm.tsq[ql], ts_j, t_last);
-                s += sm.ttab[bt];
+                tb = sm.ttab[bt];
               }
             }
-            sv[e] = s;
+            sv[e] = __builtin_fmaf(acc_s[kc][e >> 2][e & 3], kNegLog2e, tb);
             bts[e] = bt;
             his[e] = hi;
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_exp2f(sv[e] * kNegLog2e);
+          for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_exp2f(sv[e]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_rcpf(1.0f + sg[e]);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int h = e >> 2, r = e & 3;
             const int i = q0 + 32 * kc + 16 * h + 4 * q4 + r;
+            // SiLU'(S) = sigma + SiLU(S) (1 - sigma), SiLU(S) = -ln(2) sl
             float sl = sv[e] * sg[e];
-            float ds = acc_p[kc][h][r] * (sg[e] + __builtin_fmaf(-sl, sg[e], sl));
+            float ds = acc_p[kc][h][r] * __builtin_fmaf(__builtin_fmaf(-sl, sg[e], sl), kNegLn2, sg[e]);
             if constexpr (MASK) {
               const bool ok = j <= i && (j < hist || j == i) && i < L;
               sl = ok ? sl : 0.f;
@@ -514,7 +526,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
       if (jj < L) {
         const int64_t o = ((start + jj) * H + head) * (int64_t)D + 16 * db + l16;
         reinterpret_cast<bf16*>(p.dk)[o] = (bf16)acc_dk[db][r];
-        reinterpret_cast<bf16*>(p.dv)[o] = (bf16)acc_dv[db][r];
+        reinterpret_cast<bf16*>(p.dv)[o] = (bf16)(acc_dv[db][r] * kNegLn2);   // s was scaled by -log2(e)
       }
     }
   }

@@ -279,7 +279,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
       // corners bound the bucket: one bucket (mode 0), two adjacent ones split
       // by a per-query threshold (mode 1), else per-element buckets (mode 2).
       int tmode = 2, b_lo = 0, b_hi = 0;
-      int32_t thr = 0;
+      int jstar = 0;                               // keys jl < jstar of the tile are in b_hi
       if (has_time && !wide && !need_mask && sorted_ts && j0 + C::BN - 1 <= iw) {
         const int qi_hi = min(iw + 31, L - 1) - i0;
         const int kj_hi = min(j0 + C::BN - 1, L - 1) - j0;
@@ -289,7 +289,16 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           tmode = 0;
         } else if (b_hi == b_lo + 1) {
           tmode = 1;
-          thr = (int32_t)ts_i + 1 - (1 << b_hi);     // hi iff ts_j <= ts_i + 1 - 2^b_hi
+          // key j is in b_hi iff ts_j <= ts_i + 1 - 2^b_hi; the tile's 64 key
+          // timestamps are valid (every key precedes the wave's queries) and
+          // sorted, so those keys are a prefix: count them (binary search)
+          const int32_t thr = (int32_t)ts_i + 1 - (1 << b_hi);
+          int pos = 0;
+#pragma unroll
+          for (int step = C::BN / 2; step > 0; step >>= 1)
+            if ((int32_t)sm.ts[buf][pos + step - 1] <= thr) pos += step;
+          // the steps reach BN - 1 at most: the last key decides BN
+          jstar = pos + ((int32_t)sm.ts[buf][pos] <= thr ? 1 : 0);
         }
       }
       auto s_block = [&](int kb, f32x16& acc, f32x16& pacc) {
@@ -343,7 +352,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
               if constexpr (TM == 0) {
                 tb = tb_lo;
               } else if constexpr (TM == 1) {
-                const bool hi = (int32_t)sm.ts[buf][jl] <= thr;
+                const bool hi = 32 * kb + 8 * (r >> 2) + (r & 3) < jstar - 4 * g;
                 tb = hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
                 tb = sm.ttab[time_bucket_rel((uint32_t)ts_i, (uint32_t)sm.ts[buf][jl], t_last)];
