@@ -33,7 +33,12 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # (FETCH_SIZE, then WRITE_SIZE) scaled by the copy-kernel calibration; the
 # summaries are under profiles/. None when not measured for the kernel as it
 # stands.
-TRAFFIC = {}
+TRAFFIC = {
+    # key-block backward (hstu_bwd_k16_kernel, D=128, efficiency workload):
+    # FETCH_SIZE 406757 KiB x 2.00 + WRITE_SIZE 1087820 KiB x 1.00
+    "bwd": {"workload": "efficiency_8192_bf16", "bytes": 1946897000,
+            "compulsory_bytes": 1233000000, "unit": "B"},
+}
 # The pages' only figure for this path, quoted as context (not a target, not
 # comparable: another machine, and neither its hardware nor its workload
 # details are stated).
@@ -178,7 +183,9 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": TRAFFIC.get(dom),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": (TRAFFIC[dom]["bytes"] if dom in TRAFFIC and TRAFFIC[dom]["workload"] == wl.name
+                            else None),
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 5)}
 
     out = {

@@ -289,13 +289,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
 
 // rab bucket export, laid out over the jagged lower triangle: sequence
 // after sequence, query row i, then key j ascending (history rows i < hist
-// see keys 0..i, candidate rows see the history and themselves). Thread g of
-// the grid writes export slots 8g .. 8g + 7, so a wave stores 1 KB of bp and
-// 512 bytes of bt contiguously (16- and 8-byte stores). Time buckets use
-// 64-bit timestamp arithmetic, exact for any int64 pair.
-constexpr int kBktPer = 8;
+// see keys 0..i, candidate rows see the history and themselves). One
+// workgroup takes one query row at a time (grid-strided over the token
+// rows): the row's slots are one contiguous run of the export, and thread t
+// takes slots t, t + 256, ..., so that every load of key timestamps and
+// every store of bp and bt covers consecutive addresses across a wave.
+// Time buckets use 64-bit timestamp arithmetic, exact for any int64 pair.
 constexpr int kBktThreads = 256;
-constexpr int kBktGrid = 4096;
+constexpr int kBktGrid = 16384;
 
 __device__ __forceinline__ int64_t pairs_of(int L, int hist) {
   return (int64_t)hist * (hist + 1) / 2 + (int64_t)(L - hist) * (hist + 1);
@@ -312,80 +313,38 @@ __device__ __forceinline__ void seq_rows(const int64_t* seq_offsets, const int64
 
 __global__ __launch_bounds__(kBktThreads) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
                                                                 uint16_t* bp, uint8_t* bt) {
-  const int64_t total = pair_offsets[p.B];
+  const int64_t T = p.seq_offsets[p.B] - p.seq_offsets[0];
   const bool want_t = bt != nullptr;
   const int last = p.n_time_buckets - 1;
-  const bool vec = ((uintptr_t)bp % 16 == 0) && ((uintptr_t)bt % 8 == 0);
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g * kBktPer < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t o0 = g * kBktPer;
-    // the sequence holding slot o0: the last b with pair_offsets[b] <= o0
+  for (int64_t r = blockIdx.x; r < T; r += gridDim.x) {
+    // the sequence of token row r: the last b whose first row is <= r (it
+    // is not empty, since r < T)
+    const int64_t tok = p.seq_offsets[0] + r;
     int lo = 0, hi = p.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pair_offsets[mid] <= o0) lo = mid; else hi = mid;
+      if (p.seq_offsets[mid] <= tok) lo = mid; else hi = mid;
     }
-    int b = lo;
     int64_t s;
     int L, hist;
-    seq_rows(p.seq_offsets, p.num_targets, b, s, L, hist);
-    // row i and position c within the row of slot o0
-    int64_t o = o0 - pair_offsets[b];
-    const int64_t hp = (int64_t)hist * (hist + 1) / 2;
-    int i, c;
-    if (o < hp) {
-      int64_t r = (int64_t)((sqrt(8.0 * (double)o + 1.0) - 1.0) * 0.5);
-      while (r * (r + 1) / 2 > o) --r;
-      while ((r + 1) * (r + 2) / 2 <= o) ++r;
-      i = (int)r;
-      c = (int)(o - r * (r + 1) / 2);
-    } else {
-      const int64_t q = o - hp;
-      i = hist + (int)(q / (hist + 1));
-      c = (int)(q % (hist + 1));
-    }
-    int64_t ti = want_t ? p.timestamps[s + i] : 0;
-    uint16_t vp[kBktPer];
-    uint8_t vt[kBktPer];
-    const int n = total - o0 < kBktPer ? (int)(total - o0) : kBktPer;
-#pragma unroll
-    for (int m = 0; m < kBktPer; ++m) {
-      vp[m] = 0;
-      vt[m] = 0;
-      if (m < n) {
-        const int j = (i < hist || c < hist) ? c : i;
-        vp[m] = (uint16_t)pos_bucket(j - (i < hist ? i : hist), p.max_len);
-        if (want_t) vt[m] = (uint8_t)time_bucket_wide(ti, p.timestamps[s + j], last);
-        // next slot: the next key of the row, else the next row, else the
-        // first row of the next non-empty sequence
-        if (++c >= (i < hist ? i + 1 : hist + 1)) {
-          c = 0;
-          if (++i >= L && m + 1 < n) {
-            do { ++b; } while (p.seq_offsets[b + 1] == p.seq_offsets[b]);
-            seq_rows(p.seq_offsets, p.num_targets, b, s, L, hist);
-            i = 0;
-          }
-          if (want_t && m + 1 < n) ti = p.timestamps[s + i];
-        }
-      }
-    }
-    if (vec && n == kBktPer) {
-      if (bp) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = (uint32_t)vp[2 * q] | ((uint32_t)vp[2 * q + 1] << 16);
-        st16(bp + o0, w);
-      }
+    seq_rows(p.seq_offsets, p.num_targets, lo, s, L, hist);
+    const int i = (int)(tok - s);
+    const bool cand = i >= hist;
+    const int n_r = cand ? hist + 1 : i + 1;           // keys of the row
+    const int p_i = cand ? hist : i;                   // position of the row
+    const int64_t base = pair_offsets[lo] +
+                         (cand ? (int64_t)hist * (hist + 1) / 2 + (int64_t)(i - hist) * (hist + 1)
+                               : (int64_t)i * (i + 1) / 2);
+    uint16_t* const bp_row = bp ? bp + base : nullptr;
+    uint8_t* const bt_row = want_t ? bt + base : nullptr;
+    const int64_t* const ts = p.timestamps + s;
+    const int64_t ti = want_t ? ts[i] : 0;
+    for (int k = threadIdx.x; k < n_r; k += kBktThreads) {
+      const int j = (cand && k == hist) ? i : k;
+      if (bp_row) bp_row[k] = (uint16_t)pos_bucket(j - p_i, p.max_len);
       if (want_t) {
-        uint2 w;
-        w.x = (uint32_t)vt[0] | ((uint32_t)vt[1] << 8) | ((uint32_t)vt[2] << 16) | ((uint32_t)vt[3] << 24);
-        w.y = (uint32_t)vt[4] | ((uint32_t)vt[5] << 8) | ((uint32_t)vt[6] << 16) | ((uint32_t)vt[7] << 24);
-        *reinterpret_cast<uint2*>(bt + o0) = w;
-      }
-    } else {
-      for (int m = 0; m < n; ++m) {
-        if (bp) bp[o0 + m] = vp[m];
-        if (want_t) bt[o0 + m] = vt[m];
+        const int bkt = time_bucket_wide(ti, ts[j], last);
+        bt_row[k] = (uint8_t)bkt;
       }
     }
   }

@@ -180,7 +180,7 @@ def attn_bwd(q, k, v, u, seq_offsets, max_len, a_saved, d_o, *, num_targets=None
 
 def rab_bucketize(seq_offsets, max_len, *, num_targets=None, timestamps=None,
                   n_time_buckets=0, want_pos=True):
-    """Bucket export over the unmasked pairs: (bp uint16 as int32 or None, bt uint8 or None)."""
+    """Bucket export over the unmasked pairs: (bp uint16 or None, bt uint8 or None)."""
     lib = _lib.load()
     dev = seq_offsets.device
     seq_offsets, num_targets, timestamps = _i64(seq_offsets), _i64(num_targets), _i64(timestamps)
@@ -197,7 +197,7 @@ def rab_bucketize(seq_offsets, max_len, *, num_targets=None, timestamps=None,
     bt = torch.empty(max(n, 1), dtype=torch.uint8, device=dev) if timestamps is not None else None
     _lib.check(lib.hstu_rab_bucketize(ctypes.byref(d), _ptr(seq_offsets), _ptr(num_targets),
                                       _ptr(timestamps), _ptr(po), _ptr(bp), _ptr(bt), _stream()))
-    bp = bp[:n].to(torch.int32) & 0xFFFF if bp is not None else None
+    bp = bp[:n].view(torch.uint16) if bp is not None else None   # a view: no conversion kernel
     bt = bt[:n] if bt is not None else None
     return bp, bt
 
