@@ -52,6 +52,10 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int elem_bytes(int32_t dtype) { return dtype == HSTU_DTYPE_BF16 ? 2 : 4; }
 
+// Largest input row stride (elements): 64 rows of 4-byte elements must stay
+// below 2^31 bytes.
+constexpr int64_t kMaxStride = (int64_t)1 << 22;
+
 // Shape checks shared by every attention entry point.
 hstu_status check_desc(const hstu_attn_desc* d) {
   if (!d) return fail(HSTU_EINVAL, "desc is NULL");
@@ -85,6 +89,10 @@ hstu_status check_desc(const hstu_attn_desc* d) {
     if (i == 3 && strides[i] == 0) continue;  // u may be absent
     if (strides[i] < hd) return fail(HSTU_EINVAL, "%s %lld < heads*d (%lld)", names[i], (long long)strides[i], (long long)hd);
     if (strides[i] % vec) return fail(HSTU_EINVAL, "%s %lld must be a multiple of %d", names[i], (long long)strides[i], vec);
+    // the kernels address a 64-row tile of an input through a buffer
+    // resource whose range is a 32-bit byte count
+    if (strides[i] > kMaxStride)
+      return fail(HSTU_EUNSUPPORTED, "%s %lld above %lld", names[i], (long long)strides[i], (long long)kMaxStride);
   }
   return HSTU_OK;
 }

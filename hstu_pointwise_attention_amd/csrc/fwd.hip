@@ -84,13 +84,37 @@ struct FwdCfg {
 template <typename T, int D, bool GRAD>
 struct FwdSmem {
   using C = FwdCfg<T, D, GRAD>;
+  int64_t tsq[C::BM];            // query timestamps of the block
+  float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr] (forward), rab_time[hr] (gradient)
+};
+
+// The two K and V tile buffers. Direct memory-to-LDS loads into one buffer
+// run while the other is read; the compiler proves the two apart (and so
+// adds no wait for the loads before the reads) only when they are distinct
+// LDS variables named at compile time, so the kernels declare four arrays
+// and the tile loop alternates between them in two unrolled steps.
+template <typename T, int D, bool GRAD>
+struct FwdKV {
+  using C = FwdCfg<T, D, GRAD>;
   T k[2][C::BN * C::K_LD];
   T v[2][C::BN * C::V_LD];
   int64_t ts[2][C::BN];          // key timestamps: rebased (low 32 bits) or raw
-  int64_t tsq[C::BM];            // query timestamps of the block
   float win[2][C::WIN];          // rab_pos window for the tile
-  float ttab[C::MAX_TIME];       // -log2(e) * rab_time[hr] (forward), rab_time[hr] (gradient)
 };
+template <typename T>
+struct KVBufs {
+  T* k0; T* k1; T* v0; T* v1;
+  int64_t* ts0; int64_t* ts1;
+  float* w0; float* w1;
+};
+#define HSTU_FWD_TILE_BUFFERS(C)                                              \
+  __shared__ __attribute__((aligned(16))) T k0[C::BN * C::K_LD];              \
+  __shared__ __attribute__((aligned(16))) T k1[C::BN * C::K_LD];              \
+  __shared__ __attribute__((aligned(16))) T v0[C::BN * C::V_LD];              \
+  __shared__ __attribute__((aligned(16))) T v1[C::BN * C::V_LD];              \
+  __shared__ int64_t ts0[C::BN], ts1[C::BN];                                  \
+  __shared__ float w0[C::WIN], w1[C::WIN];                                    \
+  const KVBufs<T> kvb{k0, k1, v0, v1, ts0, ts1, w0, w1};
 
 // GRAD (the dQ pass of the backward): the same walk over key tiles with
 // the same bias and mask, but per tile
@@ -106,8 +130,8 @@ struct FwdSmem {
 // call's first candidate among all of the sequence's candidates.
 template <typename T, int D, bool WIDE, bool POS, bool TIME, bool GRAD, bool CAND = false>
 __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD>& sm,
-                                         const WorkItem wi, const SeqInfo si, const int head,
-                                         const int split = 0) {
+                                         const KVBufs<T> kvb, const WorkItem wi, const SeqInfo si,
+                                         const int head, const int split = 0) {
   using C = FwdCfg<T, D, GRAD>;
   using F = typename Frag<T>::type;
   const int H = p.H;
@@ -201,14 +225,64 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
 
   // ---------------------------------------------------------------- staging
   u32x4 kreg[C::CH], vreg[C::CH];
-  int64_t tsreg = 0;
+  uint32_t tsreg = 0;                            // rebased timestamp (64-bit: tsreg64)
+  int64_t tsreg64 = 0;
   float winreg = 0.f;
 
   auto tile_j0 = [&](int n) { return (n < h_n ? h_lo + n : b_start + (n - h_n)) * C::BN; };
 
-  auto load_tile = [&](int j0) {
+  // Non-candidate tiles: K and V rows through buffer resources whose range
+  // ends at the sequence's last row, so rows at or beyond L read as zero
+  // without a branch; the lane's offsets within a tile are fixed.
+  // Each LDS row of the K (V) tile is KROW (VROW) 16-byte chunks, of which
+  // the first CPR hold the row and the rest are padding. The tile is written
+  // straight from memory to LDS, 64 consecutive chunks per wave instruction:
+  // instruction k' of a tile (k' = wave, wave + 4, ...) fills chunks 64 k' ..
+  // 64 k' + 63, lane l chunk 64 k' + l, which it fetches from the row stored
+  // there (rows permuted where the tile is) and, for padding, the row's last
+  // chunk again.
+  constexpr int KROW = C::K_LD * C::ES / 16, VROW = C::V_LD * C::ES / 16;
+  constexpr int KI = (KROW + 3) / 4, VI = (VROW + 3) / 4;
+  static_assert(KROW * 16 == C::K_LD * C::ES && VROW * 16 == C::V_LD * C::ES, "chunk rows");
+  uint32_t koff[KI], voff[VI];
 #pragma unroll
-    for (int m = 0; m < C::CH; ++m) {
+  for (int i = 0; i < KI; ++i) {
+    const int c = 64 * (wave + 4 * i) + lane;
+    const int r = c / KROW, q = c % KROW;
+    const int gr = C::K_PERM ? row_perm(r) : r;
+    koff[i] = (uint32_t)((int64_t)gr * p.sk * C::ES + (q < C::CPR ? q : C::CPR - 1) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int c = 64 * (wave + 4 * i) + lane;
+    const int r = c / VROW, q = c % VROW;
+    const int gr = C::V_PERM ? row_perm(r) : r;
+    voff[i] = (uint32_t)((int64_t)gr * p.sv * C::ES + (q < C::CPR ? q : C::CPR - 1) * 16);
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto load_tile = [&](int j0, T* kn, T* vn) {
+    if constexpr (!CAND) {
+      const int rows = min(L - j0, C::BN);
+      const T* kb = kg + (start + j0) * p.sk + (int64_t)head * D;
+      const T* vb = vg + (start + j0) * p.sv + (int64_t)head * D;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, rows * (int)p.sk * C::ES, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, rows * (int)p.sv * C::ES, 0x00020000);
+      typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        if (wave_u + 4 * i < KROW)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rk, (lds_void*)((char*)kn + 1024 * (wave_u + 4 * i)), 16, koff[i], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < VI; ++i)
+        if (wave_u + 4 * i < VROW)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv, (lds_void*)((char*)vn + 1024 * (wave_u + 4 * i)), 16, voff[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int m = 0; m < (CAND ? C::CH : 0); ++m) {
       const int ch = tid + C::NT * m;
       const int row = ch / C::CPR, cc = ch % C::CPR;
       const int j = j0 + row;
@@ -225,11 +299,14 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
         vreg[m] = j < L ? ld16(vg + (start + j) * p.sv + off) : u32x4{0, 0, 0, 0};
       }
     }
-    if (has_time && tid < C::BN) {
+    // wave-uniform conditions: no divergent branch around the loads, whose
+    // results are not needed before the tile's end
+    if (has_time && wave_u == 0) {
       const int j = j0 + tid;
-      tsreg = j < L ? (wide ? p.timestamps[start + j] : (int64_t)p.ts_rel[start + j]) : 0;
+      if constexpr (wide) tsreg64 = j < L ? p.timestamps[start + j] : 0;
+      else tsreg = p.ts_rel[start + min(j, L - 1)];
     }
-    if (has_pos && tid < C::WIN) {
+    if (has_pos && wave_u < C::WIN / kWave) {
       const int rel = j0 - p_max + tid;
       // CAND: offsets >= 0 are the self terms (candidates see no other candidate)
       const int relp = CAND && rel >= 0 ? rel + sc.pos_shift : rel;
@@ -237,16 +314,16 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](T* kn, T* vn, int64_t* tsn, float* wn) {
 #pragma unroll
-    for (int m = 0; m < C::CH; ++m) {
+    for (int m = 0; m < (CAND ? C::CH : 0); ++m) {
       const int ch = tid + C::NT * m;
       const int row = ch / C::CPR, cc = ch % C::CPR;
-      st16(sm.k[buf] + (C::K_PERM ? row_perm(row) : row) * C::K_LD + cc * C::VPC, kreg[m]);
-      st16(sm.v[buf] + (C::V_PERM ? row_perm(row) : row) * C::V_LD + cc * C::VPC, vreg[m]);
+      st16(kn + (C::K_PERM ? row_perm(row) : row) * C::K_LD + cc * C::VPC, kreg[m]);
+      st16(vn + (C::V_PERM ? row_perm(row) : row) * C::V_LD + cc * C::VPC, vreg[m]);
     }
-    if (has_time && tid < C::BN) sm.ts[buf][tid] = tsreg;
-    if (has_pos && tid < C::WIN) sm.win[buf][tid] = winreg;
+    if (has_time && wave_u == 0) tsn[tid] = wide ? tsreg64 : (int64_t)tsreg;
+    if (has_pos && wave_u < C::WIN / kWave) wn[tid] = winreg;
   };
 
   f32x16 acc_o[C::DB];
@@ -256,24 +333,23 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
     for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
 
   if (n_tiles > 0) {
-    load_tile(tile_j0(0));
-    store_tile(0);
+    load_tile(tile_j0(0), kvb.k0, kvb.v0);
+    store_tile(kvb.k0, kvb.v0, kvb.ts0, kvb.w0);
   }
   __syncthreads();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int buf = n & 1;
+  // one tile: read ks / vs (buffer n & 1), load tile n + 1 into kn / vn
+  auto step = [&](const int n, const T* ks, const T* vs, const int64_t* tss, const float* wins,
+                  T* kn, T* vn, int64_t* tsn, float* wn) {
     const int j0 = tile_j0(n);
     const bool more = n + 1 < n_tiles;
-    if (more) load_tile(tile_j0(n + 1));
+    if (more) load_tile(tile_j0(n + 1), kn, vn);
 
     // Does this wave have any unmasked pair in the tile?
     const bool skip = iw >= L || j0 > iw + 31 || (j0 >= hist && j0 + C::BN - 1 < iw) ||
                       (CAND && iw + 31 < hist);   // CAND: no candidate row in this wave
     if (!skip) {
       const bool need_mask = j0 + C::BN - 1 > min(iw, hist - 1);
-      const T* ks = sm.k[buf];
-      const T* vs = sm.v[buf];
       // Time-bias mode of this wave's sub-tile (its 32 queries x the 64 keys):
       // with sorted timestamps and every key at or before every query, the
       // corners bound the bucket: one bucket (mode 0), two adjacent ones split
@@ -283,8 +359,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
       if (has_time && !wide && !need_mask && sorted_ts && j0 + C::BN - 1 <= iw) {
         const int qi_hi = min(iw + 31, L - 1) - i0;
         const int kj_hi = min(j0 + C::BN - 1, L - 1) - j0;
-        b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)sm.ts[buf][0], t_last);
-        b_lo = time_bucket_rel((uint32_t)sm.tsq[iw - i0], (uint32_t)sm.ts[buf][kj_hi], t_last);
+        b_hi = time_bucket_rel((uint32_t)sm.tsq[qi_hi], (uint32_t)tss[0], t_last);
+        b_lo = time_bucket_rel((uint32_t)sm.tsq[iw - i0], (uint32_t)tss[kj_hi], t_last);
         if (b_hi == b_lo) {
           tmode = 0;
         } else if (b_hi == b_lo + 1) {
@@ -296,14 +372,14 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           int pos = 0;
 #pragma unroll
           for (int step = C::BN / 2; step > 0; step >>= 1)
-            if ((int32_t)sm.ts[buf][pos + step - 1] <= thr) pos += step;
+            if ((int32_t)tss[pos + step - 1] <= thr) pos += step;
           // the steps reach BN - 1 at most: the last key decides BN
-          jstar = pos + ((int32_t)sm.ts[buf][pos] <= thr ? 1 : 0);
+          jstar = pos + ((int32_t)tss[pos] <= thr ? 1 : 0);
         }
       }
       auto s_block = [&](int kb, f32x16& acc, f32x16& pacc) {
         if constexpr (has_pos) {
-          const float* w = sm.win[buf] + c_lane + 32 * kb + 4 * g;
+          const float* w = wins + c_lane + 32 * kb + 4 * g;
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
         } else {
@@ -355,9 +431,9 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
                 const bool hi = 32 * kb + 8 * (r >> 2) + (r & 3) < jstar - 4 * g;
                 tb = hi ? tb_hi : tb_lo;
               } else if constexpr (TM == 2) {
-                tb = sm.ttab[time_bucket_rel((uint32_t)ts_i, (uint32_t)sm.ts[buf][jl], t_last)];
+                tb = sm.ttab[time_bucket_rel((uint32_t)ts_i, (uint32_t)tss[jl], t_last)];
               } else {
-                tb = sm.ttab[time_bucket_wide(ts_i, sm.ts[buf][jl], t_last)];
+                tb = sm.ttab[time_bucket_wide(ts_i, tss[jl], t_last)];
               }
             }
             return tb;
@@ -446,8 +522,12 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           tile_math(I2(), NoMask());
       }
     }
-    if (more) store_tile(buf ^ 1);
+    if (more) store_tile(kn, vn, tsn, wn);
     __syncthreads();
+  };
+  for (int n = 0; n < n_tiles; n += 2) {
+    step(n, kvb.k0, kvb.v0, kvb.ts0, kvb.w0, kvb.k1, kvb.v1, kvb.ts1, kvb.w1);
+    if (n + 1 < n_tiles) step(n + 1, kvb.k1, kvb.v1, kvb.ts1, kvb.w1, kvb.k0, kvb.v0, kvb.ts0, kvb.w0);
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -510,6 +590,8 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
+  using C = FwdCfg<T, D, false>;
+  HSTU_FWD_TILE_BUFFERS(C)
   if constexpr (WIDE) {
     // sequences needing 64-bit timestamps are rare: a small grid walks the
     // work slots and takes only theirs
@@ -521,7 +603,7 @@ void hstu_fwd_kernel(AttnParams p) {
       const WorkItem wi = p.items[item];
       const SeqInfo si = p.seq[wi.seq];
       if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, false>(p, sm, wi, si, head);
+      fwd_body<T, D, true, POS, TIME, false>(p, sm, kvb, wi, si, head);
       __syncthreads();                             // the next slot reuses the LDS
     }
   } else {
@@ -531,7 +613,7 @@ void hstu_fwd_kernel(AttnParams p) {
     const WorkItem wi = p.items[item];
     const SeqInfo si = p.seq[wi.seq];
     if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
-    fwd_body<T, D, false, POS, TIME, false>(p, sm, wi, si, head);
+    fwd_body<T, D, false, POS, TIME, false>(p, sm, kvb, wi, si, head);
   }
 }
 
@@ -539,6 +621,8 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_fwd_cand_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
+  __shared__ FwdKV<T, D, false> kv;
+  const KVBufs<T> kvb{kv.k[0], kv.k[1], kv.v[0], kv.v[1], kv.ts[0], kv.ts[1], kv.win[0], kv.win[1]};
   const int S = p.kv_splits;                       // workgroups per (item, head)
   if constexpr (WIDE) {
     if (p.n_items[1] == 0) return;
@@ -550,7 +634,7 @@ void hstu_fwd_cand_kernel(AttnParams p) {
       const WorkItem wi = p.items[item];
       const SeqInfo si = p.seq[wi.seq];
       if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, wi, si, head, split);
+      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, kvb, wi, si, head, split);
       __syncthreads();                             // the next slot reuses the LDS
     }
   } else {
@@ -561,7 +645,7 @@ void hstu_fwd_cand_kernel(AttnParams p) {
     const WorkItem wi = p.items[item];
     const SeqInfo si = p.seq[wi.seq];
     if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
-    fwd_body<T, D, false, POS, TIME, false, true>(p, sm, wi, si, head, split);
+    fwd_body<T, D, false, POS, TIME, false, true>(p, sm, kvb, wi, si, head, split);
   }
 }
 
@@ -595,6 +679,8 @@ template <typename T, int D, bool WIDE, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
+  using C = FwdCfg<T, D, true>;
+  HSTU_FWD_TILE_BUFFERS(C)
   if (p.ds_on != nullptr && *p.ds_on != 0) return;   // dQ comes from the exported dS tiles
   if constexpr (WIDE) {
     // sequences needing 64-bit timestamps are rare: a small grid walks the
@@ -607,7 +693,7 @@ void hstu_dq_kernel(AttnParams p) {
       const WorkItem wi = p.items[item];
       const SeqInfo si = p.seq[wi.seq];
       if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, true>(p, sm, wi, si, head);
+      fwd_body<T, D, true, POS, TIME, true>(p, sm, kvb, wi, si, head);
       __syncthreads();                             // the next slot reuses the LDS
     }
   } else {
@@ -617,7 +703,7 @@ void hstu_dq_kernel(AttnParams p) {
     const WorkItem wi = p.items[item];
     const SeqInfo si = p.seq[wi.seq];
     if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
-    fwd_body<T, D, false, POS, TIME, true>(p, sm, wi, si, head);
+    fwd_body<T, D, false, POS, TIME, true>(p, sm, kvb, wi, si, head);
   }
 }
 

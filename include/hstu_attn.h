@@ -39,7 +39,8 @@
  *    (offsets, timestamps) is not validated: offsets must be non-decreasing
  *    from 0 to total_tokens and 0 <= num_targets[b] <= L_b.
  *  - Token tensors are row-major [T, H, D]: element (t, h, d) is at
- *    t*stride + h*D + d, with `stride` (elements, >= H*D) given per input.
+ *    t*stride + h*D + d, with `stride` (elements, >= H*D, <= 2^22; larger
+ *    strides return HSTU_EUNSUPPORTED) given per input.
  *    Outputs and gradients are dense [T, H, D] (stride H*D).
  */
 #ifndef HSTU_ATTN_H

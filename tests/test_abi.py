@@ -63,6 +63,7 @@ def fwd_call(lib, d, ws_bytes=1 << 30, rab_time=FAKE, timestamps=FAKE, ws=ctypes
     ("total_tokens", 1 << 31, _lib.HSTU_EINVAL),
     ("stride_q", 64, _lib.HSTU_EINVAL),
     ("stride_k", 130, _lib.HSTU_EINVAL),
+    ("stride_v", (1 << 22) + 8, _lib.HSTU_EUNSUPPORTED),   # beyond the 32-bit tile range
     ("deterministic", 2, _lib.HSTU_EINVAL),
 ])
 def test_desc_validation(lib, field, value, status):
