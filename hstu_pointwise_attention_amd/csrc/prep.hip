@@ -498,7 +498,7 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool
       p.tile_base = (int64_t*)take(sizeof(int64_t) * (size_t)p.B);
       int32_t* flags = (int32_t*)take(2 * sizeof(int32_t));
       p.ds_on = cap > 0 ? flags : nullptr;
-      p.det_on = det ? flags + 1 : nullptr;
+      p.det_on = det && flags ? flags + 1 : nullptr;   // (no arithmetic on the sizing pass's null)
     }
     if (det) {
       p.blk_base = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1));
