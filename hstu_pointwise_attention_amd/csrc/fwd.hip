@@ -354,6 +354,32 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
       // with sorted timestamps and every key at or before every query, the
       // corners bound the bucket: one bucket (mode 0), two adjacent ones split
       // by a per-query threshold (mode 1), else per-element buckets (mode 2).
+      auto s_block = [&](int kb, f32x16& acc, f32x16& pacc) {
+        if constexpr (has_pos) {
+          const float* w = wins + c_lane + 32 * kb + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        }
+        if constexpr (GRAD)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::KC; ++c) {
+          const F a = ld_frag(ks + (32 * kb + (C::K_PERM ? row_perm(l32) : l32)) * C::K_LD + 16 * c + 8 * g);
+          mfma_32x32x16(acc, a, qf[c]);
+          if constexpr (GRAD) {
+            const F b = ld_frag(vs + (32 * kb + l32) * C::V_LD + 16 * c + 8 * g);
+            mfma_32x32x16(pacc, b, daf[c]);
+          }
+        }
+      };
+      // The first 32-key block's MFMAs do not depend on the time-bias mode:
+      // issued before it is worked out, they run under its LDS round trips.
+      f32x16 sacc_first, pacc_first;
+      if constexpr (!GRAD) s_block(0, sacc_first, pacc_first);
       int tmode = 2, b_lo = 0, b_hi = 0;
       int jstar = 0;                               // keys jl < jstar of the tile are in b_hi
       if (has_time && !wide && !need_mask && sorted_ts && j0 + C::BN - 1 <= iw) {
@@ -377,28 +403,6 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
           jstar = pos + ((int32_t)tss[pos] <= thr ? 1 : 0);
         }
       }
-      auto s_block = [&](int kb, f32x16& acc, f32x16& pacc) {
-        if constexpr (has_pos) {
-          const float* w = wins + c_lane + 32 * kb + 4 * g;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = w[8 * (r >> 2) + (r & 3)];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        }
-        if constexpr (GRAD)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C::KC; ++c) {
-          const F a = ld_frag(ks + (32 * kb + (C::K_PERM ? row_perm(l32) : l32)) * C::K_LD + 16 * c + 8 * g);
-          mfma_32x32x16(acc, a, qf[c]);
-          if constexpr (GRAD) {
-            const F b = ld_frag(vs + (32 * kb + l32) * C::V_LD + 16 * c + 8 * g);
-            mfma_32x32x16(pacc, b, daf[c]);
-          }
-        }
-      };
       // TM: time-bias mode (3: 64-bit timestamps); MASK: causal / candidate
       // masking (only tiles that cross the diagonal or hold candidates).
       auto tile_math = [&](auto tm, auto mk) {
@@ -412,7 +416,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
         // there spills).
         constexpr bool PIPE = !GRAD;
         f32x16 sacc[C::KB], pacc[GRAD ? C::KB : 1];
-        if constexpr (PIPE) s_block(0, sacc[0], pacc[0]);
+        if constexpr (PIPE) sacc[0] = sacc_first;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
           if constexpr (PIPE) {
