@@ -8,12 +8,31 @@
 // its own rows). The product is the (KS, KS) case of the layer GEMM: dS^T
 // tiles [keys][queries] and K rows [keys][d], both read by transposing LDS
 // loads, 64 keys per stage.
+//
+// Loads go through buffer resources set per stage (the stage's two dS tiles;
+// its K rows, whose range ends at the sequence's last row), so a lane's
+// offsets are the same in every stage. Only the query block's own key block
+// and a key block holding candidate keys have rows the key-block kernel did
+// not write (its waves of 16 keys that skipped a tile, or a first 32-query
+// chunk before their keys): there the lane's offset for such a row is moved
+// past the range, which reads zeros.
 #include "internal.h"
 #include "gemm_tile.h"
 
 namespace hstu {
 
 namespace {
+
+constexpr uint32_t kOob = 0x80000000u;           // a buffer offset beyond every range: reads zero
+
+// A pointer every lane holds, moved to scalar registers (a buffer resource
+// built from it then needs no per-lane loop).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void dq_ds_kernel(AttnParams p) {
@@ -43,29 +62,50 @@ __global__ __launch_bounds__(256) void dq_ds_kernel(AttnParams p) {
   const int l32 = lane & 31, g = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // This lane's chunks of a stage (i = 0..3): row kk = c >> 4 of the stage
+  // (key 64 half + kk of the block), chunk cc = c & 15: A queries 8 (cc & 7)
+  // .. + 7 of query tile qt0 + (cc >> 3); B head dims 8 cc .. + 7.
+  uint32_t aoff[2][4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int kk = c >> 4, cc = c & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      aoff[half][i] = (cc >= 8 && !has_qt1) ? kOob
+                      : (uint32_t)(((cc >> 3) * kDsTile + (64 * half + kk) * kDsQueries + 8 * (cc & 7)) * 2);
+    boff[i] = 8 * cc < D ? (uint32_t)((int64_t)kk * p.sk * 2 + 16 * cc) : kOob;
+  }
+
   // stage st: key block kb = (st / 2)-th of the list, keys kb*128 + 64 (st & 1) + kk
   auto load = [&](u32x4 (&va)[4], u32x4 (&vb)[4], int64_t st) {
     const int idx = (int)(st >> 1), half = (int)(st & 1);
     const int kb = idx < n_hist ? idx : qb;
-    const bf16* const row0 = dsb + (ds_row_start(L, kb) + qt0 - 2 * kb) * kDsTile;
+    const int64_t row0 = ds_row_start(L, kb) + qt0 - 2 * kb;   // tile (kb, qt0)
+    const int key0 = kb * kDsKeys + 64 * half;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(dsb + row0 * kDsTile), (short)0, 2 * (int)kDsTile * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(kg + (int64_t)key0 * p.sk), (short)0,
+        __builtin_amdgcn_readfirstlane(max(0, min(64, L - key0)) * (int)p.sk * 2), 0x00020000);
+    // rows the key-block kernel left unwritten: only in the query block's own
+    // key block, and in a key block holding candidate keys (whose waves of
+    // 16 candidate keys visit only their own rows)
+    const bool own = kb == qb || (kb + 1) * kDsKeys > si.hist;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int kk = c >> 4, cc = c & 15;
-      const int jl = 64 * half + kk;              // key within the block
-      // A: queries 8 cc .. 8 cc + 7 of the block, from query tile qt0 or
-      // qt0 + 1; rows the key-block kernel did not write (its wave of 16 keys
-      // skipped the tile, or the first 32-query chunk lies before those keys)
-      // are zeros
-      const int jw = kb * kDsKeys + (jl & ~15);
-      const int q0 = (qt0 + (cc >> 3)) * kDsQueries;
-      const bool skipped = jw >= L || q0 + kDsQueries - 1 < jw ||
-                           (jw >= si.hist && (q0 > jw + 15 || q0 + kDsQueries - 1 < jw));
-      const bool a_ok = (cc < 8 || has_qt1) && !skipped && !((cc & 7) < 4 && q0 + 31 < jw);
-      va[i] = a_ok ? ld16(row0 + (cc >> 3) * kDsTile + jl * kDsQueries + 8 * (cc & 7)) : u32x4{0, 0, 0, 0};
-      // B: K row of key kb*128 + jl, head dims 8 cc .. 8 cc + 7
-      const int j = kb * kDsKeys + jl;
-      vb[i] = (8 * cc < D && j < L) ? ld16(kg + (int64_t)j * p.sk + 8 * cc) : u32x4{0, 0, 0, 0};
+      uint32_t ao = half ? aoff[1][i] : aoff[0][i];
+      if (own) {
+        const int c = tid + 256 * i;
+        const int kk = c >> 4, cc = c & 15;
+        const int jw = key0 + (kk & ~15);        // first key of the writer wave
+        const int q0 = (qt0 + (cc >> 3)) * kDsQueries;
+        const bool skipped = jw >= L || q0 + kDsQueries - 1 < jw ||
+                             (jw >= si.hist && (q0 > jw + 15 || q0 + kDsQueries - 1 < jw));
+        if (skipped || ((cc & 7) < 4 && q0 + 31 < jw)) ao = kOob;
+      }
+      va[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)ao, 0, 0);
+      vb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)boff[i], 0, 0);
     }
   };
 
