@@ -82,11 +82,18 @@ struct AttnParams {
   float* part_time;
   int64_t part_cap;
   int32_t* det_on;
+  // rab_reduce's per-run sums: [rab_heads][kRedChunks][2 max_len - 1 +
+  // n_time_room] floats (position buckets, then time buckets)
+  float* part_red;
 };
 
 // Floats per tile of the position partials (>= the diagonals of a tile and
 // the entries of a position window).
 constexpr int kPartW = 192;
+
+// Runs of units the deterministic reduction sums separately before adding
+// the runs' sums in order.
+constexpr int kRedChunks = 64;
 
 // Records the message hstu_last_error() returns on this thread; returns status.
 int set_error(int status, const char* fmt, ...);

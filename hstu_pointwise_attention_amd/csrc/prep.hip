@@ -489,6 +489,7 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool
   p.part_time = nullptr;
   p.part_cap = 0;
   p.det_on = nullptr;
+  p.part_red = nullptr;
   if (bwd) {
     p.items_q = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
     p.d_a = take((size_t)elem_bytes * (size_t)p.T * p.H * p.D);
@@ -506,6 +507,8 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool
       p.part_pos = (float*)take(sizeof(float) * kPartW * (size_t)p.part_cap);
       const int64_t slots = (p.T / kBlk + p.B) * (int64_t)p.H;
       p.part_time = (float*)take(sizeof(float) * (size_t)slots * (size_t)(p.n_time_room > 0 ? p.n_time_room : 1));
+      const size_t n_red = 2 * (size_t)p.max_len - 1 + (size_t)(p.n_time_room > 0 ? p.n_time_room : 0);
+      p.part_red = (float*)take(sizeof(float) * (size_t)kRedChunks * (size_t)p.H * n_red);
     }
     if (cap > 0) {
       p.ds_cap = cap;
