@@ -294,6 +294,24 @@ def test_bf16_dq_paths_agree():
         assert P.rel_l2(P.host(got["export"]["dq"]), P.host(got[name]["dq"])) <= P.BF16_REL
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_bf16_ds_export_head_dims(D):
+    """The dQ pass over exported dS tiles at every bf16 head dim: several key
+    blocks per sequence (513 rows: five), candidate rows in every key-block
+    position (a block of history keys, one straddling the history's end, and
+    blocks of candidates only), and a length of one tile plus one row."""
+    lengths = (513, 0, 1, 129, 300, 64)
+    w = W.AttnWorkload("dsdims", 61, len(lengths), 2, D, D, 600, 128, True, "bf16", "fixed", lengths)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.array([100, 0, 1, 5, 200, 64], np.int64)
+    O, A = P.gpu_fwd(inp)
+    want_O, want_A = P.oracle_fwd(inp)
+    P.check_fwd(inp, P.host(O), P.host(A), want_O, want_A, f"D{D}")
+    got = P.gpu_bwd(inp, A, report=True)
+    assert got["info"]["dq_from_ds"] is True, got["info"]
+    P.check_bwd(inp, got, P.oracle_bwd(inp), f"D{D}")
+
+
 def _det_case(name):
     if name == "tiny_fp32":
         return W.make_attention_inputs(W.TINY)
