@@ -166,6 +166,42 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_cand_kernel(AttnPara
   }
 }
 
+// Inclusive prefix sum over the lanes of a wave (shuffles, no barrier).
+template <typename V>
+__device__ __forceinline__ V wave_scan_incl(V v) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const V t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over the workgroup (wave
+// scans, then a scan of the wave totals by the first wave); lds holds at
+// least blockDim.x / 64 + 1 values. Returns this thread's exclusive prefix
+// and sets *total to the workgroup's sum. Ends with a barrier, so lds can
+// be reused at once.
+template <typename V>
+__device__ V block_scan_one(V v, V* lds, V* total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const V incl = wave_scan_incl(v);
+  if (lane == kWave - 1) lds[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const V w = lane < nw ? lds[lane] : V(0);
+    const V wi = wave_scan_incl(w);
+    if (lane < nw) lds[lane] = wi - w;
+    if (lane == kWave - 1) lds[nw] = wi;
+  }
+  __syncthreads();
+  const V excl = lds[wave] + incl - v;
+  *total = lds[nw];
+  __syncthreads();
+  return excl;
+}
+
 // Exclusive prefix sum over n ints in place (forward or from the end), one
 // workgroup, chunks of blockDim.x with a running carry. Returns the total.
 __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
@@ -174,20 +210,12 @@ __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
     const int idx = base + threadIdx.x;
     const int pos = from_end ? n - 1 - idx : idx;
     const int v = idx < n ? data[pos] : 0;
-    lds[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-      const int add = threadIdx.x >= (unsigned)off ? lds[threadIdx.x - off] : 0;
-      __syncthreads();
-      lds[threadIdx.x] += add;
-      __syncthreads();
-    }
-    const int incl = lds[threadIdx.x];
-    const int total = lds[blockDim.x - 1];
-    if (idx < n) data[pos] = carry + incl - v;
+    int total;
+    const int excl = block_scan_one(v, lds, &total);
+    if (idx < n) data[pos] = carry + excl;
     carry += total;
-    __syncthreads();
   }
+  __syncthreads();
   return carry;
 }
 
@@ -261,26 +289,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
   if (mode == 2 && p.tile_base != nullptr) {
     // backward tile numbering: exclusive scan of H * ds_seq_tiles(L) over
     // the sequences, each thread a contiguous run of them
-    __shared__ int64_t run[kSchedThreads];
+    __shared__ int64_t run[kSchedThreads / kWave + 1];
     const int per = (B + kSchedThreads - 1) / kSchedThreads;
     const int b0 = threadIdx.x * per, b1 = b0 + per < B ? b0 + per : B;
     int64_t sum = 0;
     for (int b = b0; b < b1; ++b) sum += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
-    run[threadIdx.x] = sum;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-      const int64_t add = threadIdx.x >= off ? run[threadIdx.x - off] : 0;
-      __syncthreads();
-      run[threadIdx.x] += add;
-      __syncthreads();
-    }
-    int64_t at = threadIdx.x > 0 ? run[threadIdx.x - 1] : 0;
+    int64_t tiles;
+    int64_t at = block_scan_one(sum, run, &tiles);
     for (int b = b0; b < b1; ++b) {
       p.tile_base[b] = at;
       at += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
     }
     if (threadIdx.x == kSchedThreads - 1) {
-      const int64_t tiles = run[kSchedThreads - 1];
       if (p.ds_on) *p.ds_on = tiles <= p.ds_cap ? 1 : 0;
       if (p.det_on) *p.det_on = tiles <= p.part_cap ? 1 : 0;
     }
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(kBktThreads) void bucketize_kernel(AttnParams p, co
 __global__ __launch_bounds__(kSchedThreads) void pair_offsets_kernel(const int64_t* seq_offsets,
                                                                      const int64_t* num_targets, int B,
                                                                      int64_t* out) {
-  __shared__ int64_t lds[kSchedThreads];
+  __shared__ int64_t lds[kSchedThreads / kWave + 1];
   int64_t carry = 0;
   for (int base = 0; base < B; base += blockDim.x) {
     const int idx = base + threadIdx.x;
@@ -366,17 +386,10 @@ __global__ __launch_bounds__(kSchedThreads) void pair_offsets_kernel(const int64
       seq_rows(seq_offsets, num_targets, idx, s, L, hist);
       v = pairs_of(L, hist);
     }
-    lds[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-      const int64_t add = threadIdx.x >= (unsigned)off ? lds[threadIdx.x - off] : 0;
-      __syncthreads();
-      lds[threadIdx.x] += add;
-      __syncthreads();
-    }
-    if (idx < B) out[idx] = carry + lds[threadIdx.x] - v;
-    carry += lds[blockDim.x - 1];
-    __syncthreads();
+    int64_t total;
+    const int64_t excl = block_scan_one(v, lds, &total);
+    if (idx < B) out[idx] = carry + excl;
+    carry += total;
   }
   if (threadIdx.x == 0) out[B] = carry;
 }
