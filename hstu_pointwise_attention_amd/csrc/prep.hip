@@ -309,14 +309,33 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
 
 // rab bucket export, laid out over the jagged lower triangle: sequence
 // after sequence, query row i, then key j ascending (history rows i < hist
-// see keys 0..i, candidate rows see the history and themselves). One
-// workgroup takes one query row at a time (grid-strided over the token
-// rows): the row's slots are one contiguous run of the export, and thread t
-// takes slots t, t + 256, ..., so that every load of key timestamps and
-// every store of bp and bt covers consecutive addresses across a wave.
-// Time buckets use 64-bit timestamp arithmetic, exact for any int64 pair.
+// see keys 0..i, candidate rows see the history and themselves).
+//
+// The kernel walks the export itself, not the rows. Each wave owns a run of
+// kBktSteps steps of 512 consecutive slots; lane l takes slots l, l + 64,
+// ..., l + 448 of a step, so that the key-timestamp loads of a step are
+// consecutive across the wave. The wave locates its run's first slot once
+// (binary search over pair_offsets, staged in LDS for batches of up to
+// kBktLdsSeqs sequences; the row in closed form, since history rows start
+// at i (i + 1) / 2 and candidate rows follow with hist + 1 slots each) and
+// then moves its position forward step by step in scalar registers. A step
+// that lies within one row and holds no candidate's self term (nearly all
+// of them for rows of a few thousand keys) is the fast path: position
+// buckets from one base value, time buckets from 32-bit differences (a step
+// where some |ts_i - ts_j| does not fit is redone in 64-bit arithmetic),
+// the next step's key timestamps loaded before this step's arithmetic, and
+// the step's buckets transposed through LDS so that each lane stores its 8
+// consecutive slots with one 16-byte (bp) and one 8-byte (bt) store. Other
+// steps (row ends, self terms, the export's last slots) and unaligned
+// outputs go slot by slot, with 64-bit bucket arithmetic, exact for any
+// int64 pair.
 constexpr int kBktThreads = 256;
+constexpr int kBktWaves = kBktThreads / kWave;
+constexpr int kBktSlots = 8;                       // slots per lane and step
+constexpr int kBktStep = kWave * kBktSlots;        // consecutive slots per step
+constexpr int kBktSteps = 8;                       // steps per wave run
 constexpr int kBktGrid = 16384;
+constexpr int kBktLdsSeqs = 2047;                  // pair_offsets in LDS up to this batch
 
 __device__ __forceinline__ int64_t pairs_of(int L, int hist) {
   return (int64_t)hist * (hist + 1) / 2 + (int64_t)(L - hist) * (hist + 1);
@@ -331,41 +350,169 @@ __device__ __forceinline__ void seq_rows(const int64_t* seq_offsets, const int64
   hist = L - nt;
 }
 
-__global__ __launch_bounds__(kBktThreads) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
-                                                                uint16_t* bp, uint8_t* bt) {
-  const int64_t T = p.seq_offsets[p.B] - p.seq_offsets[0];
-  const bool want_t = bt != nullptr;
-  const int last = p.n_time_buckets - 1;
-  for (int64_t r = blockIdx.x; r < T; r += gridDim.x) {
-    // the sequence of token row r: the last b whose first row is <= r (it
-    // is not empty, since r < T)
-    const int64_t tok = p.seq_offsets[0] + r;
-    int lo = 0, hi = p.B;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.seq_offsets[mid] <= tok) lo = mid; else hi = mid;
+// Row of local slot f of a sequence (0 <= f < its pairs) and the slot's key
+// index within that row.
+__device__ __forceinline__ void bkt_locate(int64_t f, int hist, int& i, int& k) {
+  const int64_t h2 = (int64_t)hist * (hist + 1) / 2;
+  if (f < h2) {
+    // the largest i with i (i + 1) / 2 <= f, from the square root and then
+    // corrected in integers
+    int64_t r = (int64_t)((sqrt(8.0 * (double)f + 1.0) - 1.0) * 0.5);
+    while (r * (r + 1) / 2 > f) --r;
+    while ((r + 1) * (r + 2) / 2 <= f) ++r;
+    i = (int)r;
+    k = (int)(f - r * (r + 1) / 2);
+  } else {
+    const int64_t c = (f - h2) / (hist + 1);
+    i = hist + (int)c;
+    k = (int)(f - h2 - c * (hist + 1));
+  }
+}
+
+// A position in the export: sequence b (first token s, L rows, hist history
+// rows), query row i, key slot k of that row.
+struct BktPos {
+  int b, L, hist, i, k;
+  int64_t s;
+  bool cand;                 // i >= hist
+  int n_r, p_i;              // slots of the row, position of its query
+  int64_t ts_i;              // timestamp of the row's query (when timestamps are read)
+};
+
+__device__ __forceinline__ void bkt_row(BktPos& q, const int64_t* ts) {
+  q.cand = q.i >= q.hist;
+  q.n_r = q.cand ? q.hist + 1 : q.i + 1;
+  q.p_i = q.cand ? q.hist : q.i;
+  q.ts_i = ts ? ts[q.s + q.i] : 0;
+}
+
+// Moves q forward by n slots (into later rows and sequences as needed; the
+// caller guarantees the target slot exists).
+__device__ __forceinline__ void bkt_advance(BktPos& q, int n, const AttnParams& p) {
+  q.k += n;
+  while (q.k >= q.n_r) {
+    q.k -= q.n_r;
+    if (++q.i >= q.L) {
+      do {
+        ++q.b;
+        seq_rows(p.seq_offsets, p.num_targets, q.b, q.s, q.L, q.hist);
+      } while (q.L == 0);
+      q.i = 0;
     }
-    int64_t s;
-    int L, hist;
-    seq_rows(p.seq_offsets, p.num_targets, lo, s, L, hist);
-    const int i = (int)(tok - s);
-    const bool cand = i >= hist;
-    const int n_r = cand ? hist + 1 : i + 1;           // keys of the row
-    const int p_i = cand ? hist : i;                   // position of the row
-    const int64_t base = pair_offsets[lo] +
-                         (cand ? (int64_t)hist * (hist + 1) / 2 + (int64_t)(i - hist) * (hist + 1)
-                               : (int64_t)i * (i + 1) / 2);
-    uint16_t* const bp_row = bp ? bp + base : nullptr;
-    uint8_t* const bt_row = want_t ? bt + base : nullptr;
-    const int64_t* const ts = p.timestamps + s;
-    const int64_t ti = want_t ? ts[i] : 0;
-    for (int k = threadIdx.x; k < n_r; k += kBktThreads) {
-      const int j = (cand && k == hist) ? i : k;
-      if (bp_row) bp_row[k] = (uint16_t)pos_bucket(j - p_i, p.max_len);
-      if (want_t) {
-        const int bkt = time_bucket_wide(ti, ts[j], last);
-        bt_row[k] = (uint8_t)bkt;
+    bkt_row(q, p.timestamps);
+  }
+}
+
+__global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
+                                                                uint16_t* bp, uint8_t* bt, int vec) {
+  __shared__ int64_t po_lds[kBktLdsSeqs + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t xp[kBktWaves][kBktStep];
+  __shared__ __attribute__((aligned(16))) uint8_t xt[kBktWaves][kBktStep];
+  const int B = p.B;
+  const bool in_lds = B <= kBktLdsSeqs;
+  if (in_lds)
+    for (int x = threadIdx.x; x <= B; x += kBktThreads) po_lds[x] = pair_offsets[x];
+  __syncthreads();
+  const int64_t* const po = in_lds ? po_lds : pair_offsets;
+  const int64_t P = po[B];
+  const bool want_p = bp != nullptr, want_t = bt != nullptr;
+  const int64_t* const tsg = want_t ? p.timestamps : nullptr;
+  const int lim = p.max_len - 1;
+  const int last = p.n_time_buckets - 1;
+  const int lane = threadIdx.x % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  for (int64_t c = (int64_t)blockIdx.x * kBktWaves + wv; c * kBktStep * kBktSteps < P;
+       c += (int64_t)gridDim.x * kBktWaves) {
+    int64_t F = c * kBktStep * kBktSteps;
+    // the run's first slot: the last b with po[b] <= F (it has pairs, since
+    // po[B] > F), then its row
+    BktPos q;
+    {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (po[mid] <= F) lo = mid; else hi = mid;
       }
+      q.b = lo;
+      seq_rows(p.seq_offsets, p.num_targets, q.b, q.s, q.L, q.hist);
+      bkt_locate(F - po[q.b], q.hist, q.i, q.k);
+      bkt_row(q, tsg);
+    }
+    int64_t tj[kBktSlots];
+    bool have = false;                             // tj holds this step's key timestamps
+    for (int st = 0; st < kBktSteps && F < P; ++st, F += kBktStep) {
+      const int keys = q.cand ? q.hist : q.n_r;    // keys of the row before a self term
+      if (vec && F + kBktStep <= P && q.k + kBktStep <= keys) {
+        // the step's 512 slots are keys k .. k + 511 of one row
+        int64_t cur[kBktSlots];
+        if (want_t) {
+          if (!have) {
+            const int64_t* tk = tsg + q.s + q.k + lane;
+#pragma unroll
+            for (int m = 0; m < kBktSlots; ++m) tj[m] = tk[kWave * m];
+          }
+#pragma unroll
+          for (int m = 0; m < kBktSlots; ++m) cur[m] = tj[m];
+          // the next step's keys, when it stays in this row
+          have = st + 1 < kBktSteps && F + 2 * kBktStep <= P && q.k + 2 * kBktStep <= keys;
+          if (have) {
+            const int64_t* tk = tsg + q.s + q.k + kBktStep + lane;
+#pragma unroll
+            for (int m = 0; m < kBktSlots; ++m) tj[m] = tk[kWave * m];
+          }
+          // d = ts_i - ts_j from 32-bit halves; it fits in 32 bits iff its
+          // high word is the sign of its low word, and then |d| <= 2^31
+          const uint32_t til = (uint32_t)q.ts_i, tih = (uint32_t)((uint64_t)q.ts_i >> 32);
+          bool wide = false;
+          uint32_t ev[kBktSlots];
+#pragma unroll
+          for (int m = 0; m < kBktSlots; ++m) {
+            const uint32_t cl = (uint32_t)cur[m], chi = (uint32_t)((uint64_t)cur[m] >> 32);
+            const uint32_t dl = til - cl;
+            const uint32_t dh = tih - chi - (til < cl ? 1u : 0u);
+            wide = wide || (int32_t)dh != ((int32_t)dl >> 31);
+            const int32_t sd = (int32_t)dl;
+            const uint32_t a = (uint32_t)max(sd, -sd) + 1u;
+            const int e = 31 - __builtin_clz(a);
+            ev[m] = (uint32_t)(e < last ? e : last);
+          }
+          if (__builtin_amdgcn_ballot_w64(wide) != 0) {
+#pragma unroll
+            for (int m = 0; m < kBktSlots; ++m) ev[m] = (uint32_t)time_bucket_wide(q.ts_i, cur[m], last);
+          }
+#pragma unroll
+          for (int m = 0; m < kBktSlots; ++m) xt[wv][lane + kWave * m] = (uint8_t)ev[m];
+        }
+        if (want_p) {
+          // keys k + o of the row sit at k + o - p_i <= 0: the bucket is
+          // max(k + o - p_i + lim, 0)
+          const int pbase = q.k - q.p_i + lim + lane;
+#pragma unroll
+          for (int m = 0; m < kBktSlots; ++m) xp[wv][lane + kWave * m] = (uint16_t)max(pbase + kWave * m, 0);
+        }
+        // lane l's slots 8 l .. 8 l + 7 of the step: one store each
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t g = F + kBktSlots * lane;
+        if (want_t) *reinterpret_cast<uint2*>(bt + g) = *reinterpret_cast<const uint2*>(&xt[wv][kBktSlots * lane]);
+        if (want_p) st16(bp + g, *reinterpret_cast<const u32x4*>(&xp[wv][kBktSlots * lane]));
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        // slot by slot: lane l from slot F + l, then 64 slots on each time
+        have = false;
+        BktPos r = q;
+        const int nv = (int)min((int64_t)kBktSlots, (P - F - lane + kWave - 1) / kWave);
+        for (int m = 0; m < nv; ++m) {
+          bkt_advance(r, m == 0 ? lane : kWave, p);
+          const int j = (r.cand && r.k == r.hist) ? r.i : r.k;
+          const int64_t f = F + lane + kWave * m;
+          if (want_p) bp[f] = (uint16_t)pos_bucket(j - r.p_i, p.max_len);
+          if (want_t) bt[f] = (uint8_t)time_bucket_wide(r.ts_i, tsg[r.s + j], last);
+        }
+      }
+      if (F + kBktStep < P) bkt_advance(q, kBktStep, p);
     }
   }
 }
@@ -603,8 +750,10 @@ hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, ui
                             uint8_t* bt, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   prof_before(kKBucketize, s);
+  // the fast path stores 8 slots per lane: 16 bytes of bp, 8 of bt
+  const int vec = ((uintptr_t)bp % 16 == 0) && ((uintptr_t)bt % 8 == 0);
   hipLaunchKernelGGL(bucketize_kernel, dim3(kBktGrid), dim3(kBktThreads), 0, s, p, pair_offsets,
-                     bp, bt);
+                     bp, bt, vec);
   prof_after(kKBucketize, s);
   return hipGetLastError();
 }

@@ -82,6 +82,76 @@ def test_bucketize_edge_timestamps():
             _bucket_case(inp, nb)
 
 
+def test_bucketize_long_rows_mixed():
+    """Rows longer than a wave's 64 slots and shorter ones in one batch:
+    position buckets clamped (max_len well below the lengths), unsorted
+    timestamps, a sequence whose span needs 64-bit arithmetic in the middle
+    of long rows, candidates, and empty sequences."""
+    rng = np.random.default_rng(11)
+    lengths = np.array([300, 0, 517, 64, 1, 260])
+    offs = W.offsets_from_lengths(lengths)
+    T = int(offs[-1])
+    ts = rng.integers(-10 ** 8, 10 ** 8, size=T).astype(np.int64)      # unsorted, spans < 2^31
+    s3 = int(offs[2])
+    ts[s3 + 200:s3 + 240] += np.int64(3) << 33                          # |dt| > 2^31 for some pairs
+    ts[int(offs[5]) + 17] = np.iinfo(np.int64).min                      # extreme value in a long row
+    for max_len, nt in ((50, [5, 0, 40, 0, 1, 100]), (1024, [0, 0, 0, 64, 0, 0])):
+        inp = dict(seq_offsets=offs, num_targets=np.array(nt), timestamps=ts, max_len=max_len,
+                   dtype="fp32")
+        for nb in (9, 128):
+            _bucket_case(inp, nb)
+
+
+def test_bucketize_many_sequences():
+    """More sequences than the kernel stages in LDS (its search then reads
+    pair_offsets from memory)."""
+    rng = np.random.default_rng(12)
+    lengths = rng.integers(0, 40, size=2600)
+    offs = W.offsets_from_lengths(lengths)
+    T = int(offs[-1])
+    inp = dict(seq_offsets=offs, num_targets=np.minimum(rng.integers(0, 5, size=lengths.size), lengths),
+               timestamps=np.cumsum(rng.integers(0, 5000, size=T)).astype(np.int64), max_len=40,
+               dtype="fp32")
+    _bucket_case(inp, 16)
+
+
+def test_bucketize_unaligned_outputs():
+    """Outputs that start off a 16-byte boundary give the same buckets,
+    written only inside their ranges."""
+    import torch
+    from hstu_pointwise_attention_amd import _lib, ops
+    inp = W.make_attention_inputs(W.LONG)
+    dev = P.to_dev(inp)
+    nb = W.LONG.n_time_buckets
+    bp_ref, bt_ref = ops.rab_bucketize(dev["seq_offsets"], inp["max_len"], num_targets=dev["num_targets"],
+                                       timestamps=dev["timestamps"], n_time_buckets=nb)
+    n = bp_ref.numel()
+
+    def vp(t, byte_shift=0):
+        return ctypes.c_void_p(None if t is None else t.data_ptr() + byte_shift)
+
+    lib = _lib.load()
+    d = _lib.AttnDesc()
+    d.batch = inp["seq_offsets"].size - 1
+    d.heads = 1
+    d.max_len = int(inp["max_len"])
+    d.n_time_buckets = nb
+    po = torch.empty(d.batch + 1, dtype=torch.int64, device="cuda")
+    _lib.check(lib.hstu_rab_pair_offsets(ctypes.byref(d), vp(dev["seq_offsets"]), vp(dev["num_targets"]),
+                                         vp(po), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    for shift in (1, 3):
+        bp = torch.full((n + 8,), 0x5A5A, dtype=torch.int16, device="cuda")
+        bt = torch.full((n + 8,), 0xA5, dtype=torch.uint8, device="cuda")
+        _lib.check(lib.hstu_rab_bucketize(ctypes.byref(d), vp(dev["seq_offsets"]), vp(dev["num_targets"]),
+                                          vp(dev["timestamps"]), vp(po), vp(bp, 2 * shift), vp(bt, shift),
+                                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        torch.cuda.synchronize()
+        assert torch.equal(bp[shift:shift + n].view(torch.uint16), bp_ref)
+        assert torch.equal(bt[shift:shift + n], bt_ref)
+        assert bool((bp[:shift] == 0x5A5A).all()) and bool((bp[shift + n:] == 0x5A5A).all())
+        assert bool((bt[:shift] == 0xA5).all()) and bool((bt[shift + n:] == 0xA5).all())
+
+
 def test_pair_offsets_match_oracle():
     """hstu_rab_pair_offsets: exclusive sums of each sequence's unmasked pairs
     (counted on the oracle's mask), with empty sequences, candidates, and more
