@@ -201,7 +201,9 @@ def main():
                    "flops_per_step": fl["total"],
                    "rab": f"position {2 * wl.max_len - 1 if wl.use_pos_bias else 0} + time "
                           f"{wl.n_time_buckets} buckets"},
-        "dq_path": "dS export" if info["dq_from_ds"] else "recompute dS",
+        "dq_path": ("dS export" if info["dq_from_ds"] else
+                    "recompute dS" if info["ds_sequences"] == 0 else
+                    f"dS export for the first {info['ds_sequences']} sequences, recompute dS for the rest"),
         "context": {"pages_claim": PAGES_CLAIM},
         "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
         "attention_kernels": per_kernel,

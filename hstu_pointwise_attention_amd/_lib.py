@@ -61,7 +61,8 @@ class AttnDesc(ctypes.Structure):
 
 
 class BwdInfo(ctypes.Structure):
-    _fields_ = [("dq_from_ds", ctypes.c_int32), ("rab_deterministic", ctypes.c_int32)]
+    _fields_ = [("dq_from_ds", ctypes.c_int32), ("rab_deterministic", ctypes.c_int32),
+                ("ds_sequences", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p

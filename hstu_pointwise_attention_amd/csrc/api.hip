@@ -733,6 +733,7 @@ hstu_status hstu_attn_bwd_report(const hstu_attn_desc* desc, const void* workspa
   carve_workspace(p, const_cast<void*>(workspace), true, eb, ds_room);
   info->dq_from_ds = 0;
   info->rab_deterministic = 0;
+  info->ds_sequences = 0;
   if (p.T == 0 || p.B == 0) {
     info->rab_deterministic = p.det;             // nothing summed: trivially repeatable
     return ok();
@@ -743,7 +744,9 @@ hstu_status hstu_attn_bwd_report(const hstu_attn_desc* desc, const void* workspa
   const int32_t* dev_flags = p.ds_on ? p.ds_on : (p.det_on ? p.det_on - 1 : nullptr);
   if (e == hipSuccess && dev_flags) e = hipMemcpy(flags, dev_flags, sizeof(flags), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hstu_attn_bwd_report");
-  info->dq_from_ds = p.ds_on ? flags[0] : 0;
+  // flags[0]: the leading sequences whose dS tiles fit the room
+  info->ds_sequences = p.ds_on ? flags[0] : 0;
+  info->dq_from_ds = info->ds_sequences == p.B ? 1 : 0;
   info->rab_deterministic = p.det_on ? flags[1] : 0;
   return ok();
 }

@@ -180,7 +180,7 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
   // reads zeros instead.
   static_assert(C::BN == kDsKeys && C::BM == kDsQueries, "dS tile shape");
   bf16* ds_row = nullptr;
-  if (p.ds != nullptr && *p.ds_on != 0)
+  if (p.ds != nullptr && wi.seq < *p.ds_on)
     ds_row = reinterpret_cast<bf16*>(p.ds) +
              (p.tile_base[wi.seq] + (int64_t)head * ds_seq_tiles(L) + ds_row_start(L, wi.blk)) * kDsTile;
   const int ds_lane = jl * kDsQueries + 8 * q4;

@@ -36,12 +36,14 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
 
 template <int D>
 __global__ __launch_bounds__(256) void dq_ds_kernel(AttnParams p) {
-  if (*p.ds_on == 0) return;                     // the recompute pass runs instead
+  const int n_ds = *p.ds_on;                     // leading sequences with exported tiles
+  if (n_ds == 0) return;                         // the recompute pass runs instead
   __shared__ GemmSmem sm;
   const int item = blockIdx.x / p.H;
   const int head = blockIdx.x - item * p.H;
   if (item >= *p.n_items) return;
   const WorkItem wi = p.items[item];
+  if (wi.seq >= n_ds) return;                    // its dS was not exported: recomputed
   const SeqInfo si = p.seq[wi.seq];
   const int L = si.len;
   const int64_t start = si.start;

@@ -685,7 +685,9 @@ void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
   using C = FwdCfg<T, D, true>;
   HSTU_FWD_TILE_BUFFERS(C)
-  if (p.ds_on != nullptr && *p.ds_on != 0) return;   // dQ comes from the exported dS tiles
+  // sequences below n_ds take dQ from their exported dS tiles
+  const int n_ds = p.ds_on != nullptr ? *p.ds_on : 0;
+  if (n_ds >= p.B) return;
   if constexpr (WIDE) {
     // sequences needing 64-bit timestamps are rare: a small grid walks the
     // work slots and takes only theirs
@@ -695,6 +697,7 @@ void hstu_dq_kernel(AttnParams p) {
       const int item = (int)(w / p.H);
       const int head = (int)(w - (int64_t)item * p.H);
       const WorkItem wi = p.items[item];
+      if (wi.seq < n_ds) continue;
       const SeqInfo si = p.seq[wi.seq];
       if ((si.flags & kSeqWideTs) == 0) continue;
       fwd_body<T, D, true, POS, TIME, true>(p, sm, kvb, wi, si, head);
@@ -705,6 +708,7 @@ void hstu_dq_kernel(AttnParams p) {
     const int head = blockIdx.x - item * p.H;
     if (item >= *p.n_items) return;
     const WorkItem wi = p.items[item];
+    if (wi.seq < n_ds) return;
     const SeqInfo si = p.seq[wi.seq];
     if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
     fwd_body<T, D, false, POS, TIME, true>(p, sm, kvb, wi, si, head);

@@ -62,8 +62,9 @@ struct AttnParams {
   int64_t* tile_base;                // [B]
   int32_t* blk_base;                 // [B + 1]
   // dS export (bf16 backward; ds null: the dQ pass recomputes dS): storage
-  // of ds_cap tiles; the schedule kernel sets *ds_on to 1 when the batch's
-  // tiles fit, else 0 (the recompute pass runs)
+  // of ds_cap tiles. The schedule kernel sets *ds_on to the number of
+  // leading sequences whose tiles fit (all B when the batch's do): those
+  // export dS and take dq_ds_kernel, the rest take the recompute pass
   void* ds;
   int64_t ds_cap;
   int32_t* ds_on;

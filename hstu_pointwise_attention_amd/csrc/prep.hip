@@ -290,18 +290,22 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     // backward tile numbering: exclusive scan of H * ds_seq_tiles(L) over
     // the sequences, each thread a contiguous run of them
     __shared__ int64_t run[kSchedThreads / kWave + 1];
+    __shared__ int cut;                          // first sequence whose tiles overflow ds_cap
+    if (threadIdx.x == 0) cut = B;
     const int per = (B + kSchedThreads - 1) / kSchedThreads;
     const int b0 = threadIdx.x * per, b1 = b0 + per < B ? b0 + per : B;
     int64_t sum = 0;
     for (int b = b0; b < b1; ++b) sum += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
     int64_t tiles;
-    int64_t at = block_scan_one(sum, run, &tiles);
+    int64_t at = block_scan_one(sum, run, &tiles);   // (ends with a barrier)
     for (int b = b0; b < b1; ++b) {
       p.tile_base[b] = at;
       at += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
+      if (at > p.ds_cap) atomicMin(&cut, b);
     }
+    __syncthreads();
     if (threadIdx.x == kSchedThreads - 1) {
-      if (p.ds_on) *p.ds_on = tiles <= p.ds_cap ? 1 : 0;
+      if (p.ds_on) *p.ds_on = cut;
       if (p.det_on) *p.det_on = tiles <= p.part_cap ? 1 : 0;
     }
   }

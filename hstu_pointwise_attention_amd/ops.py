@@ -174,7 +174,8 @@ def attn_bwd(q, k, v, u, seq_offsets, max_len, a_saved, d_o, *, num_targets=None
         _lib.check(lib.hstu_attn_bwd_report(ctypes.byref(desc), _ptr(ws), nbytes.value,
                                             ctypes.byref(info), _stream()))
         out["info"] = {"dq_from_ds": bool(info.dq_from_ds),
-                       "rab_deterministic": bool(info.rab_deterministic)}
+                       "rab_deterministic": bool(info.rab_deterministic),
+                       "ds_sequences": int(info.ds_sequences)}
     return out
 
 

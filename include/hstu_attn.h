@@ -104,10 +104,12 @@ typedef struct {
  * tiles, at most 4 GiB (about 1.5 GB for 8 sequences of up to 8192 rows, 4
  * heads). That room is O(sum of L^2) bytes.
  * hstu_attn_bwd uses the dS export when workspace_bytes reaches the preferred
- * figure and the batch's tiles fit; otherwise it computes dQ by recomputing dS
- * per query block (the same results; measured about 1.7x the dQ time at 8
+ * figure, for the leading sequences whose tiles fit that room (all of them
+ * when no sequence is longer than max_len and the 4 GiB cap is not reached);
+ * for the others, and without the room, it computes dQ by recomputing dS per
+ * query block (the same results; measured about 1.7x the dQ time at 8
  * sequences of 4096..8192 rows, 4 heads, head dim 128).
- * hstu_attn_bwd_report tells which ran.
+ * hstu_attn_bwd_report tells how many sequences took the export.
  */
 HSTU_API hstu_status hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
 HSTU_API hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc, size_t* bytes);
@@ -241,13 +243,20 @@ HSTU_API hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* se
  * What the last hstu_attn_bwd on this workspace did (for checking and
  * reporting; it waits for `stream`, then reads two flags the call left in the
  * workspace). desc, workspace and workspace_bytes as passed to that call.
- *  dq_from_ds         1: dQ came from the exported dS tiles; 0: dQ came
- *                     from the pass that recomputes dS (no room, or fp32)
+ *  dq_from_ds         1: every sequence's dQ came from the exported dS
+ *                     tiles; 0: at least one sequence's dQ came from the
+ *                     pass that recomputes dS
  *  rab_deterministic  1: the rab gradients were summed in a fixed order
+ *  ds_sequences       how many leading sequences (0 .. batch) took the dS
+ *                     export: the tiles of sequences 0 .. n-1 fit the room
+ *                     the workspace holds and the rest did not (sequences
+ *                     longer than max_len, or a batch beyond the room's
+ *                     4 GiB cap); 0 without room, or in fp32
  */
 typedef struct {
   int32_t dq_from_ds;
   int32_t rab_deterministic;
+  int32_t ds_sequences;
 } hstu_attn_bwd_info;
 HSTU_API hstu_status hstu_attn_bwd_report(const hstu_attn_desc* desc, const void* workspace,
                                           size_t workspace_bytes, hstu_attn_bwd_info* info,
@@ -371,8 +380,9 @@ HSTU_API hstu_status hstu_layernorm_gate_fp8(int64_t M, int64_t N, const float* 
  *   max_len: a bound on every sequence's length, or 0 for none. It sizes
  *   the attention backward's exported dS tiles (about
  *   H (ceil(max_len / 128) + 1) (M / 128 + batch) tiles of 16 KB, at most
- *   4 GiB); with 0, or for a batch whose tiles exceed that room, the
- *   attention backward recomputes dS for dQ instead (same results).
+ *   4 GiB); with 0 the attention backward recomputes dS for dQ instead
+ *   (same results), and so it does for the sequences whose tiles do not fit
+ *   the room after those of the sequences before them.
  *   workspace (device) >= hstu_layer_bwd_workspace_size bytes (same sizes
  *   and max_len), 256-aligned.
  *   Every reduction runs in a fixed order (no atomics: this attention has no

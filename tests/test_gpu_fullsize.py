@@ -150,7 +150,8 @@ def test_efficiency_deterministic(eff_inputs, eff_rab_oracle):
                          A, dev["d_o"], timestamps=dev["timestamps"], rab_pos=dev["rab_pos"],
                          rab_time=dev["rab_time"], deterministic=True, report=True)
         torch.cuda.synchronize()
-        assert g["info"] == {"dq_from_ds": True, "rab_deterministic": True}, g["info"]
+        assert g["info"] == {"dq_from_ds": True, "rab_deterministic": True,
+                             "ds_sequences": len(inp["lengths"])}, g["info"]
         runs.append({k: v.clone() for k, v in g.items() if k != "info"})
     for key in runs[0]:
         assert torch.equal(runs[0][key], runs[1][key]), key

@@ -340,27 +340,30 @@ def test_autograd_function_matches_ops():
 
 def test_bf16_dq_paths_agree():
     """The bf16 backward computes dQ from the key-block kernel's exported dS
-    tiles when the workspace holds their room and the batch's tiles fit it,
-    and by recomputing dS otherwise. Without a position bias max_len changes
-    nothing else, so the same inputs run three ways: lengths 300, 200, 77 with
-    H 2 hold 2 * (9 + 6 + 2) = 34 tiles; max_len 512 sizes room for
-    2 * 5 * 7 = 70 (export), max_len 64 for 2 * 2 * 7 = 28 (recompute: the
-    tiles do not fit), and the minimum workspace has no room (recompute). The
-    report names the path each time; all match the oracle and each other."""
+    tiles for the leading sequences whose tiles fit the room the workspace
+    holds, and by recomputing dS for the others. Without a position bias
+    max_len changes nothing else, so the same inputs run three ways: lengths
+    300, 200, 77 with H 2 hold 2 * 9 + 2 * 6 + 2 * 2 = 34 tiles; max_len 512
+    sizes room for 2 * 5 * 7 = 70 (every sequence exports), max_len 64 for
+    2 * 2 * 7 = 28 (the first sequence's 18 tiles fit, the second's would end
+    at 30: one sequence exports, two recompute), and the minimum workspace
+    has no room (all recompute). The report names the split each time; all
+    match the oracle and each other."""
     lengths = (300, 200, 77)
     w = W.AttnWorkload("dqpaths", 41, 3, 2, 64, 64, 512, 16, False, "bf16", "fixed", lengths)
     inp = W.make_attention_inputs(w)
     inp["num_targets"] = np.array([20, 0, 5], np.int64)
     want = P.oracle_bwd(inp)
     got = {}
-    for name, max_len, room, from_ds in (("export", 512, True, True), ("no fit", 64, True, False),
-                                         ("min workspace", 512, False, False)):
+    for name, max_len, room, n_ds in (("export", 512, True, 3), ("partial fit", 64, True, 1),
+                                      ("min workspace", 512, False, 0)):
         run = dict(inp, max_len=max_len)
         _, A = P.gpu_fwd(run)
         got[name] = P.gpu_bwd(run, A, ds_room=room, report=True)
-        assert got[name]["info"]["dq_from_ds"] is from_ds, (name, got[name]["info"])
+        info = got[name]["info"]
+        assert info["ds_sequences"] == n_ds and info["dq_from_ds"] is (n_ds == 3), (name, info)
         P.check_bwd(run, got[name], want, name)
-    for name in ("no fit", "min workspace"):
+    for name in ("partial fit", "min workspace"):
         assert P.rel_l2(P.host(got["export"]["dq"]), P.host(got[name]["dq"])) <= P.BF16_REL
 
 
