@@ -65,9 +65,7 @@ hstu_status check_desc(const hstu_attn_desc* d) {
     return fail(HSTU_EINVAL, "unknown dtype %d", d->dtype);
   if (d->d_qk != d->d_v)
     return fail(HSTU_EUNSUPPORTED, "d_qk (%d) != d_v (%d) is not supported", d->d_qk, d->d_v);
-  const bool dim_ok = d->dtype == HSTU_DTYPE_BF16
-                          ? (d->d_qk == 32 || d->d_qk == 64 || d->d_qk == 128)
-                          : (d->d_qk == 32 || d->d_qk == 64);
+  const bool dim_ok = d->d_qk == 32 || d->d_qk == 64 || d->d_qk == 128;
   if (!dim_ok)
     return fail(HSTU_EUNSUPPORTED, "head dim %d is not supported for dtype %d", d->d_qk, d->dtype);
   if (d->max_len < 1 || d->max_len > (1 << 30)) return fail(HSTU_EINVAL, "max_len %d out of range", d->max_len);
@@ -147,6 +145,7 @@ hipError_t dispatch_fwd(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_fwd<T, 32>(p, s);
     case 64: return launch_fwd<T, 64>(p, s);
+    case 128: return launch_fwd<T, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -165,6 +164,7 @@ hipError_t dispatch_fwd_cand(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_fwd_cand<T, 32>(p, s);
     case 64: return launch_fwd_cand<T, 64>(p, s);
+    case 128: return launch_fwd_cand<T, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -194,6 +194,7 @@ hipError_t dispatch_bwd(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_bwd<T, 32>(p, s);
     case 64: return launch_bwd<T, 64>(p, s);
+    case 128: return launch_bwd<T, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -212,6 +213,7 @@ hipError_t dispatch_dq(const AttnParams& p, hipStream_t s) {
   switch (p.D) {
     case 32: return launch_dq<T, 32>(p, s);
     case 64: return launch_dq<T, 64>(p, s);
+    case 128: return launch_dq<T, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -35,6 +35,7 @@ namespace {
 template <typename T, int D> struct BwdLd;
 template <> struct BwdLd<float, 32> { static constexpr int Q = 36; };
 template <> struct BwdLd<float, 64> { static constexpr int Q = 68; };
+template <> struct BwdLd<float, 128> { static constexpr int Q = 132; };
 
 template <typename T, int D>
 struct BwdCfg {
@@ -648,5 +649,6 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
 
 template hipError_t launch_bwd<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_bwd<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd<float, 128>(const AttnParams&, hipStream_t);
 
 }  // namespace hstu

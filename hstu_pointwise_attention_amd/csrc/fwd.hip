@@ -37,6 +37,14 @@ template <> struct FwdLd<bf16, 64> { static constexpr int K = 72, V = 72; static
 template <> struct FwdLd<bf16, 128> { static constexpr int K = 136, V = 136; static constexpr bool P = true; };
 template <> struct FwdLd<float, 32> { static constexpr int K = 36, V = 36; static constexpr bool P = false; };
 template <> struct FwdLd<float, 64> { static constexpr int K = 68, V = 68; static constexpr bool P = false; };
+template <> struct FwdLd<float, 128> { static constexpr int K = 132, V = 132; static constexpr bool P = false; };
+
+// Waves per SIMD the tile kernels are built for: two, except fp32 at head
+// dim 128, whose resident Q (and dA') fragments and O (dQ) accumulators
+// alone take 128 (256) registers, and whose K/V tiles fill the LDS of one
+// workgroup per compute unit.
+template <typename T, int D> struct FwdOcc { static constexpr int W = 2; };
+template <> struct FwdOcc<float, 128> { static constexpr int W = 1; };
 
 // P: the tile read by transposed reads (V forward, K gradient) stores row r
 // at row_perm(r), which swaps the two 2-bit fields of r's low four bits.
@@ -591,7 +599,7 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
   using C = FwdCfg<T, D, false>;
@@ -622,7 +630,7 @@ void hstu_fwd_kernel(AttnParams p) {
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_fwd_cand_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
   __shared__ FwdKV<T, D, false> kv;
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(256) void cand_finish_kernel(AttnParams p) {
 }
 
 template <typename T, int D, bool WIDE, bool POS, bool TIME>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
   using C = FwdCfg<T, D, true>;
@@ -774,15 +782,18 @@ template hipError_t launch_fwd<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd<float, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd_cand<bf16, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd_cand<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd_cand<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd_cand<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_fwd_cand<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_fwd_cand<float, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 64>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<bf16, 128>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<float, 32>(const AttnParams&, hipStream_t);
 template hipError_t launch_dq<float, 64>(const AttnParams&, hipStream_t);
+template hipError_t launch_dq<float, 128>(const AttnParams&, hipStream_t);
 
 }  // namespace hstu

@@ -76,7 +76,7 @@ typedef enum {
 typedef struct {
   int32_t batch;           /* B >= 0 sequences                                   */
   int32_t heads;           /* H >= 1                                             */
-  int32_t d_qk;            /* head dim of Q, K: 32, 64 or 128 (bf16); 32, 64 (fp32) */
+  int32_t d_qk;            /* head dim of Q, K: 32, 64 or 128                  */
   int32_t d_v;             /* head dim of V, U, O: must equal d_qk               */
   int32_t max_len;         /* >= 1; rab_pos holds 2*max_len-1 buckets            */
   int32_t n_time_buckets;  /* entries per rab_time row (0: no time bias), <= 1024 */

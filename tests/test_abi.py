@@ -72,12 +72,6 @@ def test_desc_validation(lib, field, value, status):
     assert lib.hstu_last_error().decode()
 
 
-def test_fp32_d128_unsupported(lib):
-    d = good_desc(d_qk=128, d_v=128, dtype=_lib.DTYPE_FP32, stride_q=256, stride_k=256,
-                  stride_v=256, stride_u=256)
-    assert fwd_call(lib, d) == _lib.HSTU_EUNSUPPORTED
-
-
 def test_missing_inputs(lib):
     d = good_desc()
     assert fwd_call(lib, d, timestamps=None) == _lib.HSTU_EINVAL          # time bias without ts

@@ -111,7 +111,7 @@ def test_cached_random(dtype, seed):
     rng = np.random.default_rng(2000 + seed)
     B = int(rng.integers(1, 5))
     H = int(rng.choice([1, 2, 4]))
-    D = int(rng.choice([32, 64] if dtype == "fp32" else [32, 64, 128]))
+    D = int(rng.choice([32, 64, 128]))
     hist = rng.integers(0, 301, size=B)
     n_cand = rng.integers(0, 41, size=B)
     n_cand[rng.integers(B)] = int(rng.integers(1, 41))

@@ -194,13 +194,26 @@ def test_workload_parity(w):
     _run_parity(W.make_attention_inputs(w), tag=w.name)
 
 
+@pytest.mark.parametrize("pos,time", [(True, True), (False, False)])
+def test_fp32_head_dim_128(pos, time):
+    """fp32 at head dim 128 (one wave per SIMD in its tile kernels): several
+    query and key blocks, a ragged last block, candidates, an empty and a
+    one-row sequence, within the fp32 tolerance of the oracle."""
+    lengths = (300, 0, 1, 129, 257)
+    w = W.AttnWorkload("fp32d128", 61, len(lengths), 2, 128, 128, 320, 64 if time else 0, pos,
+                       "fp32", "fixed", lengths)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.array([30, 0, 1, 0, 7], np.int64)
+    _run_parity(inp, tag=f"fp32 D128 pos={pos} time={time}")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("seed", range(6))
 def test_random_small_sweep(dtype, seed):
     """Random small shapes over tile edges: lengths 0..300, H, D, rab and targets varied."""
     rng = np.random.default_rng(1000 + seed)
     H = int(rng.choice([1, 2, 4]))
-    D = int(rng.choice([32, 64] if dtype == "fp32" else [32, 64, 128]))
+    D = int(rng.choice([32, 64, 128]))
     B = int(rng.integers(1, 6))
     max_len = int(rng.choice([16, 64, 300]))
     nb = int(rng.choice([0, 16, 128]))
@@ -246,7 +259,7 @@ def test_timestamp_kinds(dtype, kind):
     negative, spans past 2^31 (the 64-bit bucket kernels), extreme int64 values, all ties, a
     value more than 2^30 s before the first one, and a batch mixing both kernel kinds."""
     lengths = (5, 0, 70, 1, 130, 200)
-    D = 64 if dtype == "fp32" else 128
+    D = 128
     w = W.AttnWorkload("tskinds", 31, len(lengths), 2, D, D, 256, 128, True, dtype, "fixed",
                        lengths)
     inp = W.make_attention_inputs(w)
@@ -393,7 +406,7 @@ def _det_case(name):
     # candidates with both tables (the position window path), 64-bit timestamps
     # in every other sequence, per-head tables, fp32 and bf16
     dtype = "fp32" if name.endswith("fp32") else "bf16"
-    D = 64 if dtype == "fp32" else 128
+    D = 128
     lengths = (130, 0, 70, 200, 1, 65)
     w = W.AttnWorkload("det", 51, len(lengths), 2, D, D, 160, 64, True, dtype, "fixed", lengths,
                        rab_heads=2)
