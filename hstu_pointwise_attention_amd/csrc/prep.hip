@@ -316,7 +316,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
 // see keys 0..i, candidate rows see the history and themselves).
 //
 // The kernel walks the export itself, not the rows. Each wave owns a run of
-// kBktSteps steps of 512 consecutive slots; lane l takes slots l, l + 64,
+// up to kBktSteps steps of 512 consecutive slots (fewer for exports too
+// small to give every wave of the grid a full run); lane l takes slots l, l + 64,
 // ..., l + 448 of a step, so that the key-timestamp loads of a step are
 // consecutive across the wave. The wave locates its run's first slot once
 // (binary search over pair_offsets, staged in LDS for batches of up to
@@ -337,7 +338,7 @@ constexpr int kBktThreads = 256;
 constexpr int kBktWaves = kBktThreads / kWave;
 constexpr int kBktSlots = 8;                       // slots per lane and step
 constexpr int kBktStep = kWave * kBktSlots;        // consecutive slots per step
-constexpr int kBktSteps = 8;                       // steps per wave run
+constexpr int kBktSteps = 8;                       // most steps per wave run
 constexpr int kBktGrid = 16384;
 constexpr int kBktLdsSeqs = 2047;                  // pair_offsets in LDS up to this batch
 
@@ -426,9 +427,13 @@ __global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))
   const int lane = threadIdx.x % kWave;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  for (int64_t c = (int64_t)blockIdx.x * kBktWaves + wv; c * kBktStep * kBktSteps < P;
-       c += (int64_t)gridDim.x * kBktWaves) {
-    int64_t F = c * kBktStep * kBktSteps;
+  // steps per run: up to kBktSteps, fewer when the export is too small to
+  // give every wave of the grid a run of that length
+  const int64_t waves = (int64_t)gridDim.x * kBktWaves;
+  const int64_t fill = (P + kBktStep * waves - 1) / (kBktStep * waves);
+  const int steps = (int)(fill < kBktSteps ? (fill > 1 ? fill : 1) : kBktSteps);
+  for (int64_t c = (int64_t)blockIdx.x * kBktWaves + wv; c * kBktStep * steps < P; c += waves) {
+    int64_t F = c * kBktStep * steps;
     // the run's first slot: the last b with po[b] <= F (it has pairs, since
     // po[B] > F), then its row
     BktPos q;
@@ -445,7 +450,7 @@ __global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))
     }
     int64_t tj[kBktSlots];
     bool have = false;                             // tj holds this step's key timestamps
-    for (int st = 0; st < kBktSteps && F < P; ++st, F += kBktStep) {
+    for (int st = 0; st < steps && F < P; ++st, F += kBktStep) {
       const int keys = q.cand ? q.hist : q.n_r;    // keys of the row before a self term
       if (vec && F + kBktStep <= P && q.k + kBktStep <= keys) {
         // the step's 512 slots are keys k .. k + 511 of one row
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))
 #pragma unroll
           for (int m = 0; m < kBktSlots; ++m) cur[m] = tj[m];
           // the next step's keys, when it stays in this row
-          have = st + 1 < kBktSteps && F + 2 * kBktStep <= P && q.k + 2 * kBktStep <= keys;
+          have = st + 1 < steps && F + 2 * kBktStep <= P && q.k + 2 * kBktStep <= keys;
           if (have) {
             const int64_t* tk = tsg + q.s + q.k + kBktStep + lane;
 #pragma unroll
