@@ -585,47 +585,22 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   }
 }
 
-// K, V, dK and dV stay in registers: one wave per SIMD.
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+// K, V, dK and dV stay in registers: one wave per SIMD. A sequence that
+// needs 64-bit timestamp arithmetic takes the 64-bit body, compiled into the
+// same kernel.
+template <typename T, int D, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void hstu_bwd_kernel(AttnParams p) {
   __shared__ BwdSmem<T, D> sm;
-  if constexpr (WIDE) {
-    // rare sequences needing 64-bit timestamps: a small grid walks the work slots
-    if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H;
-    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / p.H);
-      const int head = (int)(w - (int64_t)item * p.H);
-      const WorkItem wi = p.items[item];
-      const SeqInfo si = p.seq[wi.seq];
-      if ((si.flags & kSeqWideTs) == 0) continue;
-      bwd_body<T, D, true, POS, TIME>(p, sm, wi, si, head);
-      __syncthreads();                             // the next slot reuses the LDS
-    }
-  } else {
-    const int item = blockIdx.x / p.H;
-    const int head = blockIdx.x - item * p.H;
-    if (item >= *p.n_items) return;
-    const WorkItem wi = p.items[item];
-    const SeqInfo si = p.seq[wi.seq];
-    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (TIME && (si.flags & kSeqWideTs) != 0)
+    bwd_body<T, D, true, POS, TIME>(p, sm, wi, si, head);
+  else
     bwd_body<T, D, false, POS, TIME>(p, sm, wi, si, head);
-  }
-}
-
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
-void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
-  hipLaunchKernelGGL((hstu_bwd_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
-}
-
-template <typename T, int D, bool WIDE>
-void launch_rab(const AttnParams& p, dim3 g, hipStream_t s) {
-  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
-  if (pos && time) launch_one<T, D, WIDE, true, true>(p, g, s);
-  else if (pos) launch_one<T, D, WIDE, true, false>(p, g, s);
-  else if (time) launch_one<T, D, WIDE, false, true>(p, g, s);
-  else launch_one<T, D, WIDE, false, false>(p, g, s);
 }
 
 }  // namespace
@@ -635,14 +610,12 @@ hipError_t launch_bwd(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
   const dim3 g((unsigned)grid);
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(kKBwd, s);
-  launch_rab<T, D, false>(p, g, s);
-  // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (p.rab_time != nullptr) {
-    const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
-    if (p.rab_pos != nullptr) launch_one<T, D, true, true, true>(p, gw, s);
-    else launch_one<T, D, true, false, true>(p, gw, s);
-  }
+  if (pos && time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, true>), g, dim3(256), 0, s, p);
+  else if (pos) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, true, false>), g, dim3(256), 0, s, p);
+  else if (time) hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, true>), g, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((hstu_bwd_kernel<T, D, false, false>), g, dim3(256), 0, s, p);
   prof_after(kKBwd, s);
   return hipGetLastError();
 }

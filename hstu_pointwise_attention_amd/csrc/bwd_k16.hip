@@ -532,41 +532,22 @@ __device__ __forceinline__ void k16_body(const AttnParams& p, K16Smem<D>& sm, co
   }
 }
 
-template <int D, bool WIDE, bool POS, bool TIME>
+// One workgroup per (key block, head); a sequence that needs 64-bit
+// timestamp arithmetic takes the 64-bit body, compiled into the same kernel
+// (it needs no more registers than the 32-bit one).
+template <int D, bool POS, bool TIME>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void hstu_bwd_k16_kernel(AttnParams p) {
   __shared__ K16Smem<D> sm;
-  if constexpr (WIDE) {
-    // rare sequences needing 64-bit timestamps: a small grid walks the work slots
-    if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H;
-    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / p.H);
-      const int head = (int)(w - (int64_t)item * p.H);
-      const WorkItem wi = p.items[item];
-      const SeqInfo si = p.seq[wi.seq];
-      if ((si.flags & kSeqWideTs) == 0) continue;
-      k16_body<D, true, POS, TIME>(p, sm, wi, si, head);
-      __syncthreads();                             // the next slot reuses the LDS
-    }
-  } else {
-    const int item = blockIdx.x / p.H;
-    const int head = blockIdx.x - item * p.H;
-    if (item >= *p.n_items) return;
-    const WorkItem wi = p.items[item];
-    const SeqInfo si = p.seq[wi.seq];
-    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (TIME && (si.flags & kSeqWideTs) != 0)
+    k16_body<D, true, POS, TIME>(p, sm, wi, si, head);
+  else
     k16_body<D, false, POS, TIME>(p, sm, wi, si, head);
-  }
-}
-
-template <int D, bool WIDE>
-void launch_k16_rab(const AttnParams& p, dim3 g, hipStream_t s) {
-  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
-  if (pos && time) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, WIDE, true, true>), g, dim3(512), 0, s, p);
-  else if (pos) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, WIDE, true, false>), g, dim3(512), 0, s, p);
-  else if (time) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, WIDE, false, true>), g, dim3(512), 0, s, p);
-  else hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, WIDE, false, false>), g, dim3(512), 0, s, p);
 }
 
 }  // namespace
@@ -575,13 +556,13 @@ template <int D>
 hipError_t launch_bwd_k16(const AttnParams& p, hipStream_t s) {
   const int64_t grid = p.max_items * p.H;
   if (grid == 0) return hipSuccess;
+  const dim3 g((unsigned)grid);
+  const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(kKBwd, s);
-  launch_k16_rab<D, false>(p, dim3((unsigned)grid), s);
-  if (p.rab_time != nullptr) {
-    const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
-    if (p.rab_pos != nullptr) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, true, true, true>), gw, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, true, false, true>), gw, dim3(512), 0, s, p);
-  }
+  if (pos && time) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, true, true>), g, dim3(512), 0, s, p);
+  else if (pos) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, true, false>), g, dim3(512), 0, s, p);
+  else if (time) hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, false, true>), g, dim3(512), 0, s, p);
+  else hipLaunchKernelGGL((hstu_bwd_k16_kernel<D, false, false>), g, dim3(512), 0, s, p);
   prof_after(kKBwd, s);
   return hipGetLastError();
 }

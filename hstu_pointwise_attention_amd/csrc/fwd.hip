@@ -598,67 +598,44 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
   }
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+// One workgroup per (work item, head). A sequence whose timestamp span
+// needs 64-bit bucket arithmetic (only possible with a time bias) takes the
+// 64-bit body; both bodies are compiled into the one kernel, whose register
+// count is that of the 32-bit body, so no second launch is needed for them.
+template <typename T, int D, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
   using C = FwdCfg<T, D, false>;
   HSTU_FWD_TILE_BUFFERS(C)
-  if constexpr (WIDE) {
-    // sequences needing 64-bit timestamps are rare: a small grid walks the
-    // work slots and takes only theirs
-    if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H;
-    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / p.H);
-      const int head = (int)(w - (int64_t)item * p.H);
-      const WorkItem wi = p.items[item];
-      const SeqInfo si = p.seq[wi.seq];
-      if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, false>(p, sm, kvb, wi, si, head);
-      __syncthreads();                             // the next slot reuses the LDS
-    }
-  } else {
-    const int item = blockIdx.x / p.H;
-    const int head = blockIdx.x - item * p.H;
-    if (item >= *p.n_items) return;
-    const WorkItem wi = p.items[item];
-    const SeqInfo si = p.seq[wi.seq];
-    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (TIME && (si.flags & kSeqWideTs) != 0)
+    fwd_body<T, D, true, POS, TIME, false>(p, sm, kvb, wi, si, head);
+  else
     fwd_body<T, D, false, POS, TIME, false>(p, sm, kvb, wi, si, head);
-  }
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+template <typename T, int D, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_fwd_cand_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, false> sm;
   __shared__ FwdKV<T, D, false> kv;
   const KVBufs<T> kvb{kv.k[0], kv.k[1], kv.v[0], kv.v[1], kv.ts[0], kv.ts[1], kv.win[0], kv.win[1]};
   const int S = p.kv_splits;                       // workgroups per (item, head)
-  if constexpr (WIDE) {
-    if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H * S;
-    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / ((int64_t)p.H * S));
-      const int rem = (int)(w - (int64_t)item * p.H * S);
-      const int head = rem / S, split = rem - head * S;
-      const WorkItem wi = p.items[item];
-      const SeqInfo si = p.seq[wi.seq];
-      if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, false, true>(p, sm, kvb, wi, si, head, split);
-      __syncthreads();                             // the next slot reuses the LDS
-    }
-  } else {
-    const int item = blockIdx.x / (p.H * S);
-    const int rem = blockIdx.x - item * p.H * S;
-    const int head = rem / S, split = rem - head * S;
-    if (item >= *p.n_items) return;
-    const WorkItem wi = p.items[item];
-    const SeqInfo si = p.seq[wi.seq];
-    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+  const int item = blockIdx.x / (p.H * S);
+  const int rem = blockIdx.x - item * p.H * S;
+  const int head = rem / S, split = rem - head * S;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  const SeqInfo si = p.seq[wi.seq];
+  if (TIME && (si.flags & kSeqWideTs) != 0)
+    fwd_body<T, D, true, POS, TIME, false, true>(p, sm, kvb, wi, si, head, split);
+  else
     fwd_body<T, D, false, POS, TIME, false, true>(p, sm, kvb, wi, si, head, split);
-  }
 }
 
 // Sum of the splits' partial A (candidate calls with p.kv_splits > 1), then
@@ -687,7 +664,7 @@ __global__ __launch_bounds__(256) void cand_finish_kernel(AttnParams p) {
   }
 }
 
-template <typename T, int D, bool WIDE, bool POS, bool TIME>
+template <typename T, int D, bool POS, bool TIME>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdOcc<T, D>::W, FwdOcc<T, D>::W)))
 void hstu_dq_kernel(AttnParams p) {
   __shared__ FwdSmem<T, D, true> sm;
@@ -696,42 +673,27 @@ void hstu_dq_kernel(AttnParams p) {
   // sequences below n_ds take dQ from their exported dS tiles
   const int n_ds = p.ds_on != nullptr ? *p.ds_on : 0;
   if (n_ds >= p.B) return;
-  if constexpr (WIDE) {
-    // sequences needing 64-bit timestamps are rare: a small grid walks the
-    // work slots and takes only theirs
-    if (p.n_items[1] == 0) return;
-    const int64_t slots = (int64_t)*p.n_items * p.H;
-    for (int64_t w = blockIdx.x; w < slots; w += gridDim.x) {
-      const int item = (int)(w / p.H);
-      const int head = (int)(w - (int64_t)item * p.H);
-      const WorkItem wi = p.items[item];
-      if (wi.seq < n_ds) continue;
-      const SeqInfo si = p.seq[wi.seq];
-      if ((si.flags & kSeqWideTs) == 0) continue;
-      fwd_body<T, D, true, POS, TIME, true>(p, sm, kvb, wi, si, head);
-      __syncthreads();                             // the next slot reuses the LDS
-    }
-  } else {
-    const int item = blockIdx.x / p.H;
-    const int head = blockIdx.x - item * p.H;
-    if (item >= *p.n_items) return;
-    const WorkItem wi = p.items[item];
-    if (wi.seq < n_ds) return;
-    const SeqInfo si = p.seq[wi.seq];
-    if ((si.flags & kSeqWideTs) != 0) return;      // the other instantiation takes it
+  const int item = blockIdx.x / p.H;
+  const int head = blockIdx.x - item * p.H;
+  if (item >= *p.n_items) return;
+  const WorkItem wi = p.items[item];
+  if (wi.seq < n_ds) return;
+  const SeqInfo si = p.seq[wi.seq];
+  if (TIME && (si.flags & kSeqWideTs) != 0)
+    fwd_body<T, D, true, POS, TIME, true>(p, sm, kvb, wi, si, head);
+  else
     fwd_body<T, D, false, POS, TIME, true>(p, sm, kvb, wi, si, head);
-  }
 }
 
 // KIND: 0 forward, 1 dQ pass, 2 candidate scoring against a cached history
-template <int KIND, typename T, int D, bool WIDE, bool POS, bool TIME>
+template <int KIND, typename T, int D, bool POS, bool TIME>
 void launch_one(const AttnParams& p, dim3 g, hipStream_t s) {
   if constexpr (KIND == 1)
-    hipLaunchKernelGGL((hstu_dq_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((hstu_dq_kernel<T, D, POS, TIME>), g, dim3(256), 0, s, p);
   else if constexpr (KIND == 2)
-    hipLaunchKernelGGL((hstu_fwd_cand_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((hstu_fwd_cand_kernel<T, D, POS, TIME>), g, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((hstu_fwd_kernel<T, D, WIDE, POS, TIME>), g, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((hstu_fwd_kernel<T, D, POS, TIME>), g, dim3(256), 0, s, p);
 }
 
 template <int KIND, typename T, int D>
@@ -741,16 +703,10 @@ hipError_t launch_all(const AttnParams& p, int id, hipStream_t s) {
   const dim3 g((unsigned)grid);
   const bool pos = p.rab_pos != nullptr, time = p.rab_time != nullptr;
   prof_before(id, s);
-  if (pos && time) launch_one<KIND, T, D, false, true, true>(p, g, s);
-  else if (pos) launch_one<KIND, T, D, false, true, false>(p, g, s);
-  else if (time) launch_one<KIND, T, D, false, false, true>(p, g, s);
-  else launch_one<KIND, T, D, false, false, false>(p, g, s);
-  // Only a time bias can mark a sequence as needing 64-bit timestamps.
-  if (time) {
-    const dim3 gw((unsigned)(grid < kWideGrid ? grid : kWideGrid));
-    if (pos) launch_one<KIND, T, D, true, true, true>(p, gw, s);
-    else launch_one<KIND, T, D, true, false, true>(p, gw, s);
-  }
+  if (pos && time) launch_one<KIND, T, D, true, true>(p, g, s);
+  else if (pos) launch_one<KIND, T, D, true, false>(p, g, s);
+  else if (time) launch_one<KIND, T, D, false, true>(p, g, s);
+  else launch_one<KIND, T, D, false, false>(p, g, s);
   prof_after(id, s);
   return hipGetLastError();
 }

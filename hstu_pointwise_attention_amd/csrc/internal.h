@@ -36,7 +36,7 @@ struct AttnParams {
   uint32_t* ts_rel;                  // [T] rebased timestamps
   WorkItem* items;                   // [max_items]
   WorkItem* items_q;                 // [max_items] query-block order (backward only)
-  int32_t* n_items;                  // [2]: items, sequences that need 64-bit timestamps
+  int32_t* n_items;                  // [1]: items of the work list
   int32_t* sched_scratch;            // schedule kernel scratch
   void* d_a;                         // [T, H, D] dtype: dO * U / L (backward)
   int64_t max_items;                 // T / 128 + B
@@ -103,10 +103,6 @@ int set_error(int status, const char* fmt, ...);
 // base != nullptr). ds_room: the bf16 backward's room for the dS export;
 // p.det: the deterministic rab-gradient partials.
 size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool ds_room);
-
-// Grid of the attention kernels' 64-bit-timestamp instantiations, which walk
-// the work slots of the (rare) sequences that need them.
-constexpr int kWideGrid = 512;
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {

@@ -241,17 +241,11 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
   int* fill_q = fill + NB;                      // [NB] (mode 2: forward-order list)
   for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; fill_q[i] = 0; }
   __syncthreads();
-  if (threadIdx.x == 0) lds[0] = 0;
-  __syncthreads();
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const SeqInfo si = p.seq[b];
-    const int n = si.nblk;
+    const int n = p.seq[b].nblk;
     seq_base[b] = n;
     atomicAdd(&hist[n < NB ? n : NB - 1], 1);
-    if (si.flags & kSeqWideTs) atomicAdd(&lds[0], 1);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) p.n_items[1] = lds[0];
   __syncthreads();
   const int total = block_scan_excl(seq_base, B, false, lds);
   if (threadIdx.x == 0) seq_base[B] = total;
@@ -645,7 +639,7 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool
   p.seq = (SeqInfo*)take(sizeof(SeqInfo) * (size_t)(p.B > 0 ? p.B : 1));
   p.ts_rel = (uint32_t*)take(sizeof(uint32_t) * (size_t)(p.T > 0 ? p.T : 1));
   p.items = (WorkItem*)take(sizeof(WorkItem) * (size_t)p.max_items);
-  p.n_items = (int32_t*)take(2 * sizeof(int32_t));
+  p.n_items = (int32_t*)take(sizeof(int32_t));
   p.sched_scratch = (int32_t*)take(sizeof(int32_t) * (size_t)(p.B + 1 + 4 * NB));
   p.items_q = nullptr;
   p.d_a = nullptr;
