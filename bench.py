@@ -170,7 +170,8 @@ def main():
         return kt.avg_ms(k)
 
     fwd_ms = kms("fwd")
-    # the backward: dA' / dU preprocessing, key-block kernel, dQ kernel
+    # the backward: dA' / dU preprocessing (one launch with the backward's
+    # sequence prep), key-block kernel, dQ kernel
     bwd_ms = sum(kms(k) for k in ("bwd_pre", "bwd", "dq"))
     bwd_tf = fl["bwd"] / (bwd_ms * 1e-3) / 1e12
     fwd_tf = fl["fwd"] / (fwd_ms * 1e-3) / 1e12

@@ -236,14 +236,13 @@ hipError_t dispatch_dq_ds(const AttnParams& p, hipStream_t s) {
   }
 }
 
-// dA' and dU, then dK / dV / d_rab per key block, then dQ per query block
-// (its own schedule, the forward's). With the dS export (bf16), the device
-// flag set by the schedule picks one of the two dQ kernels; the other exits
-// at once.
+// After the prep and dA' / dU: dK / dV / d_rab per key block, then dQ per
+// query block (its own schedule, the forward's). With the dS export (bf16),
+// the schedule's count of exported sequences splits the dQ work between the
+// two dQ kernels.
 template <typename T>
 hipError_t run_bwd_main(const AttnParams& p, hipStream_t s) {
-  hipError_t e = launch_bwd_pre<T>(p, s);
-  if (e == hipSuccess) e = dispatch_bwd<T>(p, s);
+  hipError_t e = dispatch_bwd<T>(p, s);
   if (e == hipSuccess) e = launch_rab_reduce(p, s);
   AttnParams pq = p;                             // the dQ pass walks query blocks
   pq.items = p.items_q;
@@ -445,7 +444,8 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (p.T > 0 && p.B > 0) {
-    e = launch_prep(p, s);                       // also clears d_rab_pos / d_rab_time
+    // sequence prep (which also clears d_rab_pos / d_rab_time) beside dA', dU
+    e = desc->dtype == HSTU_DTYPE_BF16 ? launch_bwd_prep<bf16>(p, s) : launch_bwd_prep<float>(p, s);
     if (e == hipSuccess) e = launch_schedule(p, 2, s);
     if (e == hipSuccess)
       e = desc->dtype == HSTU_DTYPE_BF16 ? run_bwd_main<bf16>(p, s) : run_bwd_main<float>(p, s);

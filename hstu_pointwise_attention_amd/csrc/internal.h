@@ -161,7 +161,8 @@ int64_t ds_capacity(int64_t T, int B, int H, int max_len);
 // Fixed-order sums of the deterministic rab-gradient partials into
 // d_rab_pos / d_rab_time (exits at once unless *p.det_on).
 hipError_t launch_rab_reduce(const AttnParams& p, hipStream_t s);
-template <typename T> hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s);
+// The backward's sequence prep and dA' / dU pass in one launch.
+template <typename T> hipError_t launch_bwd_prep(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 
 hipError_t launch_linear(int64_t M, int64_t K, int64_t N, const void* x, int64_t ldx,

@@ -29,14 +29,16 @@ struct MinOp { __device__ int64_t operator()(int64_t a, int64_t b) const { retur
 struct MaxOp { __device__ int64_t operator()(int64_t a, int64_t b) const { return a > b ? a : b; } };
 struct AndOp { __device__ int32_t operator()(int32_t a, int32_t b) const { return a & b; } };
 
-// One workgroup per sequence: metadata + rebased timestamps. In the backward
-// the workgroups also clear the rab gradient tables (overwritten outputs).
-__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p) {
+// Metadata + rebased timestamps of sequence b, by one workgroup of any size
+// up to kSeqPrepThreads; workgroup b of the n_groups doing this also clears
+// its share of the rab gradient tables when they are set (the backward's
+// overwritten outputs).
+__device__ void seq_prep_body(const AttnParams& p, int b, int n_groups) {
   __shared__ int64_t lds64[kSeqPrepThreads / kWave];
   __shared__ int32_t lds32[kSeqPrepThreads / kWave];
   {
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)b * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)n_groups * blockDim.x;
     if (p.d_rab_pos) {
       const int64_t n = (int64_t)p.rab_heads * (2 * (int64_t)p.max_len - 1);
       for (int64_t i = i0; i < n; i += stride) p.d_rab_pos[i] = 0.f;
@@ -46,7 +48,6 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p)
       for (int64_t i = i0; i < n; i += stride) p.d_rab_time[i] = 0.f;
     }
   }
-  const int b = blockIdx.x;
   const int64_t s = p.seq_offsets[b];
   const int64_t e = p.seq_offsets[b + 1];
   const int L = (int)(e - s);
@@ -102,6 +103,11 @@ __global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p)
     si.ts_origin = origin;
     p.seq[b] = si;
   }
+}
+
+// One workgroup per sequence (the forward).
+__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p) {
+  seq_prep_body(p, blockIdx.x, gridDim.x);
 }
 
 // Candidate scoring against a cached history: one workgroup per sequence.
@@ -561,7 +567,9 @@ __device__ __forceinline__ int seq_of_token(const int64_t* offs, int B, int64_t 
 }
 
 // dA' = dO * U / L (or dO / L without gate), dU = dO * A. Eight elements per
-// thread, so every access is 16 bytes (bf16) or two of them (fp32).
+// thread, so every access is 16 bytes (bf16) or two of them (fp32). 1/L is
+// formed from the offsets as the sequence prep forms it, so this needs none
+// of the prep's outputs.
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   static __device__ __forceinline__ void load(const bf16* p, float* f) {
@@ -589,15 +597,16 @@ template <> struct Vec8<float> {
 };
 
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(AttnParams p) {
+__device__ void bwd_pre_body(const AttnParams& p, int blk, int n_blk) {
   const int HD = p.H * p.D;                      // a multiple of 32
   const int64_t n8 = p.T * HD / 8;
-  for (int64_t q8 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q8 < n8;
-       q8 += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t q8 = (int64_t)blk * blockDim.x + threadIdx.x; q8 < n8;
+       q8 += (int64_t)n_blk * blockDim.x) {
     const int64_t e0 = q8 * 8;
     const int64_t t = e0 / HD;
     const int hd = (int)(e0 - t * HD);
-    const float inv = p.seq[seq_of_token(p.seq_offsets, p.B, t)].inv_len;
+    const int b = seq_of_token(p.seq_offsets, p.B, t);
+    const float inv = 1.0f / (float)(p.seq_offsets[b + 1] - p.seq_offsets[b]);
     float go[8], da[8];
     Vec8<T>::load(reinterpret_cast<const T*>(p.d_o) + e0, go);
     if (p.u != nullptr) {
@@ -618,6 +627,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(AttnParams p) {
   }
 }
 
+// The backward's first launch: workgroups 0..B-1 prepare one sequence each
+// (and clear the rab gradient tables), the rest form dA' and dU. The two
+// parts are independent, so the prep's latency runs under the elementwise
+// pass instead of in a launch of its own.
+template <typename T>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(AttnParams p) {
+  if ((int)blockIdx.x < p.B)
+    seq_prep_body(p, blockIdx.x, p.B);
+  else
+    bwd_pre_body<T>(p, blockIdx.x - p.B, gridDim.x - p.B);
+}
 
 int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
@@ -777,16 +797,16 @@ hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_bwd_pre(const AttnParams& p, hipStream_t s) {
+hipError_t launch_bwd_prep(const AttnParams& p, hipStream_t s) {
   const int64_t n8 = p.T * p.H * p.D / 8;
-  if (n8 == 0) return hipSuccess;
+  const int g = n8 > 0 ? grid_for(n8, kPrepThreads) : 1;
   prof_before(kKBwdPre, s);
-  hipLaunchKernelGGL(bwd_pre_kernel<T>, dim3(grid_for(n8, 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(p.B + g), dim3(kPrepThreads), 0, s, p);
   prof_after(kKBwdPre, s);
   return hipGetLastError();
 }
 
-template hipError_t launch_bwd_pre<bf16>(const AttnParams&, hipStream_t);
-template hipError_t launch_bwd_pre<float>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd_prep<bf16>(const AttnParams&, hipStream_t);
+template hipError_t launch_bwd_prep<float>(const AttnParams&, hipStream_t);
 
 }  // namespace hstu
