@@ -310,8 +310,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   carve_workspace(p, workspace, false, elem_bytes(desc->dtype), false);
   if (p.T == 0 || p.B == 0) return ok();
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep(p, s);
-  if (e == hipSuccess) e = launch_schedule(p, 0, s);
+  hipError_t e = launch_fwd_prep(p, s);         // sequence prep and work list
   if (e == hipSuccess)
     e = desc->dtype == HSTU_DTYPE_BF16 ? dispatch_fwd<bf16>(p, s) : dispatch_fwd<float>(p, s);
   if (e != hipSuccess) return hip_fail(e, "hstu_attn_fwd launch");
@@ -444,9 +443,9 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (p.T > 0 && p.B > 0) {
-    // sequence prep (which also clears d_rab_pos / d_rab_time) beside dA', dU
+    // work lists, sequence prep (which also clears d_rab_pos / d_rab_time)
+    // and dA', dU in one launch
     e = desc->dtype == HSTU_DTYPE_BF16 ? launch_bwd_prep<bf16>(p, s) : launch_bwd_prep<float>(p, s);
-    if (e == hipSuccess) e = launch_schedule(p, 2, s);
     if (e == hipSuccess)
       e = desc->dtype == HSTU_DTYPE_BF16 ? run_bwd_main<bf16>(p, s) : run_bwd_main<float>(p, s);
   } else {

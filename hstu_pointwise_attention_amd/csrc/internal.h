@@ -113,7 +113,6 @@ enum KernelId : int {
 void prof_before(int id, hipStream_t s);
 void prof_after(int id, hipStream_t s);
 
-hipError_t launch_prep(const AttnParams& p, hipStream_t s);
 // mode 0: forward order (query block index descending) into items; 1:
 // backward order into items; 2: backward order into items and forward order
 // into items_q.
@@ -161,7 +160,9 @@ int64_t ds_capacity(int64_t T, int B, int H, int max_len);
 // Fixed-order sums of the deterministic rab-gradient partials into
 // d_rab_pos / d_rab_time (exits at once unless *p.det_on).
 hipError_t launch_rab_reduce(const AttnParams& p, hipStream_t s);
-// The backward's sequence prep and dA' / dU pass in one launch.
+// The forward's sequence prep and work list in one launch; the backward's
+// sequence prep, work lists and dA' / dU pass in one launch.
+hipError_t launch_fwd_prep(const AttnParams& p, hipStream_t s);
 template <typename T> hipError_t launch_bwd_prep(const AttnParams& p, hipStream_t s);
 hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s);
 

@@ -7,7 +7,6 @@ namespace hstu {
 
 namespace {
 
-constexpr int kPrepThreads = 256;
 constexpr int kSeqPrepThreads = 1024;
 constexpr int kSchedThreads = 1024;
 
@@ -105,15 +104,10 @@ __device__ void seq_prep_body(const AttnParams& p, int b, int n_groups) {
   }
 }
 
-// One workgroup per sequence (the forward).
-__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_kernel(AttnParams p) {
-  seq_prep_body(p, blockIdx.x, gridDim.x);
-}
-
 // Candidate scoring against a cached history: one workgroup per sequence.
 // The sequence's rows are numbered as in the single-shot layout (history,
 // then this call's candidates); the joined timestamps of that numbering go
-// to c.ts_joined (64-bit) and p.ts_rel (rebased, as in seq_prep_kernel).
+// to c.ts_joined (64-bit) and p.ts_rel (rebased, as in seq_prep_body).
 // Normalisation is 1 / (h + n) over all n candidates of the sequence, and
 // only query blocks holding candidates are scheduled (nblk counts blocks
 // from the one holding row h).
@@ -232,13 +226,22 @@ __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
 // descending: start[x] = number of items with a larger x. Both orders hold
 // the same multiset of x, so mode 2 places every item in both lists.
 // Its arrays live in LDS when they fit (every access is then a short LDS
-// round trip instead of a global one), else in the workspace scratch.
+// round trip instead of a global one), else in the workspace scratch. One
+// workgroup of any size up to kSchedThreads. With from_offsets, each
+// sequence's block count and length come straight from seq_offsets (the
+// sequence prep's values for them), so the schedule can run beside the prep
+// in one launch; the cached-history path, whose block counts the prep sets
+// otherwise, reads them from p.seq.
 constexpr int kSchedLds = 6144;
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
+__device__ void schedule_body(const AttnParams& p, int mode, bool from_offsets) {
   __shared__ int lds[kSchedThreads];
   __shared__ int small[kSchedLds];
   const int B = p.B;
+  auto len_of = [&](int b) {
+    return from_offsets ? (int)(p.seq_offsets[b + 1] - p.seq_offsets[b]) : p.seq[b].len;
+  };
+  auto nblk_of = [&](int b) { return from_offsets ? (len_of(b) + kBlk - 1) / kBlk : p.seq[b].nblk; };
   const int NB = (int)(p.T / kBlk) + 2;       // x ranges over [0, NB)
   int* seq_base = (B + 1 + 4 * NB <= kSchedLds) ? small : p.sched_scratch;   // [B + 1]
   int* hist = seq_base + (B + 1);               // [NB]: sequences with n blocks
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
   for (int i = threadIdx.x; i < NB; i += blockDim.x) { hist[i] = 0; fill[i] = 0; fill_q[i] = 0; }
   __syncthreads();
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int n = p.seq[b].nblk;
+    const int n = nblk_of(b);
     seq_base[b] = n;
     atomicAdd(&hist[n < NB ? n : NB - 1], 1);
   }
@@ -292,23 +295,37 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, i
     __shared__ int64_t run[kSchedThreads / kWave + 1];
     __shared__ int cut;                          // first sequence whose tiles overflow ds_cap
     if (threadIdx.x == 0) cut = B;
-    const int per = (B + kSchedThreads - 1) / kSchedThreads;
+    const int per = (B + (int)blockDim.x - 1) / (int)blockDim.x;
     const int b0 = threadIdx.x * per, b1 = b0 + per < B ? b0 + per : B;
     int64_t sum = 0;
-    for (int b = b0; b < b1; ++b) sum += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
+    for (int b = b0; b < b1; ++b) sum += (int64_t)p.H * ds_seq_tiles(len_of(b));
     int64_t tiles;
     int64_t at = block_scan_one(sum, run, &tiles);   // (ends with a barrier)
     for (int b = b0; b < b1; ++b) {
       p.tile_base[b] = at;
-      at += (int64_t)p.H * ds_seq_tiles(p.seq[b].len);
+      at += (int64_t)p.H * ds_seq_tiles(len_of(b));
       if (at > p.ds_cap) atomicMin(&cut, b);
     }
     __syncthreads();
-    if (threadIdx.x == kSchedThreads - 1) {
+    if (threadIdx.x == blockDim.x - 1) {
       if (p.ds_on) *p.ds_on = cut;
       if (p.det_on) *p.det_on = tiles <= p.part_cap ? 1 : 0;
     }
   }
+}
+
+// The cached-history path's schedule (after its own prep).
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
+  schedule_body(p, mode, false);
+}
+
+// The forward's first launch: workgroup 0 builds the work list, workgroups
+// 1..B prepare one sequence each; the two are independent.
+__global__ __launch_bounds__(kSchedThreads) void fwd_prep_kernel(AttnParams p) {
+  if (blockIdx.x == 0)
+    schedule_body(p, 0, true);
+  else
+    seq_prep_body(p, blockIdx.x - 1, p.B);
 }
 
 // rab bucket export, laid out over the jagged lower triangle: sequence
@@ -627,16 +644,19 @@ __device__ void bwd_pre_body(const AttnParams& p, int blk, int n_blk) {
   }
 }
 
-// The backward's first launch: workgroups 0..B-1 prepare one sequence each
-// (and clear the rab gradient tables), the rest form dA' and dU. The two
-// parts are independent, so the prep's latency runs under the elementwise
-// pass instead of in a launch of its own.
+// The backward's first launch: workgroup 0 builds both work lists and
+// numbers the dS tiles, workgroups 1..B prepare one sequence each (and clear
+// the rab gradient tables), the rest form dA' and dU. The three parts are
+// independent, so the schedule's and the prep's latency run under the
+// elementwise pass instead of in launches of their own.
 template <typename T>
-__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(AttnParams p) {
-  if ((int)blockIdx.x < p.B)
-    seq_prep_body(p, blockIdx.x, p.B);
+__global__ __launch_bounds__(kSchedThreads) void bwd_prep_kernel(AttnParams p) {
+  if (blockIdx.x == 0)
+    schedule_body(p, 2, true);
+  else if ((int)blockIdx.x <= p.B)
+    seq_prep_body(p, blockIdx.x - 1, p.B);
   else
-    bwd_pre_body<T>(p, blockIdx.x - p.B, gridDim.x - p.B);
+    bwd_pre_body<T>(p, blockIdx.x - 1 - p.B, gridDim.x - 1 - p.B);
 }
 
 int grid_for(int64_t n, int threads) {
@@ -754,14 +774,6 @@ hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const AttnParams& p, hipStream_t s) {
-  if (p.B == 0) return hipSuccess;
-  prof_before(kKPrep, s);
-  hipLaunchKernelGGL(seq_prep_kernel, dim3(p.B), dim3(kSeqPrepThreads), 0, s, p);
-  prof_after(kKPrep, s);
-  return hipGetLastError();
-}
-
 hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s) {
   prof_before(kKSchedule, s);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p, mode);
@@ -796,12 +808,19 @@ hipError_t launch_fill_f32(float* x, int64_t n, float value, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_fwd_prep(const AttnParams& p, hipStream_t s) {
+  prof_before(kKPrep, s);
+  hipLaunchKernelGGL(fwd_prep_kernel, dim3(1 + p.B), dim3(kSchedThreads), 0, s, p);
+  prof_after(kKPrep, s);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_bwd_prep(const AttnParams& p, hipStream_t s) {
   const int64_t n8 = p.T * p.H * p.D / 8;
-  const int g = n8 > 0 ? grid_for(n8, kPrepThreads) : 1;
+  const int g = n8 > 0 ? grid_for(n8, kSchedThreads) : 1;
   prof_before(kKBwdPre, s);
-  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(p.B + g), dim3(kPrepThreads), 0, s, p);
+  hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(1 + p.B + g), dim3(kSchedThreads), 0, s, p);
   prof_after(kKBwdPre, s);
   return hipGetLastError();
 }
