@@ -35,8 +35,8 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 # stands.
 TRAFFIC = {
     # key-block backward (hstu_bwd_k16_kernel, D=128, efficiency workload):
-    # FETCH_SIZE 395799 KiB x 2.00 + WRITE_SIZE 1087914 KiB x 1.00
-    "bwd": {"workload": "efficiency_8192_bf16", "bytes": 1924620902,
+    # FETCH_SIZE 393752 KiB x 2.00 + WRITE_SIZE 1088013 KiB x 1.00
+    "bwd": {"workload": "efficiency_8192_bf16", "bytes": 1920529818,
             "compulsory_bytes": 1233000000, "unit": "B"},
 }
 # The pages' only figure for this path, quoted as context (not a target, not
