@@ -394,8 +394,7 @@ hstu_status hstu_attn_fwd_cached(const hstu_attn_desc* desc, const int64_t* cand
   p.timestamps = rab_time ? c.ts_joined : nullptr;   // the joined numbering's timestamps
   if (desc->total_tokens == 0 || p.B == 0) return ok();
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_prep_cand(p, c, s);
-  if (e == hipSuccess) e = launch_schedule(p, 0, s);
+  hipError_t e = launch_prep_cand(p, c, s);     // sequence prep and work list
   if (e == hipSuccess)
     e = desc->dtype == HSTU_DTYPE_BF16 ? dispatch_fwd_cand<bf16>(p, s) : dispatch_fwd_cand<float>(p, s);
   if (e != hipSuccess) return hip_fail(e, "hstu_attn_fwd_cached launch");

@@ -106,17 +106,13 @@ size_t carve_workspace(AttnParams& p, void* base, bool bwd, int elem_bytes, bool
 
 // Kernel identities for the optional per-launch timing (hstu_profile_*).
 enum KernelId : int {
-  kKPrep = 0, kKSchedule, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
+  kKPrep = 0, kKFwd, kKBwdPre, kKBwd, kKDq, kKFill, kKLinear, kKLayerNorm,
   kKBucketize, kKFp8Linear, kKFp8Quant, kKDqDs, kKRabReduce, kNumKernelIds
 };
 // Records a HIP event on `s` before / after a launch when timing is enabled.
 void prof_before(int id, hipStream_t s);
 void prof_after(int id, hipStream_t s);
 
-// mode 0: forward order (query block index descending) into items; 1:
-// backward order into items; 2: backward order into items and forward order
-// into items_q.
-hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s);
 hipError_t launch_bucketize(const AttnParams& p, const int64_t* pair_offsets, uint16_t* bp,
                             uint8_t* bt, hipStream_t s);
 // out[b] = unmasked pairs of sequences 0..b-1; out[B] = all of them.

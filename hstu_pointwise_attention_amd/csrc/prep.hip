@@ -111,10 +111,9 @@ __device__ void seq_prep_body(const AttnParams& p, int b, int n_groups) {
 // Normalisation is 1 / (h + n) over all n candidates of the sequence, and
 // only query blocks holding candidates are scheduled (nblk counts blocks
 // from the one holding row h).
-__global__ __launch_bounds__(kSeqPrepThreads) void seq_prep_cand_kernel(AttnParams p, CandArgs c) {
+__device__ void seq_prep_cand_body(const AttnParams& p, const CandArgs& c, int b) {
   __shared__ int64_t lds64[kSeqPrepThreads / kWave];
   __shared__ int32_t lds32[kSeqPrepThreads / kWave];
-  const int b = blockIdx.x;
   const int64_t hs = c.hist_offsets[b], cs = c.cand_offsets[b];
   const int h = (int)(c.hist_offsets[b + 1] - hs);
   const int m = (int)(c.cand_offsets[b + 1] - cs);
@@ -227,21 +226,32 @@ __device__ int block_scan_excl(int* data, int n, bool from_end, int* lds) {
 // the same multiset of x, so mode 2 places every item in both lists.
 // Its arrays live in LDS when they fit (every access is then a short LDS
 // round trip instead of a global one), else in the workspace scratch. One
-// workgroup of any size up to kSchedThreads. With from_offsets, each
-// sequence's block count and length come straight from seq_offsets (the
-// sequence prep's values for them), so the schedule can run beside the prep
-// in one launch; the cached-history path, whose block counts the prep sets
-// otherwise, reads them from p.seq.
+// workgroup of any size up to kSchedThreads. Each sequence's block count and
+// length come straight from the offsets (the values the sequence prep
+// derives from them), so the schedule runs beside the prep in one launch.
+// cand: candidate scoring against a cached history, whose rows are the
+// history's and the call's candidates and whose scheduled blocks are those
+// from the one holding the first candidate. mode 0: the forward order (query
+// blocks, the last block first) into items; 2: the backward order (key
+// blocks, the first block first) into items and the forward order into
+// items_q, with the dS tile numbering and the export count.
 constexpr int kSchedLds = 6144;
 
-__device__ void schedule_body(const AttnParams& p, int mode, bool from_offsets) {
+__device__ void schedule_body(const AttnParams& p, int mode, const CandArgs* cand) {
   __shared__ int lds[kSchedThreads];
   __shared__ int small[kSchedLds];
   const int B = p.B;
   auto len_of = [&](int b) {
-    return from_offsets ? (int)(p.seq_offsets[b + 1] - p.seq_offsets[b]) : p.seq[b].len;
+    return cand ? (int)(cand->hist_offsets[b + 1] - cand->hist_offsets[b] +
+                        cand->cand_offsets[b + 1] - cand->cand_offsets[b])
+                : (int)(p.seq_offsets[b + 1] - p.seq_offsets[b]);
   };
-  auto nblk_of = [&](int b) { return from_offsets ? (len_of(b) + kBlk - 1) / kBlk : p.seq[b].nblk; };
+  auto nblk_of = [&](int b) {
+    if (!cand) return (len_of(b) + kBlk - 1) / kBlk;
+    const int h = (int)(cand->hist_offsets[b + 1] - cand->hist_offsets[b]);
+    const int m = (int)(cand->cand_offsets[b + 1] - cand->cand_offsets[b]);
+    return m > 0 ? (h + m + kBlk - 1) / kBlk - h / kBlk : 0;
+  };
   const int NB = (int)(p.T / kBlk) + 2;       // x ranges over [0, NB)
   int* seq_base = (B + 1 + 4 * NB <= kSchedLds) ? small : p.sched_scratch;   // [B + 1]
   int* hist = seq_base + (B + 1);               // [NB]: sequences with n blocks
@@ -314,18 +324,21 @@ __device__ void schedule_body(const AttnParams& p, int mode, bool from_offsets) 
   }
 }
 
-// The cached-history path's schedule (after its own prep).
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(AttnParams p, int mode) {
-  schedule_body(p, mode, false);
-}
-
 // The forward's first launch: workgroup 0 builds the work list, workgroups
 // 1..B prepare one sequence each; the two are independent.
 __global__ __launch_bounds__(kSchedThreads) void fwd_prep_kernel(AttnParams p) {
   if (blockIdx.x == 0)
-    schedule_body(p, 0, true);
+    schedule_body(p, 0, nullptr);
   else
     seq_prep_body(p, blockIdx.x - 1, p.B);
+}
+
+// The same for candidate scoring against a cached history.
+__global__ __launch_bounds__(kSchedThreads) void cand_prep_kernel(AttnParams p, CandArgs c) {
+  if (blockIdx.x == 0)
+    schedule_body(p, 0, &c);
+  else
+    seq_prep_cand_body(p, c, blockIdx.x - 1);
 }
 
 // rab bucket export, laid out over the jagged lower triangle: sequence
@@ -652,7 +665,7 @@ __device__ void bwd_pre_body(const AttnParams& p, int blk, int n_blk) {
 template <typename T>
 __global__ __launch_bounds__(kSchedThreads) void bwd_prep_kernel(AttnParams p) {
   if (blockIdx.x == 0)
-    schedule_body(p, 2, true);
+    schedule_body(p, 2, nullptr);
   else if ((int)blockIdx.x <= p.B)
     seq_prep_body(p, blockIdx.x - 1, p.B);
   else
@@ -769,15 +782,8 @@ int cand_kv_splits(int64_t m_rows, int64_t hist_rows, int B, int H) {
 hipError_t launch_prep_cand(const AttnParams& p, const CandArgs& c, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   prof_before(kKPrep, s);
-  hipLaunchKernelGGL(seq_prep_cand_kernel, dim3(p.B), dim3(kSeqPrepThreads), 0, s, p, c);
+  hipLaunchKernelGGL(cand_prep_kernel, dim3(1 + p.B), dim3(kSchedThreads), 0, s, p, c);
   prof_after(kKPrep, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_schedule(const AttnParams& p, int mode, hipStream_t s) {
-  prof_before(kKSchedule, s);
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, p, mode);
-  prof_after(kKSchedule, s);
   return hipGetLastError();
 }
 

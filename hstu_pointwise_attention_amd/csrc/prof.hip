@@ -34,7 +34,7 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* const kNames[kNumKernelIds] = {"prep", "schedule", "fwd", "bwd_pre", "bwd",
+const char* const kNames[kNumKernelIds] = {"prep", "fwd", "bwd_pre", "bwd",
                                            "dq", "fill", "linear", "layernorm_gate",
                                            "bucketize", "fp8_linear", "fp8_quantize", "dq_ds",
                                            "rab_reduce"};
