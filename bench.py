@@ -163,8 +163,9 @@ def main():
     kern = {name: round(kt.avg_ms(name), 5) for name in kt.results}
 
     def kms(k):
-        # the dQ pass is two launches, one of which exits at once: dQ from the
-        # exported dS tiles ("dq_ds") or by recomputing dS ("dq")
+        # the dQ pass is two launches: dQ from the exported dS tiles ("dq_ds")
+        # and by recomputing dS ("dq") for sequences whose tiles did not fit
+        # (it exits at once when every sequence exported)
         if k == "dq" and "dq_ds" in kt.results:
             return kt.avg_ms("dq") + kt.avg_ms("dq_ds")
         return kt.avg_ms(k)

@@ -116,7 +116,8 @@ __device__ __forceinline__ void bwd_body(const AttnParams& p, BwdSmem<T, D>& sm,
   constexpr bool time_grad = has_time;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
-  // timestamps and run in the second instantiation of the kernel.
+  // timestamps and take this body with WIDE set (every tile in the general
+  // time-bias mode).
   constexpr bool wide = WIDE;
   const int n_pos = 2 * p.max_len - 1;
   const int t_last = p.n_time_buckets - 1;

@@ -163,7 +163,8 @@ __device__ __forceinline__ void fwd_body(const AttnParams& p, FwdSmem<T, D, GRAD
   constexpr bool has_time = TIME;
   const bool sorted_ts = (si.flags & kSeqSortedTs) != 0;
   // Sequences whose timestamp span needs 64-bit bucket arithmetic keep raw
-  // timestamps and run in the second instantiation of the kernel.
+  // timestamps and take this body with WIDE set (every tile in the general
+  // time-bias mode).
   constexpr bool wide = WIDE;
   const int t_last = p.n_time_buckets - 1;
 

@@ -146,7 +146,7 @@ int cand_kv_splits(int64_t m_rows, int64_t hist_rows, int B, int H);
 template <typename T, int D> hipError_t launch_bwd(const AttnParams& p, hipStream_t s);
 template <int D> hipError_t launch_bwd_k16(const AttnParams& p, hipStream_t s);
 template <typename T, int D> hipError_t launch_dq(const AttnParams& p, hipStream_t s);
-// dQ from the exported dS tiles (dq_ds.hip); exits at once unless *p.ds_on.
+// dQ from the exported dS tiles (dq_ds.hip) for the first *p.ds_on sequences.
 template <int D> hipError_t launch_dq_ds(const AttnParams& p, hipStream_t s);
 // Tiles of a batch of T tokens in B sequences of at most max_len rows each,
 // H heads (an upper bound of the exact count), capped at max_tiles.
