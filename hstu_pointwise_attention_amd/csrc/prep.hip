@@ -438,8 +438,10 @@ __device__ __forceinline__ void bkt_advance(BktPos& q, int n, const AttnParams& 
   }
 }
 
-__global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))) void bucketize_kernel(AttnParams p, const int64_t* pair_offsets,
-                                                                uint16_t* bp, uint8_t* bt, int vec) {
+// The kernel is bound by the latency of its steps, so it asks the compiler
+// for a register budget that keeps many waves per SIMD in flight.
+__global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void bucketize_kernel(AttnParams p, const int64_t* pair_offsets, uint16_t* bp, uint8_t* bt, int vec) {
   __shared__ int64_t po_lds[kBktLdsSeqs + 1];
   __shared__ __attribute__((aligned(16))) uint16_t xp[kBktWaves][kBktStep];
   __shared__ __attribute__((aligned(16))) uint8_t xt[kBktWaves][kBktStep];
@@ -511,8 +513,7 @@ __global__ __launch_bounds__(kBktThreads) __attribute__((amdgpu_waves_per_eu(8))
             const uint32_t dl = til - cl;
             const uint32_t dh = tih - chi - (til < cl ? 1u : 0u);
             wide = wide || (int32_t)dh != ((int32_t)dl >> 31);
-            const int32_t sd = (int32_t)dl;
-            const uint32_t a = (uint32_t)max(sd, -sd) + 1u;
+            const uint32_t a = ((int32_t)dl < 0 ? 0u - dl : dl) + 1u;
             const int e = 31 - __builtin_clz(a);
             ev[m] = (uint32_t)(e < last ? e : last);
           }
