@@ -102,6 +102,25 @@ def test_bucketize_long_rows_mixed():
             _bucket_case(inp, nb)
 
 
+def test_bucketize_differences_at_2_pow_31():
+    """Key-timestamp differences of exactly +-(2^31 - 1), +-2^31 and
+    +-(2^31 + 1) inside rows long enough for whole 512-slot steps of one row,
+    where the export first computes buckets from 32-bit differences (buckets
+    30, 31 and 31 before the clamp at 64 buckets)."""
+    L = 1500
+    offs = W.offsets_from_lengths(np.array([L, L]))
+    base = np.int64(1) << 40
+    ts = np.full(2 * L, base, dtype=np.int64)
+    rng = np.random.default_rng(13)
+    for s in (0, L):
+        for d in (2 ** 31 - 1, 2 ** 31, 2 ** 31 + 1):
+            for sign in (1, -1):
+                idx = s + rng.integers(0, L, size=40)
+                ts[idx] = base + sign * d
+    inp = dict(seq_offsets=offs, num_targets=np.array([0, 100]), timestamps=ts, max_len=2048, dtype="fp32")
+    _bucket_case(inp, 64)
+
+
 def test_bucketize_many_sequences():
     """More sequences than the kernel stages in LDS (its search then reads
     pair_offsets from memory)."""
