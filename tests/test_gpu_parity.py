@@ -399,6 +399,23 @@ def test_bf16_dq_paths_agree():
         assert P.rel_l2(P.host(got["export"]["dq"]), P.host(got[name]["dq"])) <= P.BF16_REL
 
 
+def test_bf16_partial_export_multiblock():
+    """Sequences far longer than max_len (positions clamp) overflow the dS
+    room sized from max_len after the first ones: the leading sequences take
+    dQ from their exported tiles and the rest recompute it, over many key
+    and query blocks, with both bias tables and candidate rows; the report
+    counts the split and every gradient matches the oracle."""
+    lengths = (1500, 1100, 1800, 900, 1300, 1700)
+    w = W.AttnWorkload("partial", 71, len(lengths), 2, 64, 64, 512, 128, True, "bf16", "fixed", lengths)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.array([0, 40, 0, 0, 100, 0], np.int64)
+    _, A = P.gpu_fwd(inp)
+    got = P.gpu_bwd(inp, A, report=True)
+    n_ds = got["info"]["ds_sequences"]
+    assert 0 < n_ds < len(lengths) and not got["info"]["dq_from_ds"], got["info"]
+    P.check_bwd(inp, got, P.oracle_bwd(inp), f"partial export ({n_ds} of {len(lengths)} sequences)")
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_bf16_ds_export_head_dims(D):
     """The dQ pass over exported dS tiles at every bf16 head dim: several key
