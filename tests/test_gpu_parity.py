@@ -399,6 +399,21 @@ def test_bf16_dq_paths_agree():
         assert P.rel_l2(P.host(got["export"]["dq"]), P.host(got[name]["dq"])) <= P.BF16_REL
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_many_short_sequences(dtype):
+    """6000 sequences of 0 to 9 rows (empty ones included) with candidates and
+    both bias tables: the schedule's arrays (B + 1 + 4 (T / 128 + 2) ints)
+    no longer fit its LDS and go through the workspace scratch, and the first
+    launch of each call holds 6000 prep workgroups beside the schedule (and,
+    in the backward, the dA' / dU pass)."""
+    rng = np.random.default_rng(81)
+    lengths = tuple(int(x) for x in rng.integers(0, 10, size=6000))
+    w = W.AttnWorkload("many", 82, len(lengths), 2, 32, 32, 16, 16, True, dtype, "fixed", lengths)
+    inp = W.make_attention_inputs(w)
+    inp["num_targets"] = np.minimum(rng.integers(0, 3, size=len(lengths)), np.array(lengths)).astype(np.int64)
+    _run_parity(inp, tag=f"many short {dtype}")
+
+
 def test_bf16_partial_export_multiblock():
     """Sequences far longer than max_len (positions clamp) overflow the dS
     room sized from max_len after the first ones: the leading sequences take
